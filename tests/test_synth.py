@@ -1,0 +1,41 @@
+"""The seeded input generators: determinism, chunk independence, bf16 rounding."""
+import numpy as np
+import pytest
+
+import synth
+
+
+def test_bf16_round_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(100000) * 10.0 ** rng.integers(-6, 6, 100000)).astype(np.float32)
+    x[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 0.0]    # ties to even, plain values
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(synth.bf16_round(x), want)
+
+
+def test_generators_are_deterministic_and_chunked():
+    wl = synth.get("attn4096").resized(rows=16, n=256, tokens=2 * synth.CHUNK + 100)
+    a = synth.activations_raw(wl)
+    b = synth.activations_raw(wl)
+    assert a.shape == (2 * synth.CHUNK + 100, 256) and a.dtype == np.uint16
+    assert np.array_equal(a, b)
+    c2 = synth.activations_chunk_raw(wl, 2)
+    assert np.array_equal(c2, a[2 * synth.CHUNK:])
+    w = synth.weights(wl)
+    assert w.shape == (16, 256) and np.array_equal(w, synth.weights(wl))
+
+
+def test_outlier_channels_present():
+    wl = synth.get("attn4096").resized(rows=4, n=1000, tokens=4096)
+    x = synth.activations(wl)
+    rms = np.sqrt(np.mean(x.astype(np.float64) ** 2, axis=0))
+    big = np.sort(rms)[-10:]
+    assert np.all(big > 10 * np.median(rms))          # 1% of 1000 channels scaled x20
+
+
+def test_toy_is_fp32_and_shaped():
+    wl = synth.get("toy256")
+    x = synth.activations(wl)
+    assert x.dtype == np.float32 and x.shape == (2048, 256)
+    assert synth.weights(wl).shape == (256, 256)
