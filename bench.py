@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Throughput of the GPTQ layer solve on one MI355X.
+
+One step = the whole hot path on one layer: Hessian accumulation over the
+calibration tokens (H from scratch), prepare (dead columns, act-order,
+damping, fp64 Cholesky and triangular inverse -> U), and the quantize sweep
+(lazy block updates, packing, loss).  Inputs are synthetic, seeded, and
+resident in HBM before timing starts.
+
+Prints one JSON line.  value = weights quantized per second for the whole
+step (rows * n / step time).  Also reported: Hessian TFLOP/s (algorithmic:
+n(n+1) flops per token, the unique entries of the symmetric product), the
+solve-only rate (prepare + quantize, H given), per-stage times, the roofline of
+the Hessian kernel measured live with HIP events on its stream, and the
+float64 CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload attn4096]
+       python bench.py --pmc-probe   (short run for rocprofv3 --pmc counter passes)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
+METRIC = "GPTQ weights quantized/sec per layer (4096×4096, g128) + Hessian TFLOP/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hessian_attn4096_traffic.json")
+HESSIAN_SRC = os.path.join(ROOT, "post_weight_quantization_13_amd", "csrc", "hessian.hip")
+
+
+def _log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _hessian_sha() -> str:
+    with open(HESSIAN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic():
+    """HBM bytes per Hessian launch from the committed counter summary, if it is
+    for the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != _hessian_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def _device_inputs(wl, torch):
+    import numpy as np
+    import synth
+    lin = wl.linears[0]
+    _log(f"generating {wl.name}: W {lin.rows}x{lin.n}, X {wl.tokens}x{lin.n} ({wl.dtype})")
+    w_raw = synth.weights_raw(wl, 0)
+    x_raw = synth.activations_raw(wl, lin.xset)
+    if wl.dtype == "bf16":
+        W = torch.from_numpy(w_raw.view(np.int16)).view(torch.bfloat16).cuda()
+        X = torch.from_numpy(x_raw.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        W = torch.from_numpy(w_raw).cuda()
+        X = torch.from_numpy(x_raw).cuda()
+    return w_raw, x_raw, W, X
+
+
+def cpu_baseline(wl, w_raw, x_raw):
+    """The float64 oracle on a bounded sample of the same layer, scaled to weights/s."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"] or [0])
+    except Exception:  # pragma: no cover
+        cores = 0
+    cores = cores or len(os.sched_getaffinity(0))
+    rows, n = wl.rows, wl.n
+    tok_s = min(wl.tokens, 8192)
+    rows_s = min(rows, 256)
+    xv = synth.bf16_value(x_raw[:tok_s]) if wl.dtype == "bf16" else x_raw[:tok_s]
+    wv = synth.bf16_value(w_raw[:rows_s]) if wl.dtype == "bf16" else w_raw[:rows_s]
+    cfg = oracle.QuantConfig(bits=wl.bits, group_size=wl.group_size, sym=wl.sym, desc_act=wl.desc_act,
+                             damp=wl.damp)
+    t0 = time.perf_counter()
+    H, _ = oracle.hessian(xv)
+    t1 = time.perf_counter()
+    p = oracle.prepare(H, cfg.damp, cfg.desc_act)
+    t2 = time.perf_counter()
+    oracle.quantize_layer(wv.astype(np.float64), p["U"], p["perm"], p["dead"], cfg)
+    t3 = time.perf_counter()
+    t_h = (t1 - t0) * wl.tokens / tok_s
+    t_p = t2 - t1
+    t_s = (t3 - t2) * rows / rows_s
+    total = t_h + t_p + t_s
+    return {
+        "value": rows * n / total, "unit": "weights/s", "cores": cores, "kind": "oracle",
+        "sample": (f"Hessian on {tok_s} of {wl.tokens} tokens (time x{wl.tokens / tok_s:g}), prepare at full "
+                   f"n={n}, sweep on {rows_s} of {rows} rows (time x{rows / rows_s:g}; rows are independent); "
+                   f"measured {t1 - t0:.2f}+{t2 - t1:.2f}+{t3 - t2:.2f} s"),
+        "stage_s": {"hessian": t_h, "prepare": t_p, "quantize": t_s},
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="attn4096")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="copy 1 GiB (counter calibration) then 3 Hessian launches; no timing output")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); the layer solve "
+              f"is not sharded across GPUs in this build.", file=sys.stderr)
+        return 2
+
+    import torch
+    import post_weight_quantization_13_amd as g
+    import synth
+
+    wl = synth.get(args.workload)
+    if len(wl.linears) != 1:
+        print("bench.py times single-layer workloads", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    w_raw, x_raw, W, X = _device_inputs(wl, torch)
+    rows, n, tokens = wl.rows, wl.n, wl.tokens
+    cfg = g.Config(bits=wl.bits, group_size=wl.group_size, sym=wl.sym, desc_act=wl.desc_act,
+                   damp_percent=wl.damp, block_size=wl.block_size)
+    dev = W.device
+    H = torch.empty((n, n), dtype=torch.float64, device=dev)
+    U = torch.empty((n, n), dtype=torch.float32, device=dev)
+    perm = torch.empty(n, dtype=torch.int32, device=dev)
+    dead = torch.empty(n, dtype=torch.uint8, device=dev)
+    qweight, scales, zeros, g_idx = g.alloc_outputs(rows, n, cfg, dev)
+    ws_p = g.workspace(g.gptq_prepare_workspace_bytes(n, cfg), dev)
+    ws_q = g.workspace(g.gptq_quantize_workspace_bytes(rows, n, cfg), dev)
+    torch.cuda.synchronize()
+
+    if args.pmc_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.gptq_hessian_accumulate(H, 0, X)
+        torch.cuda.synchronize()
+        _log("pmc probe done: 1 GiB copy + 3 Hessian launches")
+        return 0
+
+    def step():
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
+        g.gptq_hessian_accumulate(H, 0, X)
+        ev[1].record()
+        g.gptq_prepare_hinv(H, cfg, U, perm, dead, ws_p)
+        ev[2].record()
+        loss = g.gptq_quantize_layer(U, perm, dead, cfg, W, qweight, scales, zeros, g_idx, ws_q)
+        ev[3].record()
+        return ev, loss
+
+    for i in range(args.warmup):
+        step()
+        _log(f"warmup step {i + 1}/{args.warmup} done")
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        events.append(step()[0])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    _log(f"timed {args.steps} steps")
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    st = {k: sum(e[a].elapsed_time(e[b]) for e in events) / args.steps
+          for k, a, b in (("hessian", 0, 1), ("prepare", 1, 2), ("quantize", 2, 3))}
+    hess_flops = float(n) * (n + 1) * tokens
+    hess_tflops = hess_flops / (st["hessian"] * 1e-3) / 1e12
+    traffic = _traffic()
+    out = {
+        "metric": METRIC,
+        "value": rows * n / (ms_step * 1e-3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 mfma (fp32/fp64 accumulate) + fp64 cholesky + fp32 sweep",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "rows": rows, "n": n, "tokens": tokens, "bits": wl.bits,
+                   "group_size": wl.group_size, "sym": wl.sym, "desc_act": wl.desc_act, "damp": wl.damp,
+                   "description": wl.description},
+        "hessian_tflops": hess_tflops,
+        "solve_weights_per_s": rows * n / ((st["prepare"] + st["quantize"]) * 1e-3),
+        "stage_ms": st,
+        "roofline": {
+            "kernel": "syrk_mfma_kernel<bf16> (Hessian)",
+            "bound": "mfma",
+            "achieved": hess_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": hess_tflops / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        _log("timing the float64 oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(wl, w_raw, x_raw)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

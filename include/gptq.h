@@ -1,0 +1,174 @@
+/*
+ * gptq.h -- C ABI of the GPTQ layer-wise quantization solver for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Method (web pages about GPTQ, cited by title and section):
+ *   polydesk.ai glossary "GPTQ (Generative Pre-trained Transformer Quantization)":
+ *     "Comment fonctionne l'algorithme GPTQ"  -- per-layer objective ||W X - W_hat X||^2
+ *     "Étape 1 : Ordre arbitraire"             -- one fixed column order for all rows
+ *     "Étape 2 : Compensation d'erreur via la Hessienne" -- H = 2 X X^T, errors pushed
+ *                                                 onto later columns through the
+ *                                                 Cholesky factor of H^-1
+ *     "Étape 3 : Mises à jour par blocs"       -- lazy updates in blocks of 128 columns
+ *     "Paramètres clés de GPTQ"                -- bits, group_size, desc_act, sym
+ *   skillmd.com "Gptq" skill page, "Quantização group-wise" and
+ *     "Configurações de quantização"           -- groups of 128 with own scale/zero,
+ *                                                 damp_percent
+ *   ayinedjimi-consultants "Quantization : GPTQ, GGUF, AWQ", "Calibration et dataset"
+ *                                              -- fp16 scale/zero, packed low-bit weights
+ *
+ * Conventions shared by every call
+ *   - All array pointers are DEVICE pointers (memory of the current HIP device)
+ *     unless a comment says "host".  The caller owns every buffer; the library
+ *     never allocates or frees device memory.  Scratch space is passed in as a
+ *     workspace whose size is given by the matching *_workspace_bytes() query.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *     enqueued on it in order; calls return once the work is enqueued, except
+ *     where a comment says the call synchronizes the stream.
+ *   - Matrices are row-major.  W is [rows, n] (out features x in features);
+ *     X is [tokens, n] (one calibration token per row); H and U are [n, n].
+ *   - Errors are returned as gptq_status; arguments are checked before any
+ *     device work is enqueued, so an error other than GPTQ_ERR_HIP /
+ *     GPTQ_ERR_NOT_PD leaves every output untouched.  gptq_last_error() gives a
+ *     message for the last failing call on the calling thread.
+ *   - Calls that share a workspace or outputs must not overlap on different
+ *     streams.
+ */
+#ifndef GPTQ_H
+#define GPTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad leading dimension   */
+  GPTQ_ERR_UNSUPPORTED = -2,  /* valid but not supported: bits, group size, dtype ... */
+  GPTQ_ERR_NOT_PD = -3,       /* damped Hessian not positive definite                 */
+  GPTQ_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed           */
+  GPTQ_ERR_WORKSPACE = -5     /* workspace null or smaller than the query returned    */
+} gptq_status;
+
+typedef enum { GPTQ_BF16 = 0, GPTQ_FP16 = 1, GPTQ_FP32 = 2 } gptq_dtype;
+
+/* The quantize config of the pages ("Configurações de quantização", "Paramètres clés"). */
+typedef struct {
+  int32_t bits;          /* code width: 3 or 4                                              */
+  int32_t group_size;    /* weights per scale/zero group along a row: 128                    */
+  int32_t sym;           /* 0: asymmetric grid (zero point in [0, 2^bits-1]);               */
+                         /* 1: symmetric grid, levels -(2^(b-1)-1)..2^(b-1)-1, zero exact    */
+  int32_t desc_act;      /* 1: act-order, columns visited by decreasing diag(H)              */
+  float damp_percent;    /* lambda = damp_percent * mean(diag H) is added to the diagonal    */
+  int32_t block_size;    /* lazy-batch width in columns: 128                                 */
+} gptq_config;
+
+/* ------------------------------------------------------------------------- *
+ * Calibration Hessian ("Étape 2": H = 2 X X^T).
+ *
+ * Maintains the running mean H = (2 / N) * sum_t x_t x_t^T over all tokens fed
+ * so far, N = *n_tokens.  One call adds `tokens` rows of X:
+ *     H <- (N_old / N_new) * H + (2 / N_new) * X^T X,   N_new = N_old + tokens.
+ * If *n_tokens == 0 on entry the previous contents of H are ignored (no need to
+ * clear it).  tokens == 0 is a no-op returning GPTQ_OK.
+ *   H        device fp64 [n, n]; the full symmetric matrix is written (both
+ *            triangles, bit-identical mirror).  1 <= n <= 2097120.
+ *   n_tokens HOST int64 in/out: running token count, updated on success.
+ *   X        device [tokens, ldx] of dtype xdt (bf16, fp16 or fp32), ldx >= n;
+ *            only columns 0..n-1 are read.  Not modified.
+ *   workspace, ws_bytes: currently gptq_hessian_workspace_bytes() == 0 and
+ *            NULL is accepted.
+ * bf16/fp16 products are summed by MFMA with fp32 accumulation in chains of at
+ * most gptq_hessian_chain_tokens() tokens; chains are combined in fp64, which
+ * is also the storage precision of H (GPTQ's codes react to Hessian error far
+ * below fp32 chain-summation error).  fp32 inputs accumulate in fp64.
+ * Deterministic: same inputs, same bits.
+ * ------------------------------------------------------------------------- */
+size_t gptq_hessian_workspace_bytes(int64_t n, int64_t tokens, gptq_dtype xdt);
+int64_t gptq_hessian_chain_tokens(void);
+gptq_status gptq_hessian_accumulate(double* H, int64_t n, int64_t* n_tokens,
+                                    const void* X, gptq_dtype xdt, int64_t tokens,
+                                    int64_t ldx, void* workspace, size_t ws_bytes,
+                                    void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * Prepare ("Étape 2": Cholesky factor of the inverse Hessian; damp_percent;
+ * desc_act).  Reads H, writes
+ *   perm  device int32 [n]: sweep position j visits original column perm[j]
+ *         (identity unless cfg->desc_act; else stable sort of diag(H), largest
+ *         first, ties by lower index),
+ *   dead  device uint8 [n]: 1 where H_ii == 0 (original column order); such a
+ *         diagonal is taken as 1 and the weight column is zeroed by the quantizer,
+ *   U     device fp32 [n, n]: the upper triangular factor with positive diagonal
+ *         and U^T U = (H_p + lambda I)^-1, H_p = H permuted to sweep order,
+ *         lambda = damp_percent * mean(diag H_p).  Entries below the diagonal
+ *         are written as 0.
+ * H is device fp64 [n, n] as written by gptq_hessian_accumulate (symmetric;
+ * entries of both triangles are read) and is not modified.
+ * The factorization runs in fp64 on the device (the result is rounded to fp32).
+ * Synchronizes `stream` once, to read back the positive-definiteness flag:
+ * returns GPTQ_ERR_NOT_PD (U then undefined) if a pivot is not > 0 or not
+ * finite, or a diagonal entry of H is negative or not finite.
+ * 1 <= n <= 65535.
+ * ------------------------------------------------------------------------- */
+size_t gptq_prepare_workspace_bytes(int64_t n, const gptq_config* cfg);
+gptq_status gptq_prepare_hinv(const double* H, int64_t n, const gptq_config* cfg,
+                              float* U, int32_t* perm, uint8_t* dead,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * Quantize one layer ("Étape 1/2/3", "Quantização group-wise").
+ *   U, perm, dead  as written by gptq_prepare_hinv for this n and cfg (several
+ *                  layers that share a Hessian may reuse them).
+ *   W        device [rows, ldw] of dtype wdt, ldw >= n.  Not modified.
+ * Outputs (caller-allocated device buffers):
+ *   qweight  int32 [n*bits/32, rows]: row r's codes in ORIGINAL column order form
+ *            a little-endian bit stream, column i at bits [bits*i, bits*i+bits);
+ *            qweight[k, r] is word k of that stream (4-bit: 8 codes per word;
+ *            3-bit: 32 codes per 3 words).
+ *   scales   fp16 bits [n/group_size, rows]: group g = sweep columns
+ *            [g*gs, (g+1)*gs).
+ *   zeros    fp16 bits [n/group_size, rows]: integer-valued zero points.
+ *   g_idx    int32 [n]: g_idx[perm[j]] = j / group_size.
+ *   loss_out HOST double, may be NULL: sum over rows and columns of e^2 / 2 with
+ *            e = (w - w_hat) / U[j, j] (equals tr(D H_d D^T) / 2, D = W - W_hat).
+ * Dequantization: W_hat[r, i] = scales[g_idx[i], r] * (code[r, i] - zeros[g_idx[i], r]).
+ * Supported: bits in {3, 4}; group_size == block_size == 128; n % 128 == 0.
+ * rows == 0 is a no-op.  Synchronizes `stream` once when loss_out != NULL.
+ * ------------------------------------------------------------------------- */
+size_t gptq_quantize_workspace_bytes(int64_t rows, int64_t n, const gptq_config* cfg);
+gptq_status gptq_quantize_layer(const float* U, const int32_t* perm, const uint8_t* dead,
+                                int64_t n, const gptq_config* cfg,
+                                const void* W, gptq_dtype wdt, int64_t rows, int64_t ldw,
+                                int32_t* qweight, uint16_t* scales, uint16_t* zeros,
+                                int32_t* g_idx, double* loss_out,
+                                void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * Relative layer loss ("Comment fonctionne l'algorithme GPTQ": the objective is
+ * the squared output error).  Dequantizes the packed outputs and returns
+ *   *rel_loss (HOST) = tr(D H D^T) / tr(W H W^T),  D = W - W_hat,
+ * which equals ||W X - W_hat X||^2 / ||W X||^2 for H = (2/N) X^T X.
+ * H is the undamped fp64 Hessian in original column order.  Synchronizes `stream`.
+ * A measurement helper: not part of the quantization itself.
+ * ------------------------------------------------------------------------- */
+size_t gptq_layer_loss_workspace_bytes(int64_t rows, int64_t n);
+gptq_status gptq_layer_loss(const double* H, int64_t n, const void* W, gptq_dtype wdt,
+                            int64_t rows, int64_t ldw, const int32_t* qweight,
+                            const uint16_t* scales, const uint16_t* zeros, const int32_t* g_idx,
+                            const gptq_config* cfg, double* rel_loss,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/* Message for the last failing call on this thread (empty string if none). */
+const char* gptq_last_error(void);
+/* Library version string. */
+const char* gptq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_H */

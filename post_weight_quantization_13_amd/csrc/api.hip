@@ -1,0 +1,203 @@
+// extern "C" entry points of libgptq: argument checks, workspace sizing and
+// the launch sequence of each call.  Declarations and contracts: include/gptq.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/gptq.h"
+
+namespace gptq {
+hipError_t launch_hessian(double* H, int64_t n, const void* X, int dt, int64_t tokens, int64_t ldx, double alpha,
+                          double beta, hipStream_t s);
+int64_t hessian_chain_tokens();
+size_t prepare_workspace(int64_t n);
+hipError_t launch_prepare(const double* H, int64_t n, double damp, int desc_act, float* U, int32_t* perm,
+                          uint8_t* dead, void* ws, hipStream_t s, int* info_host);
+size_t quantize_workspace(int64_t rows, int64_t n);
+hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* dead, int64_t n, int bits, int sym,
+                           const void* W, int wdt, int64_t rows, int64_t ldw, int32_t* qweight, uint16_t* scales,
+                           uint16_t* zeros, int32_t* g_idx, double* loss_host, void* ws, hipStream_t s);
+size_t loss_workspace(int64_t rows, int64_t n);
+hipError_t launch_layer_loss(const double* H, int64_t n, const void* W, int wdt, int64_t rows, int64_t ldw,
+                             const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                             const int32_t* g_idx, int bits, double* rel_host, void* ws, hipStream_t s);
+}  // namespace gptq
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int64_t kMaxDim = 65535 * 32;  // keeps every grid dimension in range
+
+gptq_status fail(gptq_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+gptq_status fail(gptq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+gptq_status ok() {
+  g_last_error.clear();
+  return GPTQ_OK;
+}
+
+gptq_status hip_fail(const char* where, hipError_t e) {
+  return fail(GPTQ_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool valid_dtype(int dt) { return dt == GPTQ_BF16 || dt == GPTQ_FP16 || dt == GPTQ_FP32; }
+
+gptq_status check_config(const gptq_config* cfg, bool for_quantize) {
+  if (!cfg) return fail(GPTQ_ERR_INVALID_ARG, "cfg is NULL");
+  if (!(cfg->damp_percent >= 0.0f) || !std::isfinite(cfg->damp_percent))
+    return fail(GPTQ_ERR_INVALID_ARG, "damp_percent must be finite and >= 0 (got %g)", cfg->damp_percent);
+  if (cfg->desc_act != 0 && cfg->desc_act != 1) return fail(GPTQ_ERR_INVALID_ARG, "desc_act must be 0 or 1");
+  if (!for_quantize) return GPTQ_OK;
+  if (cfg->sym != 0 && cfg->sym != 1) return fail(GPTQ_ERR_INVALID_ARG, "sym must be 0 or 1");
+  if (cfg->bits != 3 && cfg->bits != 4) return fail(GPTQ_ERR_UNSUPPORTED, "bits=%d (supported: 3, 4)", cfg->bits);
+  if (cfg->group_size != 128)
+    return fail(GPTQ_ERR_UNSUPPORTED, "group_size=%d (supported: 128)", cfg->group_size);
+  if (cfg->block_size != 128)
+    return fail(GPTQ_ERR_UNSUPPORTED, "block_size=%d (supported: 128)", cfg->block_size);
+  return GPTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gptq_last_error(void) { return g_last_error.c_str(); }
+
+const char* gptq_version(void) { return "gptq-gfx950 0.1.0"; }
+
+// ----------------------------------------------------------------------------- Hessian
+size_t gptq_hessian_workspace_bytes(int64_t n, int64_t tokens, gptq_dtype xdt) {
+  (void)n;
+  (void)tokens;
+  (void)xdt;
+  return 0;
+}
+
+int64_t gptq_hessian_chain_tokens(void) { return gptq::hessian_chain_tokens(); }
+
+gptq_status gptq_hessian_accumulate(double* H, int64_t n, int64_t* n_tokens, const void* X, gptq_dtype xdt,
+                                    int64_t tokens, int64_t ldx, void* workspace, size_t ws_bytes,
+                                    void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  if (!H) return fail(GPTQ_ERR_INVALID_ARG, "H is NULL");
+  if (!n_tokens) return fail(GPTQ_ERR_INVALID_ARG, "n_tokens is NULL");
+  if (n < 1 || n > kMaxDim) return fail(GPTQ_ERR_INVALID_ARG, "n=%lld out of range", (long long)n);
+  if (*n_tokens < 0) return fail(GPTQ_ERR_INVALID_ARG, "*n_tokens=%lld < 0", (long long)*n_tokens);
+  if (tokens < 0) return fail(GPTQ_ERR_INVALID_ARG, "tokens=%lld < 0", (long long)tokens);
+  if (!valid_dtype(xdt)) return fail(GPTQ_ERR_INVALID_ARG, "unknown dtype %d", (int)xdt);
+  if (tokens == 0) return ok();
+  if (!X) return fail(GPTQ_ERR_INVALID_ARG, "X is NULL");
+  if (ldx < n) return fail(GPTQ_ERR_INVALID_ARG, "ldx=%lld < n=%lld", (long long)ldx, (long long)n);
+  const int64_t n_old = *n_tokens;
+  const int64_t n_new = n_old + tokens;
+  const double alpha = 2.0 / static_cast<double>(n_new);
+  const double beta = static_cast<double>(n_old) / static_cast<double>(n_new);
+  hipError_t e = gptq::launch_hessian(H, n, X, static_cast<int>(xdt), tokens, ldx, alpha, beta,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("gptq_hessian_accumulate", e);
+  *n_tokens = n_new;
+  return ok();
+}
+
+// ----------------------------------------------------------------------------- prepare
+size_t gptq_prepare_workspace_bytes(int64_t n, const gptq_config* cfg) {
+  (void)cfg;
+  if (n < 1) return 0;
+  return gptq::prepare_workspace(n);
+}
+
+gptq_status gptq_prepare_hinv(const double* H, int64_t n, const gptq_config* cfg, float* U, int32_t* perm,
+                              uint8_t* dead, void* workspace, size_t ws_bytes, void* stream) {
+  gptq_status st = check_config(cfg, false);
+  if (st != GPTQ_OK) return st;
+  if (!H || !U || !perm || !dead) return fail(GPTQ_ERR_INVALID_ARG, "NULL H, U, perm or dead");
+  if (n < 1 || n > 65535) return fail(GPTQ_ERR_INVALID_ARG, "n=%lld out of range [1, 65535]", (long long)n);
+  const size_t need = gptq::prepare_workspace(n);
+  if (!workspace || ws_bytes < need)
+    return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace ? ws_bytes : 0, need);
+  int info = 0;
+  hipError_t e = gptq::launch_prepare(H, n, static_cast<double>(cfg->damp_percent), cfg->desc_act, U, perm, dead,
+                                      workspace, static_cast<hipStream_t>(stream), &info);
+  if (e != hipSuccess) return hip_fail("gptq_prepare_hinv", e);
+  if (info != 0) return fail(GPTQ_ERR_NOT_PD, "damped Hessian is not positive definite");
+  return ok();
+}
+
+// ----------------------------------------------------------------------------- quantize
+size_t gptq_quantize_workspace_bytes(int64_t rows, int64_t n, const gptq_config* cfg) {
+  (void)cfg;
+  if (rows < 1 || n < 1) return 0;
+  return gptq::quantize_workspace(rows, n);
+}
+
+gptq_status gptq_quantize_layer(const float* U, const int32_t* perm, const uint8_t* dead, int64_t n,
+                                const gptq_config* cfg, const void* W, gptq_dtype wdt, int64_t rows, int64_t ldw,
+                                int32_t* qweight, uint16_t* scales, uint16_t* zeros, int32_t* g_idx,
+                                double* loss_out, void* workspace, size_t ws_bytes, void* stream) {
+  gptq_status st = check_config(cfg, true);
+  if (st != GPTQ_OK) return st;
+  if (n < 1 || n > kMaxDim) return fail(GPTQ_ERR_INVALID_ARG, "n=%lld out of range", (long long)n);
+  if (n % cfg->group_size != 0)
+    return fail(GPTQ_ERR_UNSUPPORTED, "n=%lld is not a multiple of group_size=%d", (long long)n, cfg->group_size);
+  if (rows < 0 || rows > (int64_t)1 << 30) return fail(GPTQ_ERR_INVALID_ARG, "rows=%lld out of range", (long long)rows);
+  if (!valid_dtype(wdt)) return fail(GPTQ_ERR_INVALID_ARG, "unknown dtype %d", (int)wdt);
+  if (rows == 0) {
+    if (loss_out) *loss_out = 0.0;
+    return ok();
+  }
+  if (!U || !perm || !dead || !W || !qweight || !scales || !zeros || !g_idx)
+    return fail(GPTQ_ERR_INVALID_ARG, "NULL input or output pointer");
+  if (ldw < n) return fail(GPTQ_ERR_INVALID_ARG, "ldw=%lld < n=%lld", (long long)ldw, (long long)n);
+  const size_t need = gptq::quantize_workspace(rows, n);
+  if (!workspace || ws_bytes < need)
+    return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace ? ws_bytes : 0, need);
+  hipError_t e = gptq::launch_quantize(U, perm, dead, n, cfg->bits, cfg->sym, W, static_cast<int>(wdt), rows, ldw,
+                                       qweight, scales, zeros, g_idx, loss_out, workspace,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("gptq_quantize_layer", e);
+  return ok();
+}
+
+// ----------------------------------------------------------------------------- loss
+size_t gptq_layer_loss_workspace_bytes(int64_t rows, int64_t n) {
+  if (rows < 1 || n < 1) return 0;
+  return gptq::loss_workspace(rows, n);
+}
+
+gptq_status gptq_layer_loss(const double* H, int64_t n, const void* W, gptq_dtype wdt, int64_t rows, int64_t ldw,
+                            const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                            const int32_t* g_idx, const gptq_config* cfg, double* rel_loss, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  gptq_status st = check_config(cfg, true);
+  if (st != GPTQ_OK) return st;
+  if (!H || !W || !qweight || !scales || !zeros || !g_idx || !rel_loss)
+    return fail(GPTQ_ERR_INVALID_ARG, "NULL pointer argument");
+  if (n < 1 || n > kMaxDim || n % cfg->group_size != 0)
+    return fail(GPTQ_ERR_INVALID_ARG, "n=%lld invalid", (long long)n);
+  if (rows < 1 || rows > (int64_t)1 << 30) return fail(GPTQ_ERR_INVALID_ARG, "rows=%lld invalid", (long long)rows);
+  if (!valid_dtype(wdt)) return fail(GPTQ_ERR_INVALID_ARG, "unknown dtype %d", (int)wdt);
+  if (ldw < n) return fail(GPTQ_ERR_INVALID_ARG, "ldw=%lld < n=%lld", (long long)ldw, (long long)n);
+  const size_t need = gptq::loss_workspace(rows, n);
+  if (!workspace || ws_bytes < need)
+    return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace ? ws_bytes : 0, need);
+  hipError_t e = gptq::launch_layer_loss(H, n, W, static_cast<int>(wdt), rows, ldw, qweight, scales, zeros, g_idx,
+                                         cfg->bits, rel_loss, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("gptq_layer_loss", e);
+  return ok();
+}
+
+}  // extern "C"

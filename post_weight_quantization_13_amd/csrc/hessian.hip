@@ -1,0 +1,312 @@
+// Calibration Hessian H = (2/N) X^T X on gfx950.
+//
+// polydesk.ai "GPTQ" glossary, "Étape 2 : Compensation d'erreur via la
+// Hessienne": the Hessian is twice X X^T over the calibration activations
+// (kept here as a running mean over tokens).
+//
+// Design
+//   * One workgroup (4 waves) owns one 128x128 tile (I, J), I <= J, of the upper
+//     triangle and walks the whole token range.  Each wave computes a 64x64
+//     quarter with bf16/fp16 MFMA (v_mfma_f32_32x32x16, 2x2 MFMA tiles).
+//   * Precision: the fp32 MFMA accumulators are flushed into an fp64 master
+//     copy (in registers) every kFlushSteps stages of 32 tokens, so no fp32
+//     accumulation chain is longer than kFlushSteps*32 tokens.  The codes GPTQ
+//     produces are very sensitive to Hessian error (one flipped code changes
+//     the rest of its row), and long fp32 chains measurably lower agreement
+//     with an exact Hessian; short chains summed in fp64 do not.  H is stored
+//     in fp64 for the same reason.
+//   * Operand staging: per stage every thread loads 8 tokens x 2 features
+//     (eight 4-byte loads, 256 contiguous bytes per wave instruction),
+//     transposes them in registers and stores 2 feature rows of 8 consecutive
+//     tokens into LDS, so each MFMA operand fragment (8 consecutive tokens of
+//     one feature) is a single 16-byte LDS read.  LDS is double buffered and
+//     the next stage's global loads are issued before the current MFMAs.
+//   * Epilogue: H <- beta*H + alpha*master; each element is written once and
+//     mirrored through LDS so H is exactly symmetric and both writes coalesce.
+//   * fp32 inputs use a VALU kernel accumulating in fp64.
+#include "common.hpp"
+
+namespace gptq {
+
+constexpr int kTile = 128;       // output tile edge (features)
+constexpr int kKStep = 32;       // tokens per LDS stage
+constexpr int kFlushSteps = 8;   // stages per fp32 chain: 8 x 32 = 256 tokens (16 MFMAs)
+
+// LDS panel: kTile features x kKStep tokens of 16-bit values (64 bytes per
+// feature = four 16-byte chunks of 8 tokens).  Chunk c of feature f is stored
+// at 16-byte unit f*4 + (c ^ ((f >> 2) & 3)): fragment reads (16 lanes on
+// consecutive features) hit 16 distinct bank groups; the transposed stores
+// (lanes on features 2l, 2l+1) hit 8.
+__device__ __forceinline__ int panel_offset_bytes(int f, int c) {
+  return ((f << 2) | (c ^ ((f >> 2) & 3))) << 4;
+}
+
+// Upper-triangle tile enumeration: t -> (ti, tj), ti <= tj, row by row.
+__device__ __forceinline__ void upper_tile(int t, int nt, int& ti, int& tj) {
+  int i = 0;
+  int rem = t;
+  while (rem >= nt - i) {
+    rem -= nt - i;
+    ++i;
+  }
+  ti = i;
+  tj = i + rem;
+}
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma_32x32x16(const u32x4& a, const u32x4& b, f32x16 c) {
+  if constexpr (DT == DT_BF16) {
+    bf16x8 av, bv;
+    __builtin_memcpy(&av, &a, 16);
+    __builtin_memcpy(&bv, &b, 16);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
+  } else {
+    f16x8 av, bv;
+    __builtin_memcpy(&av, &a, 16);
+    __builtin_memcpy(&bv, &b, 16);
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, c, 0, 0, 0);
+  }
+}
+
+// grid.x = upper 128x128 tiles; 256 threads.
+template <int DT>
+__global__ void __launch_bounds__(256) syrk_mfma_kernel(
+    const uint16_t* __restrict__ X, int64_t ldx, int n, int64_t tokens, int nt, int vec_ok,
+    double alpha, double beta, double* __restrict__ H) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTile * kKStep * 2];  // 32 KB
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  int ti, tj;
+  upper_tile(blockIdx.x, nt, ti, tj);
+  const bool diag = (ti == tj);
+
+  // Loader units: u = tid + 256*k (k = 0, 1) -> feature pair fp = u & 63,
+  // panel p = (u >> 6) & 1, token group tg = u >> 7 (8 tokens each).
+  int ld_fp[2], ld_p[2], ld_tg[2], ld_feat[2];
+  bool ld_on[2], ld_vec[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = tid + 256 * k;
+    ld_fp[k] = u & 63;
+    ld_p[k] = (u >> 6) & 1;
+    ld_tg[k] = u >> 7;
+    ld_feat[k] = (ld_p[k] ? tj : ti) * kTile + 2 * ld_fp[k];
+    ld_on[k] = !(diag && ld_p[k] == 1);
+    ld_vec[k] = vec_ok && (ld_feat[k] + 2 <= n);
+  }
+
+  uint32_t regs[2][8];
+  auto global_load = [&](int64_t t0) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int64_t t = t0 + ld_tg[k] * 8 + e;
+        uint32_t v = 0u;
+        if (ld_on[k] && t < tokens) {
+          const uint16_t* p = X + t * ldx + ld_feat[k];
+          if (ld_vec[k]) {
+            v = *reinterpret_cast<const uint32_t*>(p);
+          } else {
+            const uint32_t lo = (ld_feat[k] < n) ? p[0] : 0u;
+            const uint32_t hi = (ld_feat[k] + 1 < n) ? p[1] : 0u;
+            v = lo | (hi << 16);
+          }
+        }
+        regs[k][e] = v;
+      }
+    }
+  };
+  auto lds_store = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (!ld_on[k]) continue;
+      u32x4 f0, f1;  // tokens 0..7 of features 2fp and 2fp+1
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t lo = regs[k][2 * d], hi = regs[k][2 * d + 1];
+        f0[d] = (lo & 0xFFFFu) | (hi << 16);
+        f1[d] = (lo >> 16) | (hi & 0xFFFF0000u);
+      }
+      uint8_t* base = lds[buf][ld_p[k]];
+      *reinterpret_cast<u32x4*>(base + panel_offset_bytes(2 * ld_fp[k], ld_tg[k])) = f0;
+      *reinterpret_cast<u32x4*>(base + panel_offset_bytes(2 * ld_fp[k] + 1, ld_tg[k])) = f1;
+    }
+  };
+
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  f32x16 acc[2][2];
+  double master[2][2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc[i][j][r] = 0.0f;
+        master[i][j][r] = 0.0;
+      }
+
+  const int b_panel = diag ? 0 : 1;
+  global_load(0);
+  lds_store(0);
+  __syncthreads();
+  int buf = 0;
+  int step = 0;
+  for (int64_t t0 = 0; t0 < tokens; t0 += kKStep) {
+    const bool more = (t0 + kKStep < tokens);
+    if (more) global_load(t0 + kKStep);
+    const uint8_t* pa = lds[buf][0];
+    const uint8_t* pb = lds[buf][b_panel];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = kk * 2 + (lane >> 5);
+      u32x4 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fa[i] = *reinterpret_cast<const u32x4*>(pa + panel_offset_bytes(wm * 64 + i * 32 + (lane & 31), c));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[j] = *reinterpret_cast<const u32x4*>(pb + panel_offset_bytes(wn * 64 + j * 32 + (lane & 31), c));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16<DT>(fa[i], fb[j], acc[i][j]);
+    }
+    if (++step == kFlushSteps || !more) {
+      step = 0;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            master[i][j][r] += static_cast<double>(acc[i][j][r]);
+            acc[i][j][r] = 0.0f;
+          }
+    }
+    if (more) {
+      lds_store(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+  // Epilogue.  MFMA 32x32 output layout: accumulator r of lane l is row
+  // 8*(r/4) + 4*(l/32) + r%4, column l%32 of the 32x32 block.
+  __syncthreads();  // every wave is done with the staging buffers
+  double* stage = reinterpret_cast<double*>(&lds[0][0][0]);  // 64x64 fp64 = 32 KB
+  for (int w = 0; w < 4; ++w) {
+    const int rw = (w >> 1) * 64, cw = (w & 1) * 64;  // quarter owned by wave w
+    if (wave == w) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int lr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int lc = j * 32 + (lane & 31);
+            const int gi = ti * kTile + rw + lr, gj = tj * kTile + cw + lc;
+            double v = alpha * master[i][j][r];
+            const bool own = gi < n && gj < n && !(diag && gi > gj);
+            if (own) {
+              if (beta != 0.0) v += beta * H[static_cast<int64_t>(gi) * n + gj];
+              H[static_cast<int64_t>(gi) * n + gj] = v;
+            }
+            stage[lc * 64 + (lr ^ (lc & 63))] = v;  // transposed, XOR-swizzled
+          }
+    }
+    __syncthreads();
+    // Mirror: H[gj][gi] for the quarter, rows of the mirror are lc.
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int lc = e >> 6, lr = e & 63;
+      const int gi = ti * kTile + rw + lr, gj = tj * kTile + cw + lc;
+      if (gi < n && gj < n && gi < gj) H[static_cast<int64_t>(gj) * n + gi] = stage[lc * 64 + (lr ^ (lc & 63))];
+    }
+    __syncthreads();
+  }
+}
+
+// fp32 inputs: 64x64 tiles of the upper triangle, fp64 accumulation on the VALU.
+__global__ void __launch_bounds__(256) syrk_f32_kernel(
+    const float* __restrict__ X, int64_t ldx, int n, int64_t tokens, int nt64,
+    double alpha, double beta, double* __restrict__ H) {
+  __shared__ float sa[32][65];
+  __shared__ float sb[32][65];
+  int ti, tj;
+  upper_tile(blockIdx.x, nt64, ti, tj);
+  const int tid = threadIdx.x;
+  const int tr = tid / 16, tc = tid % 16;  // 16x16 threads, 4x4 outputs each
+  double acc[4][4] = {};
+  for (int64_t t0 = 0; t0 < tokens; t0 += 32) {
+    for (int e = tid; e < 32 * 64; e += 256) {
+      const int k = e / 64, f = e % 64;
+      const int64_t t = t0 + k;
+      const int fa = ti * 64 + f, fb = tj * 64 + f;
+      sa[k][f] = (t < tokens && fa < n) ? X[t * ldx + fa] : 0.0f;
+      sb[k][f] = (t < tokens && fb < n) ? X[t * ldx + fb] : 0.0f;
+    }
+    __syncthreads();
+    for (int k = 0; k < 32; ++k) {
+      double a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sa[k][tr * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = sb[k][tc * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  const bool diag = (ti == tj);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gi = ti * 64 + tr * 4 + i, gj = tj * 64 + tc * 4 + j;
+      if (gi >= n || gj >= n || (diag && gi > gj)) continue;
+      double v = alpha * acc[i][j];
+      if (beta != 0.0) v += beta * H[static_cast<int64_t>(gi) * n + gj];
+      H[static_cast<int64_t>(gi) * n + gj] = v;
+      if (gi != gj) H[static_cast<int64_t>(gj) * n + gi] = v;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Host-side launcher (called from api.hip).
+// ----------------------------------------------------------------------------
+static inline int64_t upper_tiles(int64_t nt) { return nt * (nt + 1) / 2; }
+
+int64_t hessian_chain_tokens() { return static_cast<int64_t>(kFlushSteps) * kKStep; }
+
+hipError_t launch_hessian(double* H, int64_t n, const void* X, int dt, int64_t tokens,
+                          int64_t ldx, double alpha, double beta, hipStream_t s) {
+  if (dt == DT_FP32) {
+    const int nt64 = static_cast<int>((n + 63) / 64);
+    hipLaunchKernelGGL(syrk_f32_kernel, dim3(static_cast<unsigned>(upper_tiles(nt64))), dim3(256), 0, s,
+                       static_cast<const float*>(X), ldx, static_cast<int>(n), tokens, nt64, alpha,
+                       beta, H);
+    return hipGetLastError();
+  }
+  const int nt = static_cast<int>((n + kTile - 1) / kTile);
+  const unsigned ntiles = static_cast<unsigned>(upper_tiles(nt));
+  const int vec_ok = (ldx % 2 == 0) && (reinterpret_cast<uintptr_t>(X) % 4 == 0);
+  if (dt == DT_BF16) {
+    hipLaunchKernelGGL(syrk_mfma_kernel<DT_BF16>, dim3(ntiles), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(X), ldx, static_cast<int>(n), tokens, nt, vec_ok,
+                       alpha, beta, H);
+  } else {
+    hipLaunchKernelGGL(syrk_mfma_kernel<DT_FP16>, dim3(ntiles), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(X), ldx, static_cast<int>(n), tokens, nt, vec_ok,
+                       alpha, beta, H);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gptq
