@@ -174,7 +174,8 @@ __global__ void __launch_bounds__(256) chol_diag_kernel(double* __restrict__ A, 
 // A is addressed A[m*lda + k]; B as B[k*ldb + n] (BT = false) or B[n*ldb + k]
 // (BT = true).  Rows >= mv, columns >= nv and k >= k1 read as 0.
 // v_mfma_f64_16x16x4: lane l supplies A[l%16][l/16] and B[l/16][l%16];
-// accumulator r of lane l is D[4*(l/16) + r][l%16].  Wave (wm, wn) owns the
+// accumulator r of lane l is D[l/16 + 4*r][l%16] (rows interleaved across the
+// four accumulators; measured on gfx950).  Wave (wm, wn) owns the
 // 32x32 quarter (wm*32.., wn*32..): 2x2 MFMA tiles.
 struct TileSmem {
   double a[kB][17];
@@ -239,7 +240,7 @@ __device__ __forceinline__ void tile_foreach(const f64x4 (&acc)[2][2], F f) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        f(wm * 32 + i * 16 + (lane >> 4) * 4 + r, wn * 32 + j * 16 + (lane & 15), acc[i][j][r]);
+        f(wm * 32 + i * 16 + (lane >> 4) + 4 * r, wn * 32 + j * 16 + (lane & 15), acc[i][j][r]);
 }
 
 __device__ __forceinline__ void zero_acc(f64x4 (&acc)[2][2]) {
