@@ -9,18 +9,18 @@
 //     triangle and walks the whole token range.  Each wave computes a 64x64
 //     quarter with bf16/fp16 MFMA (v_mfma_f32_32x32x16, 2x2 MFMA tiles).
 //   * Precision: the fp32 MFMA accumulators are flushed into an fp64 master
-//     copy (in registers) every kFlushSteps stages of 32 tokens, so no fp32
-//     accumulation chain is longer than kFlushSteps*32 tokens.  The codes GPTQ
+//     copy (in registers) every kFlushSteps stages of 64 tokens, so no fp32
+//     accumulation chain is longer than 256 tokens.  The codes GPTQ
 //     produces are very sensitive to Hessian error (one flipped code changes
 //     the rest of its row), and long fp32 chains measurably lower agreement
 //     with an exact Hessian; short chains summed in fp64 do not.  H is stored
 //     in fp64 for the same reason.
-//   * Operand staging: per stage every thread loads 8 tokens x 2 features
-//     (eight 4-byte loads, 256 contiguous bytes per wave instruction),
-//     transposes them in registers and stores 2 feature rows of 8 consecutive
-//     tokens into LDS, so each MFMA operand fragment (8 consecutive tokens of
-//     one feature) is a single 16-byte LDS read.  LDS is double buffered and
-//     the next stage's global loads are issued before the current MFMAs.
+//   * Operand staging: per stage of 64 tokens every thread loads 8 tokens x 8
+//     features (eight 16-byte loads), transposes the 8x8 block of 16-bit
+//     values in registers and stores 8 feature rows of 8 consecutive tokens
+//     into LDS, so each MFMA operand fragment (8 consecutive tokens of one
+//     feature) is a single 16-byte LDS read.  LDS is double buffered and two
+//     further stages are held in registers / in flight ahead of the MFMAs.
 //   * Epilogue: H <- beta*H + alpha*master; each element is written once and
 //     mirrored through LDS so H is exactly symmetric and both writes coalesce.
 //   * fp32 inputs use a VALU kernel accumulating in fp64.
@@ -29,16 +29,17 @@
 namespace gptq {
 
 constexpr int kTile = 128;       // output tile edge (features)
-constexpr int kKStep = 32;       // tokens per LDS stage
-constexpr int kFlushSteps = 8;   // stages per fp32 chain: 8 x 32 = 256 tokens (16 MFMAs)
+constexpr int kKStep = 64;       // tokens per LDS stage
+constexpr int kFlushSteps = 4;   // stages per fp32 chain: 4 x 64 = 256 tokens (16 MFMAs)
 
-// LDS panel: kTile features x kKStep tokens of 16-bit values (64 bytes per
-// feature = four 16-byte chunks of 8 tokens).  Chunk c of feature f is stored
-// at 16-byte unit f*4 + (c ^ ((f >> 2) & 3)): fragment reads (16 lanes on
-// consecutive features) hit 16 distinct bank groups; the transposed stores
-// (lanes on features 2l, 2l+1) hit 8.
+// LDS panel: kTile features x kKStep tokens of 16-bit values = 16 KB; a feature
+// row is 128 bytes = eight 16-byte chunks of 8 tokens.  Chunk c of feature f
+// sits at 16-byte unit f*8 + (c ^ s(f)), s(f) = ((f >> 1) ^ (f >> 3)) & 7:
+// fragment reads (16 lanes on consecutive features) touch 16 distinct bank
+// groups, the transposed stores (16 lanes on features 8l + i) at most two per
+// group.
 __device__ __forceinline__ int panel_offset_bytes(int f, int c) {
-  return ((f << 2) | (c ^ ((f >> 2) & 3))) << 4;
+  return ((f << 3) | (c ^ (((f >> 1) ^ (f >> 3)) & 7))) << 4;
 }
 
 // Upper-triangle tile enumeration: t -> (ti, tj), ti <= tj, row by row.
@@ -68,12 +69,26 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const u32x4& a, const u32x4& b, 
   }
 }
 
+// 8x8 transpose of 16-bit values: in[t] holds features 0..7 of token t (two per
+// dword, lower feature in the low half); out[f] holds tokens 0..7 of feature f.
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t lo = in[2 * d][f >> 1];      // token 2d
+      const uint32_t hi = in[2 * d + 1][f >> 1];  // token 2d+1
+      out[f][d] = (f & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    }
+  }
+}
+
 // grid.x = upper 128x128 tiles; 256 threads.
 template <int DT>
 __global__ void __launch_bounds__(256) syrk_mfma_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int n, int64_t tokens, int nt, int vec_ok,
     double alpha, double beta, double* __restrict__ H) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTile * kKStep * 2];  // 32 KB
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTile * kKStep * 2];  // 64 KB
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -82,58 +97,41 @@ __global__ void __launch_bounds__(256) syrk_mfma_kernel(
   upper_tile(blockIdx.x, nt, ti, tj);
   const bool diag = (ti == tj);
 
-  // Loader units: u = tid + 256*k (k = 0, 1) -> feature pair fp = u & 63,
-  // panel p = (u >> 6) & 1, token group tg = u >> 7 (8 tokens each).
-  int ld_fp[2], ld_p[2], ld_tg[2], ld_feat[2];
-  bool ld_on[2], ld_vec[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int u = tid + 256 * k;
-    ld_fp[k] = u & 63;
-    ld_p[k] = (u >> 6) & 1;
-    ld_tg[k] = u >> 7;
-    ld_feat[k] = (ld_p[k] ? tj : ti) * kTile + 2 * ld_fp[k];
-    ld_on[k] = !(diag && ld_p[k] == 1);
-    ld_vec[k] = vec_ok && (ld_feat[k] + 2 <= n);
-  }
+  // Loader: thread -> feature octet fo (16 per panel), panel p, token octet to
+  // (8 per stage).  Eight 16-byte loads (8 tokens x 8 features) per stage.
+  const int fo = tid & 15;
+  const int ld_p = (tid >> 4) & 1;
+  const int to = tid >> 5;
+  const int ld_feat = (ld_p ? tj : ti) * kTile + 8 * fo;
+  const bool ld_on = !(diag && ld_p == 1);
+  const bool ld_vec = vec_ok && (ld_feat + 8 <= n);
 
-  uint32_t regs[2][8];
-  auto global_load = [&](int64_t t0) {
+  auto global_load = [&](u32x4 (&regs)[8], int64_t t0) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int e = 0; e < 8; ++e) {
+      const int64_t t = t0 + to * 8 + e;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ld_on && t < tokens) {
+        const uint16_t* p = X + t * ldx + ld_feat;
+        if (ld_vec) {
+          v = *reinterpret_cast<const u32x4*>(p);
+        } else {
+          uint16_t tmp[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int64_t t = t0 + ld_tg[k] * 8 + e;
-        uint32_t v = 0u;
-        if (ld_on[k] && t < tokens) {
-          const uint16_t* p = X + t * ldx + ld_feat[k];
-          if (ld_vec[k]) {
-            v = *reinterpret_cast<const uint32_t*>(p);
-          } else {
-            const uint32_t lo = (ld_feat[k] < n) ? p[0] : 0u;
-            const uint32_t hi = (ld_feat[k] + 1 < n) ? p[1] : 0u;
-            v = lo | (hi << 16);
-          }
+          for (int q = 0; q < 8; ++q) tmp[q] = (ld_feat + q < n) ? p[q] : 0;
+          __builtin_memcpy(&v, tmp, 16);
         }
-        regs[k][e] = v;
       }
+      regs[e] = v;
     }
   };
-  auto lds_store = [&](int buf) {
+  auto lds_store = [&](const u32x4 (&regs)[8], int buf) {
+    if (!ld_on) return;
+    u32x4 out[8];
+    transpose8x8(regs, out);
+    uint8_t* base = lds[buf][ld_p];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      if (!ld_on[k]) continue;
-      u32x4 f0, f1;  // tokens 0..7 of features 2fp and 2fp+1
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t lo = regs[k][2 * d], hi = regs[k][2 * d + 1];
-        f0[d] = (lo & 0xFFFFu) | (hi << 16);
-        f1[d] = (lo >> 16) | (hi & 0xFFFF0000u);
-      }
-      uint8_t* base = lds[buf][ld_p[k]];
-      *reinterpret_cast<u32x4*>(base + panel_offset_bytes(2 * ld_fp[k], ld_tg[k])) = f0;
-      *reinterpret_cast<u32x4*>(base + panel_offset_bytes(2 * ld_fp[k] + 1, ld_tg[k])) = f1;
-    }
+    for (int f = 0; f < 8; ++f) *reinterpret_cast<u32x4*>(base + panel_offset_bytes(8 * fo + f, to)) = out[f];
   };
 
   const int wm = wave >> 1;
@@ -151,18 +149,11 @@ __global__ void __launch_bounds__(256) syrk_mfma_kernel(
       }
 
   const int b_panel = diag ? 0 : 1;
-  global_load(0);
-  lds_store(0);
-  __syncthreads();
-  int buf = 0;
-  int step = 0;
-  for (int64_t t0 = 0; t0 < tokens; t0 += kKStep) {
-    const bool more = (t0 + kKStep < tokens);
-    if (more) global_load(t0 + kKStep);
+  auto compute = [&](int buf) {
     const uint8_t* pa = lds[buf][0];
     const uint8_t* pb = lds[buf][b_panel];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < kKStep / 16; ++kk) {
       const int c = kk * 2 + (lane >> 5);
       u32x4 fa[2], fb[2];
 #pragma unroll
@@ -176,24 +167,46 @@ __global__ void __launch_bounds__(256) syrk_mfma_kernel(
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16<DT>(fa[i], fb[j], acc[i][j]);
     }
-    if (++step == kFlushSteps || !more) {
-      step = 0;
+  };
+  int step = 0;
+  auto flush = [&]() {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            master[i][j][r] += static_cast<double>(acc[i][j][r]);
-            acc[i][j][r] = 0.0f;
-          }
-    }
-    if (more) {
-      lds_store(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-    }
+        for (int r = 0; r < 16; ++r) {
+          master[i][j][r] += static_cast<double>(acc[i][j][r]);
+          acc[i][j][r] = 0.0f;
+        }
+  };
+
+  // Pipeline: stage s computes from LDS buffer s%2 while stages s+1 and s+2 are
+  // in registers (ra, rb) or in flight.
+  const int64_t nstages = (tokens + kKStep - 1) / kKStep;
+  u32x4 ra[8], rb[8];
+  global_load(ra, 0);
+  lds_store(ra, 0);
+  global_load(ra, kKStep);
+  global_load(rb, 2 * kKStep);
+  __syncthreads();
+  for (int64_t s = 0; s < nstages; s += 2) {
+    // even stage s: buffer 0; next data in ra
+    compute(0);
+    if (++step == kFlushSteps) { flush(); step = 0; }
+    if (s + 1 >= nstages) break;
+    lds_store(ra, 1);
+    global_load(ra, (s + 3) * kKStep);
+    __syncthreads();
+    // odd stage s+1: buffer 1; next data in rb
+    compute(1);
+    if (++step == kFlushSteps) { flush(); step = 0; }
+    if (s + 2 >= nstages) break;
+    lds_store(rb, 0);
+    global_load(rb, (s + 4) * kKStep);
+    __syncthreads();
   }
+  flush();
 
   // Epilogue.  MFMA 32x32 output layout: accumulator r of lane l is row
   // 8*(r/4) + 4*(l/32) + r%4, column l%32 of the 32x32 block.
@@ -296,7 +309,7 @@ hipError_t launch_hessian(double* H, int64_t n, const void* X, int dt, int64_t t
   }
   const int nt = static_cast<int>((n + kTile - 1) / kTile);
   const unsigned ntiles = static_cast<unsigned>(upper_tiles(nt));
-  const int vec_ok = (ldx % 2 == 0) && (reinterpret_cast<uintptr_t>(X) % 4 == 0);
+  const int vec_ok = (ldx % 8 == 0) && (reinterpret_cast<uintptr_t>(X) % 16 == 0);
   if (dt == DT_BF16) {
     hipLaunchKernelGGL(syrk_mfma_kernel<DT_BF16>, dim3(ntiles), dim3(256), 0, s,
                        static_cast<const uint16_t*>(X), ldx, static_cast<int>(n), tokens, nt, vec_ok,

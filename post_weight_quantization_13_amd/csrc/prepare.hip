@@ -14,8 +14,8 @@
 // enough codes to matter; U is rounded to fp32 at the end.
 //
 // Blocked right-looking Cholesky with 64x64 blocks, per block column k:
-//   chol_diag  one workgroup factors A_kk in LDS and inverts L_kk (written to
-//              the diagonal block of Linv),
+//   chol_diag  one wave factors A_kk (rows in registers),
+//   diag_inv   one wave inverts L_kk into the diagonal block of Linv,
 //   chol_trsm  L_ik = A_ik inv(L_kk)^T for every block row i > k  (fp64 MFMA),
 //   chol_syrk  A_ij -= L_ik L_jk^T for k < j <= i                   (fp64 MFMA).
 // Triangular inverse by recursive doubling: with the diagonal blocks already
@@ -108,65 +108,92 @@ __global__ void prep_gather_kernel(const double* __restrict__ H, const int32_t* 
 }
 
 // ---------------------------------------------------------------- diagonal block
-// Factor the 64x64 diagonal block k in LDS (rows/cols beyond n are identity),
-// write L_kk back to A and inv(L_kk) to the diagonal block of Linv.
-__global__ void __launch_bounds__(256) chol_diag_kernel(double* __restrict__ A, double* __restrict__ Linv,
-                                                        int n, int k, int* __restrict__ info) {
-  __shared__ double a[kB][kB + 1];
-  __shared__ double xs[kB][kB + 1];
-  __shared__ double rinv[kB];
-  const int tid = threadIdx.x;
+// Factor the 64x64 diagonal block k (rows/cols beyond n are identity) and
+// write L_kk back to A; a second kernel writes inv(L_kk) to the diagonal block
+// of Linv.  One wave each.
+// Factorization, right-looking, lane i keeps row i in registers: for column j
+// the pivot comes from lane j (readlane), each lane scales its entry, the
+// column goes through LDS and every lane applies the rank-1 update to its row.
+// Inverse, lane c keeps column c of inv(L) in registers:
+//   x_r = (delta_rc - sum_{q<r} l_rq x_q) / l_rr, rows of L read as LDS broadcasts.
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(b), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(b >> 32), lane);
+  return __longlong_as_double((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__global__ void __launch_bounds__(64) chol_diag_kernel(double* __restrict__ A, int n, int k,
+                                                       int* __restrict__ info) {
+  __shared__ __attribute__((aligned(16))) double col[2][kB];
+  const int i = threadIdx.x;
   const int r0 = k * kB;
   const int m = (n - r0 < kB) ? n - r0 : kB;
-  for (int e = tid; e < kB * kB; e += 256) {
-    const int i = e / kB, j = e % kB;
-    double v;
-    if (i < m && j < m) v = (j <= i) ? A[static_cast<int64_t>(r0 + i) * n + r0 + j] : 0.0;
-    else v = (i == j) ? 1.0 : 0.0;
-    a[i][j] = v;
+  const double* arow = A + static_cast<int64_t>(r0 + i) * n + r0;
+  double a[kB];
+#pragma unroll
+  for (int c = 0; c < kB; ++c) {
+    double v = (i == c) ? 1.0 : 0.0;
+    if (i < m && c < m && c <= i) v = arow[c];
+    a[c] = v;
   }
-  __syncthreads();
+  int bad = 0;
+#pragma unroll
   for (int j = 0; j < kB; ++j) {
-    if (tid == 0) {
-      double p = a[j][j];
-      if (!(p > 0.0) || !(p < INFINITY)) {
-        atomicOr(info, 1);
-        p = 1.0;
-      }
-      a[j][j] = sqrt(p);
+    double piv = readlane_f64(a[j], j);
+    if (!(piv > 0.0) || !(piv < INFINITY)) {  // uniform across the wave
+      bad = 1;
+      piv = 1.0;
     }
-    __syncthreads();
-    const double d = a[j][j];
-    for (int i = j + 1 + tid; i < kB; i += 256) a[i][j] = a[i][j] / d;
-    __syncthreads();
-    const int w = kB - 1 - j;  // trailing size
-    for (int e = tid; e < w * w; e += 256) {
-      const int i = j + 1 + e / w, c = j + 1 + e % w;
-      if (c <= i) a[i][c] -= a[i][j] * a[c][j];
-    }
-    __syncthreads();
+    const double rs = 1.0 / sqrt(piv);
+    const double l = a[j] * rs;
+    a[j] = l;
+    col[j & 1][i] = l;
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the column is in LDS
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int c = j + 1; c < kB; ++c) a[c] = fma(-l, col[j & 1][c], a[c]);
   }
-  for (int i = tid; i < kB; i += 256) rinv[i] = 1.0 / a[i][i];
+  if (bad && i == 0) atomicOr(info, 1);
+  double* wrow = A + static_cast<int64_t>(r0 + i) * n + r0;
+#pragma unroll
+  for (int c = 0; c < kB; ++c)
+    if (i < m && c < m && c <= i) wrow[c] = a[c];
+}
+
+// inv(L_kk) into the diagonal block of Linv; lane c keeps column c in registers.
+__global__ void __launch_bounds__(64) diag_inv_kernel(const double* __restrict__ A, double* __restrict__ Linv,
+                                                      int n, int k) {
+  __shared__ __attribute__((aligned(16))) double Ls[kB][kB];
+  __shared__ double rinv[kB];
+  const int i = threadIdx.x;
+  const int r0 = k * kB;
+  const int m = (n - r0 < kB) ? n - r0 : kB;
+  for (int c = 0; c < kB; ++c) {
+    double v = (i == c) ? 1.0 : 0.0;
+    if (i < m && c < m && c <= i) v = A[static_cast<int64_t>(r0 + i) * n + r0 + c];
+    Ls[i][c] = v;
+  }
+  rinv[i] = 1.0 / Ls[i][i];
   __syncthreads();
-  // Inverse: thread c owns column c of inv(L) (kept in LDS):
-  // x[i][c] = (delta_ic - sum_{c <= q < i} l_iq x[q][c]) / l_ii.
-  if (tid < kB) {
-    const int c = tid;
-    for (int i = 0; i < kB; ++i) {
-      double acc = (i == c) ? 1.0 : 0.0;
-      for (int q = c; q < i; ++q) acc -= a[i][q] * xs[q][c];
-      xs[i][c] = (i >= c) ? acc * rinv[i] : 0.0;
+  const int cc = i;
+  double x[kB];
+#pragma unroll
+  for (int r = 0; r < kB; ++r) {
+    double acc0 = (r == cc) ? 1.0 : 0.0, acc1 = 0.0;
+#pragma unroll
+    for (int q = 0; q < r; q += 2) {
+      acc0 = fma(-Ls[r][q], x[q], acc0);
+      if (q + 1 < r) acc1 = fma(-Ls[r][q + 1], x[q + 1], acc1);
     }
+    x[r] = (r >= cc) ? (acc0 + acc1) * rinv[r] : 0.0;
   }
+  __syncthreads();  // L no longer needed: the block goes out through LDS
+#pragma unroll
+  for (int r = 0; r < kB; ++r) Ls[r][cc] = x[r];
   __syncthreads();
-  for (int e = tid; e < m * m; e += 256) {
-    const int i = e / m, c = e % m;
-    Linv[static_cast<int64_t>(r0 + i) * n + r0 + c] = xs[i][c];
-  }
-  for (int e = tid; e < m * m; e += 256) {
-    const int i = e / m, j = e % m;
-    if (j <= i) A[static_cast<int64_t>(r0 + i) * n + r0 + j] = a[i][j];
-  }
+  for (int r = 0; r < m; ++r)
+    if (cc < m) Linv[static_cast<int64_t>(r0 + r) * n + r0 + cc] = Ls[r][cc];
 }
 
 // ---------------------------------------------------------------- fp64 MFMA tile
@@ -395,7 +422,9 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
 
   const int nblk = (n + kB - 1) / kB;
   for (int k = 0; k < nblk; ++k) {
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, s, A, Linv, n, k, info);
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(64), 0, s, A, n, k, info);
+    GPTQ_CHECK_LAUNCH();
+    hipLaunchKernelGGL(diag_inv_kernel, dim3(1), dim3(64), 0, s, A, Linv, n, k);
     GPTQ_CHECK_LAUNCH();
     const int rest = nblk - k - 1;
     if (rest > 0) {
