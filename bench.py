@@ -149,6 +149,7 @@ def main() -> int:
     perm = torch.empty(n, dtype=torch.int32, device=dev)
     dead = torch.empty(n, dtype=torch.uint8, device=dev)
     qweight, scales, zeros, g_idx = g.alloc_outputs(rows, n, cfg, dev)
+    ws_h = g.hessian_workspace(n, X)
     ws_p = g.workspace(g.gptq_prepare_workspace_bytes(n, cfg), dev)
     ws_q = g.workspace(g.gptq_quantize_workspace_bytes(rows, n, cfg), dev)
     torch.cuda.synchronize()
@@ -159,7 +160,7 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         for _ in range(3):
-            g.gptq_hessian_accumulate(H, 0, X)
+            g.gptq_hessian_accumulate(H, 0, X, ws_h)
         torch.cuda.synchronize()
         _log("pmc probe done: 1 GiB copy + 3 Hessian launches")
         return 0
@@ -167,7 +168,7 @@ def main() -> int:
     def step():
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         ev[0].record()
-        g.gptq_hessian_accumulate(H, 0, X)
+        g.gptq_hessian_accumulate(H, 0, X, ws_h)
         ev[1].record()
         g.gptq_prepare_hinv(H, cfg, U, perm, dead, ws_p)
         ev[2].record()

@@ -79,8 +79,10 @@ typedef struct {
  *   n_tokens HOST int64 in/out: running token count, updated on success.
  *   X        device [tokens, ldx] of dtype xdt (bf16, fp16 or fp32), ldx >= n;
  *            only columns 0..n-1 are read.  Not modified.
- *   workspace, ws_bytes: currently gptq_hessian_workspace_bytes() == 0 and
- *            NULL is accepted.
+ *   workspace, ws_bytes: device scratch of at least
+ *            gptq_hessian_workspace_bytes(n, tokens, xdt) bytes (token pieces of
+ *            the tiles that do not fill the last round of the current device's
+ *            compute units); NULL is accepted when that size is 0.
  * bf16/fp16 products are summed by MFMA with fp32 accumulation in chains of at
  * most gptq_hessian_chain_tokens() tokens; chains are combined in fp64, which
  * is also the storage precision of H (GPTQ's codes react to Hessian error far

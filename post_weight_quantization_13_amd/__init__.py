@@ -156,9 +156,13 @@ def gptq_hessian_chain_tokens() -> int:
     return lib().gptq_hessian_chain_tokens()
 
 
-def gptq_hessian_accumulate(H, n_tokens: int, X, workspace=None, stream=None) -> int:
-    """H (float64 [n, n], device) <- running mean of 2 x x^T; returns the new token count."""
+def gptq_hessian_accumulate(H, n_tokens: int, X, workspace="auto", stream=None) -> int:
+    """H (float64 [n, n], device) <- running mean of 2 x x^T; returns the new token count.
+
+    workspace="auto" allocates the scratch the call needs (a torch tensor)."""
     n = H.shape[0]
+    if isinstance(workspace, str):
+        workspace = hessian_workspace(n, X) if X.shape[0] > 0 else None
     ldx = _row_major_2d(X, "X")
     cnt = ctypes.c_int64(int(n_tokens))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -224,7 +228,14 @@ def hessian(X, H=None, n_tokens: int = 0):
     n = X.shape[1]
     if H is None:
         H = torch.empty((n, n), dtype=torch.float64, device=X.device)
-    return H, gptq_hessian_accumulate(H, n_tokens, X)
+    ws = hessian_workspace(n, X)
+    return H, gptq_hessian_accumulate(H, n_tokens, X, ws)
+
+
+def hessian_workspace(n: int, X):
+    """Workspace tensor (or None) for accumulating X into an n x n Hessian."""
+    nb = gptq_hessian_workspace_bytes(n, X.shape[0], _dtype_code(X))
+    return workspace(nb, X.device) if nb else None
 
 
 def prepare(H, cfg):

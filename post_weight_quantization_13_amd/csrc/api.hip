@@ -12,7 +12,8 @@
 
 namespace gptq {
 hipError_t launch_hessian(double* H, int64_t n, const void* X, int dt, int64_t tokens, int64_t ldx, double alpha,
-                          double beta, hipStream_t s);
+                          double beta, void* ws, hipStream_t s);
+size_t hessian_workspace(int64_t n, int64_t tokens, int dt);
 int64_t hessian_chain_tokens();
 size_t prepare_workspace(int64_t n);
 hipError_t launch_prepare(const double* H, int64_t n, double damp, int desc_act, float* U, int32_t* perm,
@@ -80,10 +81,8 @@ const char* gptq_version(void) { return "gptq-gfx950 0.1.0"; }
 
 // ----------------------------------------------------------------------------- Hessian
 size_t gptq_hessian_workspace_bytes(int64_t n, int64_t tokens, gptq_dtype xdt) {
-  (void)n;
-  (void)tokens;
-  (void)xdt;
-  return 0;
+  if (n < 1 || n > kMaxDim || tokens < 1 || !valid_dtype(xdt)) return 0;
+  return gptq::hessian_workspace(n, tokens, static_cast<int>(xdt));
 }
 
 int64_t gptq_hessian_chain_tokens(void) { return gptq::hessian_chain_tokens(); }
@@ -91,8 +90,6 @@ int64_t gptq_hessian_chain_tokens(void) { return gptq::hessian_chain_tokens(); }
 gptq_status gptq_hessian_accumulate(double* H, int64_t n, int64_t* n_tokens, const void* X, gptq_dtype xdt,
                                     int64_t tokens, int64_t ldx, void* workspace, size_t ws_bytes,
                                     void* stream) {
-  (void)workspace;
-  (void)ws_bytes;
   if (!H) return fail(GPTQ_ERR_INVALID_ARG, "H is NULL");
   if (!n_tokens) return fail(GPTQ_ERR_INVALID_ARG, "n_tokens is NULL");
   if (n < 1 || n > kMaxDim) return fail(GPTQ_ERR_INVALID_ARG, "n=%lld out of range", (long long)n);
@@ -102,11 +99,14 @@ gptq_status gptq_hessian_accumulate(double* H, int64_t n, int64_t* n_tokens, con
   if (tokens == 0) return ok();
   if (!X) return fail(GPTQ_ERR_INVALID_ARG, "X is NULL");
   if (ldx < n) return fail(GPTQ_ERR_INVALID_ARG, "ldx=%lld < n=%lld", (long long)ldx, (long long)n);
+  const size_t need = gptq::hessian_workspace(n, tokens, static_cast<int>(xdt));
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace ? ws_bytes : 0, need);
   const int64_t n_old = *n_tokens;
   const int64_t n_new = n_old + tokens;
   const double alpha = 2.0 / static_cast<double>(n_new);
   const double beta = static_cast<double>(n_old) / static_cast<double>(n_new);
-  hipError_t e = gptq::launch_hessian(H, n, X, static_cast<int>(xdt), tokens, ldx, alpha, beta,
+  hipError_t e = gptq::launch_hessian(H, n, X, static_cast<int>(xdt), tokens, ldx, alpha, beta, workspace,
                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("gptq_hessian_accumulate", e);
   *n_tokens = n_new;

@@ -5,9 +5,10 @@
 // (kept here as a running mean over tokens).
 //
 // Design
-//   * One workgroup (4 waves) owns one 128x128 tile (I, J), I <= J, of the upper
-//     triangle and walks the whole token range.  Each wave computes a 64x64
-//     quarter with bf16/fp16 MFMA (v_mfma_f32_32x32x16, 2x2 MFMA tiles).
+//   * A workgroup (4 waves) computes 128x128 tiles (I, J), I <= J, of the upper
+//     triangle over the whole token range.  Each wave computes a 64x64 quarter
+//     with bf16/fp16 MFMA (v_mfma_f32_32x32x16, 2x2 MFMA tiles).  The launch is
+//     persistent and balanced (see syrk_mfma_kernel).
 //   * Precision: the fp32 MFMA accumulators are flushed into an fp64 master
 //     copy (in registers) every kFlushSteps stages of 64 tokens, so no fp32
 //     accumulation chain is longer than 256 tokens.  The codes GPTQ
@@ -19,8 +20,8 @@
 //     features (eight 16-byte loads), transposes the 8x8 block of 16-bit
 //     values in registers and stores 8 feature rows of 8 consecutive tokens
 //     into LDS, so each MFMA operand fragment (8 consecutive tokens of one
-//     feature) is a single 16-byte LDS read.  LDS is double buffered and two
-//     further stages are held in registers / in flight ahead of the MFMAs.
+//     feature) is a single 16-byte LDS read.  LDS is double buffered and one
+//     further stage is in flight into registers ahead of the MFMAs.
 //   * Epilogue: H <- beta*H + alpha*master; each element is written once and
 //     mirrored through LDS so H is exactly symmetric and both writes coalesce.
 //   * fp32 inputs use a VALU kernel accumulating in fp64.
@@ -83,36 +84,69 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
   }
 }
 
-// grid.x = upper 128x128 tiles; 256 threads.
-template <int DT>
-__global__ void __launch_bounds__(256) syrk_mfma_kernel(
-    const uint16_t* __restrict__ X, int64_t ldx, int n, int64_t tokens, int nt, int vec_ok,
-    double alpha, double beta, double* __restrict__ H) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTile * kKStep * 2];  // 64 KB
+// Schedule order of the upper-triangle tiles: super-blocks of 4 tile-rows x 8
+// tile-columns, row-major over the super-blocks that meet the triangle, tiles
+// row-major inside each.  A run of 32 consecutive indices (one XCD's share of
+// a round) then needs about 12 panels of X instead of 33, so the XCD's L2
+// serves most operand loads.  index -> (ti, tj), O(#super-blocks).
+__device__ void sched_tile(int idx, int nt, int& ti, int& tj) {
+  const int nsr = (nt + 3) / 4, nsc = (nt + 7) / 8;
+  int rem = idx;
+  ti = 0;
+  tj = 0;
+  for (int SR = 0; SR < nsr; ++SR) {
+    const int a_end = (4 * SR + 4 < nt) ? 4 * SR + 4 : nt;
+    for (int SC = SR / 2; SC < nsc; ++SC) {
+      const int c_hi = (8 * SC + 8 < nt) ? 8 * SC + 8 : nt;
+      for (int a = 4 * SR; a < a_end; ++a) {
+        const int lo = (a > 8 * SC) ? a : 8 * SC;
+        const int cnt = (c_hi > lo) ? c_hi - lo : 0;
+        if (rem < cnt) {
+          ti = a;
+          tj = lo + rem;
+          return;
+        }
+        rem -= cnt;
+      }
+    }
+  }
+}
 
+struct TileCtx {
+  const uint16_t* X;
+  int64_t ldx;
+  int n;
+  int vec_ok;
+  uint8_t* lds;  // 2 buffers x 2 panels x 16 KB
+};
+
+// master (this wave's 64x64 quarter, fp64) += X[t0:t1, I]^T X[t0:t1, J] for
+// tile (ti, tj).  Pipeline: stage s computes from LDS buffer s%2 while stage
+// s+1 waits in LDS and stage s+2 is in flight into registers; fp32 chains are
+// flushed every 256 tokens.
+template <int DT>
+__device__ __forceinline__ void tile_accumulate(const TileCtx& cx, int ti, int tj, int64_t t0, int64_t t1,
+                                                double (&master)[2][2][16]) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  int ti, tj;
-  upper_tile(blockIdx.x, nt, ti, tj);
   const bool diag = (ti == tj);
-
-  // Loader: thread -> feature octet fo (16 per panel), panel p, token octet to
-  // (8 per stage).  Eight 16-byte loads (8 tokens x 8 features) per stage.
+  const int n = cx.n;
   const int fo = tid & 15;
   const int ld_p = (tid >> 4) & 1;
   const int to = tid >> 5;
   const int ld_feat = (ld_p ? tj : ti) * kTile + 8 * fo;
   const bool ld_on = !(diag && ld_p == 1);
-  const bool ld_vec = vec_ok && (ld_feat + 8 <= n);
+  const bool ld_vec = cx.vec_ok && (ld_feat + 8 <= n);
+  auto panel = [&](int buf, int p) { return cx.lds + (buf * 2 + p) * (kTile * kKStep * 2); };
 
-  auto global_load = [&](u32x4 (&regs)[8], int64_t t0) {
+  auto global_load = [&](u32x4 (&regs)[8], int64_t ts) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int64_t t = t0 + to * 8 + e;
+      const int64_t t = ts + to * 8 + e;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (ld_on && t < tokens) {
-        const uint16_t* p = X + t * ldx + ld_feat;
+      if (ld_on && t < t1) {
+        const uint16_t* p = cx.X + t * cx.ldx + ld_feat;
         if (ld_vec) {
           v = *reinterpret_cast<const u32x4*>(p);
         } else {
@@ -129,7 +163,7 @@ __global__ void __launch_bounds__(256) syrk_mfma_kernel(
     if (!ld_on) return;
     u32x4 out[8];
     transpose8x8(regs, out);
-    uint8_t* base = lds[buf][ld_p];
+    uint8_t* base = panel(buf, ld_p);
 #pragma unroll
     for (int f = 0; f < 8; ++f) *reinterpret_cast<u32x4*>(base + panel_offset_bytes(8 * fo + f, to)) = out[f];
   };
@@ -137,21 +171,16 @@ __global__ void __launch_bounds__(256) syrk_mfma_kernel(
   const int wm = wave >> 1;
   const int wn = wave & 1;
   f32x16 acc[2][2];
-  double master[2][2][16];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acc[i][j][r] = 0.0f;
-        master[i][j][r] = 0.0;
-      }
-
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   const int b_panel = diag ? 0 : 1;
   auto compute = [&](int buf) {
-    const uint8_t* pa = lds[buf][0];
-    const uint8_t* pb = lds[buf][b_panel];
+    const uint8_t* pa = panel(buf, 0);
+    const uint8_t* pb = panel(buf, b_panel);
 #pragma unroll
     for (int kk = 0; kk < kKStep / 16; ++kk) {
       const int c = kk * 2 + (lane >> 5);
@@ -181,39 +210,43 @@ __global__ void __launch_bounds__(256) syrk_mfma_kernel(
         }
   };
 
-  // Pipeline: stage s computes from LDS buffer s%2 while stages s+1 and s+2 are
-  // in registers (ra, rb) or in flight.
-  const int64_t nstages = (tokens + kKStep - 1) / kKStep;
-  u32x4 ra[8], rb[8];
-  global_load(ra, 0);
+  const int64_t nstages = (t1 - t0 + kKStep - 1) / kKStep;
+  if (nstages <= 0) return;
+  u32x4 ra[8];
+  global_load(ra, t0);
   lds_store(ra, 0);
-  global_load(ra, kKStep);
-  global_load(rb, 2 * kKStep);
+  global_load(ra, t0 + kKStep);
   __syncthreads();
-  for (int64_t s = 0; s < nstages; s += 2) {
-    // even stage s: buffer 0; next data in ra
-    compute(0);
-    if (++step == kFlushSteps) { flush(); step = 0; }
+  int buf = 0;
+  for (int64_t s = 0; s < nstages; ++s) {
+    compute(buf);
+    if (++step == kFlushSteps) {
+      flush();
+      step = 0;
+    }
     if (s + 1 >= nstages) break;
-    lds_store(ra, 1);
-    global_load(ra, (s + 3) * kKStep);
+    lds_store(ra, buf ^ 1);
+    global_load(ra, t0 + (s + 2) * kKStep);
     __syncthreads();
-    // odd stage s+1: buffer 1; next data in rb
-    compute(1);
-    if (++step == kFlushSteps) { flush(); step = 0; }
-    if (s + 2 >= nstages) break;
-    lds_store(rb, 0);
-    global_load(rb, (s + 4) * kKStep);
-    __syncthreads();
+    buf ^= 1;
   }
   flush();
+  __syncthreads();  // staging buffers free for the next user
+}
 
-  // Epilogue.  MFMA 32x32 output layout: accumulator r of lane l is row
-  // 8*(r/4) + 4*(l/32) + r%4, column l%32 of the 32x32 block.
-  __syncthreads();  // every wave is done with the staging buffers
-  double* stage = reinterpret_cast<double*>(&lds[0][0][0]);  // 64x64 fp64 = 32 KB
+// H <- beta*H + alpha*master for tile (ti, tj): each element written once, the
+// mirror staged through LDS (64x64 fp64 per wave quarter) so both writes coalesce.
+// MFMA 32x32 output layout: accumulator r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
+// column l%32 of the 32x32 block.
+__device__ __forceinline__ void tile_epilogue(const double (&master)[2][2][16], int ti, int tj, int n,
+                                              double alpha, double beta, double* __restrict__ H, uint8_t* lds) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const bool diag = (ti == tj);
+  double* stage = reinterpret_cast<double*>(lds);  // 32 KB
   for (int w = 0; w < 4; ++w) {
-    const int rw = (w >> 1) * 64, cw = (w & 1) * 64;  // quarter owned by wave w
+    const int rw = (w >> 1) * 64, cw = (w & 1) * 64;
     if (wave == w) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -230,17 +263,114 @@ __global__ void __launch_bounds__(256) syrk_mfma_kernel(
               if (beta != 0.0) v += beta * H[static_cast<int64_t>(gi) * n + gj];
               H[static_cast<int64_t>(gi) * n + gj] = v;
             }
-            stage[lc * 64 + (lr ^ (lc & 63))] = v;  // transposed, XOR-swizzled
+            stage[lc * 64 + (lr ^ (lc & 63))] = v;
           }
     }
     __syncthreads();
-    // Mirror: H[gj][gi] for the quarter, rows of the mirror are lc.
     for (int e = tid; e < 64 * 64; e += 256) {
       const int lc = e >> 6, lr = e & 63;
       const int gi = ti * kTile + rw + lr, gj = tj * kTile + cw + lc;
       if (gi < n && gj < n && gi < gj) H[static_cast<int64_t>(gj) * n + gi] = stage[lc * 64 + (lr ^ (lc & 63))];
     }
     __syncthreads();
+  }
+}
+
+// Raw fp64 partial tile (row-major 128x128) for a token piece of a leftover tile.
+__device__ __forceinline__ void tile_store_partial(const double (&master)[2][2][16], double* __restrict__ dst) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int col = wn * 64 + j * 32 + (lane & 31);
+        dst[row * kTile + col] = master[i][j][r];
+      }
+}
+
+// Balanced launch over T = nt(nt+1)/2 tiles with P = min(T, #CUs): a first
+// launch of R*P workgroups (R = T / P) runs whole tiles, one per workgroup, in
+// R rounds; the workgroups of round r take schedule indices r*P + slot, the
+// slot chosen so that the 32 workgroups one XCD receives share a compact
+// group of tiles.  The L = T % P leftover tiles are cut into S = P / L token
+// pieces, one per workgroup of a second launch, whose fp64 partials
+// syrk_reduce_kernel sums in a fixed order (S == 1: the pieces are whole tiles).
+struct HessSched {
+  int nt, T, P, R, L, S;
+  int64_t chunk;  // tokens per piece
+};
+
+template <int DT>
+__global__ void __launch_bounds__(256) syrk_mfma_kernel(const uint16_t* __restrict__ X, int64_t ldx, int n,
+                                                        int64_t tokens, HessSched sc, int pieces, int vec_ok,
+                                                        double alpha, double beta, double* __restrict__ H,
+                                                        double* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 2 * kTile * kKStep * 2];  // 64 KB
+  const TileCtx cx{X, ldx, n, vec_ok, lds};
+  const int b = blockIdx.x;
+  int idx;
+  int64_t p0 = 0, p1 = tokens;
+  bool partial_out = false;
+  if (!pieces) {
+    const int r = b / sc.P, s = b % sc.P;
+    idx = r * sc.P + ((sc.P % 8 == 0) ? (s % 8) * (sc.P / 8) + s / 8 : s);
+  } else {
+    idx = sc.R * sc.P + b / sc.S;
+    if (sc.S > 1) {
+      partial_out = true;
+      p0 = (b % sc.S) * sc.chunk;
+      p1 = (p0 + sc.chunk < tokens) ? p0 + sc.chunk : tokens;
+    }
+  }
+  int ti, tj;
+  sched_tile(idx, sc.nt, ti, tj);
+  double master[2][2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) master[i][j][e] = 0.0;
+  tile_accumulate<DT>(cx, ti, tj, p0, p1, master);
+  if (partial_out) tile_store_partial(master, partial + static_cast<int64_t>(b) * kTile * kTile);
+  else tile_epilogue(master, ti, tj, n, alpha, beta, H, lds);
+}
+
+// Leftover tiles split into S pieces: sum the pieces in piece order (fp64),
+// apply H <- beta*H + alpha*sum, write tile and mirror.  grid = (L, 4 quarters).
+__global__ void __launch_bounds__(256) syrk_reduce_kernel(const double* __restrict__ partial, HessSched sc, int n,
+                                                          double alpha, double beta, double* __restrict__ H) {
+  __shared__ double stage[64 * 64];
+  const int q = blockIdx.x;
+  const int w = blockIdx.y;
+  int ti, tj;
+  sched_tile(sc.R * sc.P + q, sc.nt, ti, tj);
+  const bool diag = (ti == tj);
+  const int rw = (w >> 1) * 64, cw = (w & 1) * 64;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int lr = e >> 6, lc = e & 63;
+    const int gi = ti * kTile + rw + lr, gj = tj * kTile + cw + lc;
+    double s = 0.0;
+    for (int p = 0; p < sc.S; ++p)
+      s += partial[static_cast<int64_t>(q * sc.S + p) * kTile * kTile + (rw + lr) * kTile + cw + lc];
+    double v = alpha * s;
+    if (gi < n && gj < n && !(diag && gi > gj)) {
+      if (beta != 0.0) v += beta * H[static_cast<int64_t>(gi) * n + gj];
+      H[static_cast<int64_t>(gi) * n + gj] = v;
+    }
+    stage[lc * 64 + (lr ^ lc)] = v;
+  }
+  __syncthreads();
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int lc = e >> 6, lr = e & 63;
+    const int gi = ti * kTile + rw + lr, gj = tj * kTile + cw + lc;
+    if (gi < n && gj < n && gi < gj) H[static_cast<int64_t>(gj) * n + gi] = stage[lc * 64 + (lr ^ lc)];
   }
 }
 
@@ -298,27 +428,62 @@ static inline int64_t upper_tiles(int64_t nt) { return nt * (nt + 1) / 2; }
 
 int64_t hessian_chain_tokens() { return static_cast<int64_t>(kFlushSteps) * kKStep; }
 
-hipError_t launch_hessian(double* H, int64_t n, const void* X, int dt, int64_t tokens,
-                          int64_t ldx, double alpha, double beta, hipStream_t s) {
+static int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+  return cus;
+}
+
+static HessSched make_sched(int64_t n, int64_t tokens) {
+  HessSched sc{};
+  sc.nt = static_cast<int>((n + kTile - 1) / kTile);
+  sc.T = static_cast<int>(upper_tiles(sc.nt));
+  const int cus = device_cus();
+  sc.P = sc.T < cus ? sc.T : cus;
+  sc.R = sc.T / sc.P;
+  sc.L = sc.T % sc.P;
+  sc.S = sc.L > 0 ? sc.P / sc.L : 0;
+  if (sc.S > 1) {
+    const int64_t per = (tokens + sc.S - 1) / sc.S;
+    const int64_t chain = hessian_chain_tokens();
+    sc.chunk = (per + chain - 1) / chain * chain;
+  } else {
+    sc.chunk = tokens;
+  }
+  return sc;
+}
+
+size_t hessian_workspace(int64_t n, int64_t tokens, int dt) {
+  if (dt == DT_FP32 || n <= 0 || tokens <= 0) return 0;
+  const HessSched sc = make_sched(n, tokens);
+  if (sc.S <= 1) return 0;
+  return static_cast<size_t>(sc.L) * sc.S * kTile * kTile * sizeof(double);
+}
+
+hipError_t launch_hessian(double* H, int64_t n, const void* X, int dt, int64_t tokens, int64_t ldx, double alpha,
+                          double beta, void* ws, hipStream_t s) {
   if (dt == DT_FP32) {
     const int nt64 = static_cast<int>((n + 63) / 64);
     hipLaunchKernelGGL(syrk_f32_kernel, dim3(static_cast<unsigned>(upper_tiles(nt64))), dim3(256), 0, s,
-                       static_cast<const float*>(X), ldx, static_cast<int>(n), tokens, nt64, alpha,
-                       beta, H);
+                       static_cast<const float*>(X), ldx, static_cast<int>(n), tokens, nt64, alpha, beta, H);
     return hipGetLastError();
   }
-  const int nt = static_cast<int>((n + kTile - 1) / kTile);
-  const unsigned ntiles = static_cast<unsigned>(upper_tiles(nt));
+  const HessSched sc = make_sched(n, tokens);
   const int vec_ok = (ldx % 8 == 0) && (reinterpret_cast<uintptr_t>(X) % 16 == 0);
-  if (dt == DT_BF16) {
-    hipLaunchKernelGGL(syrk_mfma_kernel<DT_BF16>, dim3(ntiles), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(X), ldx, static_cast<int>(n), tokens, nt, vec_ok,
-                       alpha, beta, H);
-  } else {
-    hipLaunchKernelGGL(syrk_mfma_kernel<DT_FP16>, dim3(ntiles), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(X), ldx, static_cast<int>(n), tokens, nt, vec_ok,
-                       alpha, beta, H);
-  }
+  double* partial = static_cast<double*>(ws);
+  auto kern = (dt == DT_BF16) ? syrk_mfma_kernel<DT_BF16> : syrk_mfma_kernel<DT_FP16>;
+  const uint16_t* Xp = static_cast<const uint16_t*>(X);
+  hipLaunchKernelGGL(kern, dim3(sc.R * sc.P), dim3(256), 0, s, Xp, ldx, static_cast<int>(n), tokens, sc, 0, vec_ok,
+                     alpha, beta, H, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sc.L == 0) return e;
+  hipLaunchKernelGGL(kern, dim3(sc.L * sc.S), dim3(256), 0, s, Xp, ldx, static_cast<int>(n), tokens, sc, 1, vec_ok,
+                     alpha, beta, H, partial);
+  e = hipGetLastError();
+  if (e != hipSuccess || sc.S <= 1) return e;
+  hipLaunchKernelGGL(syrk_reduce_kernel, dim3(sc.L, 4), dim3(256), 0, s, partial, sc, static_cast<int>(n), alpha,
+                     beta, H);
   return hipGetLastError();
 }
 

@@ -38,7 +38,10 @@ def test_exports_every_declared_symbol(g):
 
 def test_workspace_queries(g):
     cfg = g.Config()
-    assert g.gptq_hessian_workspace_bytes(4096, 65536, g.GPTQ_BF16) == 0
+    # 528 tiles on 256 compute units: 16 leftover tiles in 16 token pieces of 128x128 fp64
+    assert g.gptq_hessian_workspace_bytes(4096, 65536, g.GPTQ_BF16) == 16 * 16 * 128 * 128 * 8
+    assert g.gptq_hessian_workspace_bytes(4096, 65536, g.GPTQ_FP32) == 0
+    assert g.gptq_hessian_workspace_bytes(256, 65536, g.GPTQ_BF16) == 0   # 3 tiles: one round
     assert g.gptq_hessian_chain_tokens() == 256
     assert g.gptq_prepare_workspace_bytes(4096, cfg) >= 2 * 4096 * 4096 * 8
     assert g.gptq_quantize_workspace_bytes(4096, 4096, cfg) >= 4096 * 4096 * 5
