@@ -248,6 +248,19 @@ __device__ __forceinline__ void tile_epilogue(const double (&master)[2][2][16], 
   for (int w = 0; w < 4; ++w) {
     const int rw = (w >> 1) * 64, cw = (w & 1) * 64;
     if (wave == w) {
+      double old[2][2][16];  // previous H, all loads issued before any store
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int lr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int lc = j * 32 + (lane & 31);
+            const int gi = ti * kTile + rw + lr, gj = tj * kTile + cw + lc;
+            const bool own = gi < n && gj < n && !(diag && gi > gj);
+            old[i][j][r] = (beta != 0.0 && own) ? H[static_cast<int64_t>(gi) * n + gj] : 0.0;
+          }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -260,7 +273,7 @@ __device__ __forceinline__ void tile_epilogue(const double (&master)[2][2][16], 
             double v = alpha * master[i][j][r];
             const bool own = gi < n && gj < n && !(diag && gi > gj);
             if (own) {
-              if (beta != 0.0) v += beta * H[static_cast<int64_t>(gi) * n + gj];
+              if (beta != 0.0) v += beta * old[i][j][r];
               H[static_cast<int64_t>(gi) * n + gj] = v;
             }
             stage[lc * 64 + (lr ^ (lc & 63))] = v;

@@ -270,6 +270,38 @@ __device__ __forceinline__ void tile_foreach(const f64x4 (&acc)[2][2], F f) {
         f(wm * 32 + i * 16 + (lane >> 4) + 4 * r, wn * 32 + j * 16 + (lane & 15), acc[i][j][r]);
 }
 
+// The same element map with a second accumulator-shaped array.
+template <typename F>
+__device__ __forceinline__ void tile_foreach2(const f64x4 (&acc)[2][2], const f64x4 (&o)[2][2], F f) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        f(wm * 32 + i * 16 + (lane >> 4) + 4 * r, wn * 32 + j * 16 + (lane & 15), acc[i][j][r], o[i][j][r]);
+}
+
+// Loads the 64x64 tile at p (row stride ld) in accumulator layout, all loads
+// issued before anything else touches memory; rows >= mv or columns >= nv read 0.
+__device__ __forceinline__ void tile_load(f64x4 (&o)[2][2], const double* p, int64_t ld, int mv, int nv) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = wm * 32 + i * 16 + (lane >> 4) + 4 * r, cc = wn * 32 + j * 16 + (lane & 15);
+        o[i][j][r] = (rr < mv && cc < nv) ? p[static_cast<int64_t>(rr) * ld + cc] : 0.0;
+      }
+}
+
 __device__ __forceinline__ void zero_acc(f64x4 (&acc)[2][2]) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -317,11 +349,11 @@ __global__ void __launch_bounds__(256) chol_syrk_kernel(double* __restrict__ A, 
   tile_gemm_f64<true>(A + static_cast<int64_t>(r0) * n + k0, n, A + static_cast<int64_t>(cc0) * n + k0, n,
                       mv, nv, 0, kv, acc, sm);
   __syncthreads();
-  tile_foreach(acc, [&](int r, int c, double v) {
-    if (r < mv && c < nv && (i != j || c <= r)) {
-      double* p = A + static_cast<int64_t>(r0 + r) * n + cc0 + c;
-      *p -= v;
-    }
+  // all loads of the tile issued before any store (see tile_load)
+  f64x4 old[2][2];
+  tile_load(old, A + static_cast<int64_t>(r0) * n + cc0, n, mv, nv);
+  tile_foreach2(acc, old, [&](int r, int c, double v, double o) {
+    if (r < mv && c < nv && (i != j || c <= r)) A[static_cast<int64_t>(r0 + r) * n + cc0 + c] = o - v;
   });
 }
 

@@ -17,12 +17,16 @@
 // Kernels, per layer:
 //   gather_w      W (bf16/fp16/fp32, original order) -> Wk fp32 [rows, n] in sweep
 //                 order, dead columns zeroed.
-//   sweep_block   one block of 128 columns for 64 rows per workgroup (lane = row):
-//                 group scale/zero, the sequential quantize/compensate chain, codes,
-//                 E for the block, fp16 scale/zero, per-row loss.
-//   trailing      Wk[:, i2:] -= E U[i1:i2, i2:] with fp32 MFMA (v_mfma_f32_32x32x2f32).
+//   sweep_block   one block of 128 columns for 64 rows per workgroup (lane = row;
+//                 one wave runs the sequential chain, three apply its errors):
+//                 group scale/zero, quantize/compensate, codes, E for the block,
+//                 fp16 scale/zero, per-row loss.
+//   trailing      Wk[:, i2:] -= E U[i1:i2, i2:] as a split-bf16 product on the bf16
+//                 MFMA (three products per operand pair, fp32 accumulation).
 //   pack          codes back to the original column order, little-endian bit stream
 //                 per row, int32 words.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace gptq {
@@ -55,120 +59,285 @@ __global__ void gidx_kernel(const int32_t* __restrict__ perm, int n, int gs, int
 }
 
 // ---------------------------------------------------------------- sweep
-// Grid: ceil(rows / 64) workgroups of 64 threads (one wave).  LDS: the block
-// of U transposed (UT[k][j] = U[i1+j][i1+k], 64 KB) and the 64 x 128 block of
-// Wk column-major over lanes (32 KB).
+// One workgroup (4 waves) per strip of 64 rows and one block of 128 columns;
+// lane = row in every wave.  LDS: UT[k][j] = U[i1+j][i1+k] (the block of U,
+// transposed), the 64x128 block of Wk column-major over rows, and the errors
+// of the last two 16-column sub-blocks.
+// Sub-block s (16 columns), two barriers:
+//   wave 0   : the sequential chain -- quantize column j, e_j = (w - q) / U_jj,
+//              rank-1 update of the remaining columns of the sub-block (the
+//              16x16 block of U is read into registers first);
+//   waves 1-3: meanwhile apply the errors of sub-block s-1 to the columns past
+//              sub-block s+1 ("far" update);
+//   barrier; all waves apply the errors of sub-block s to the columns of
+//   sub-block s+1 ("near" update, which the next chain step needs); barrier.
+// Codes: c = clamp(rint(w / s) + z).  Each sub-block's chain first runs with
+// the quotient formed as w * (1/s).  If any quotient lay within 2^-18 of a
+// rounding midpoint (that form errs by at most ~2 ulp = 2^-18 for |w/s| < 16,
+// the only range where rint decides a code), the sub-block is replayed from
+// its saved inputs with IEEE division, so the codes equal those of a
+// correctly rounded w / s.  The fast path has no branch inside the chain.
+constexpr int kSubs = kBlk / kSub;  // 8
+
 template <int BITS, bool SYM>
-__global__ void __launch_bounds__(64) sweep_block_kernel(
+__global__ void __launch_bounds__(256) sweep_block_kernel(
     float* __restrict__ Wk, const float* __restrict__ U, int n, int rows, int i1,
     uint8_t* __restrict__ codes, float* __restrict__ E, uint16_t* __restrict__ scales,
     uint16_t* __restrict__ zeros, double* __restrict__ rowloss) {
-  __shared__ float UT[kBlk][kBlk];
+  __shared__ __attribute__((aligned(16))) float UT[kBlk][kBlk + 4];
   __shared__ float Ws[kBlk][kRowsSweep];
-  const int lane = threadIdx.x;
+  __shared__ float Es[2][kSub][kRowsSweep];
+  __shared__ float rdiag[kBlk];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int r = blockIdx.x * kRowsSweep + lane;
   const bool valid = r < rows;
 
-  for (int e = lane; e < kBlk * kBlk; e += 64) {
-    const int j = e / kBlk, k = e % kBlk;  // U row j, column k (coalesced read)
-    UT[k][j] = U[static_cast<int64_t>(i1 + j) * n + i1 + k];
-  }
-  if (valid) {
-    const float* wrow = Wk + static_cast<int64_t>(r) * n + i1;
-    for (int k = 0; k < kBlk; k += 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(wrow + k);
-      Ws[k][lane] = v[0];
-      Ws[k + 1][lane] = v[1];
-      Ws[k + 2][lane] = v[2];
-      Ws[k + 3][lane] = v[3];
+  // Staging: every global load of the block is issued before the LDS stores.
+  {
+    f32x4 ut[16];  // U rows: unit i -> row j = e4 / 32, columns 4*(e4 % 32) ..
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e4 = tid + 256 * i;
+      ut[i] = *reinterpret_cast<const f32x4*>(U + static_cast<int64_t>(i1 + (e4 >> 5)) * n + i1 + 4 * (e4 & 31));
     }
-  } else {
-    for (int k = 0; k < kBlk; ++k) Ws[k][lane] = 0.0f;
+    // Ws[k][row]: thread -> (row rr, quarter q of 32 columns)
+    const int rr = tid >> 2, q = tid & 3;
+    const int gr = blockIdx.x * kRowsSweep + rr;
+    f32x4 wv[8];
+#pragma unroll
+    for (int k4 = 0; k4 < 8; ++k4)
+      wv[k4] = (gr < rows) ? *reinterpret_cast<const f32x4*>(Wk + static_cast<int64_t>(gr) * n + i1 + q * 32 + 4 * k4)
+                           : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const float dg = (tid < kBlk) ? U[static_cast<int64_t>(i1 + tid) * n + i1 + tid] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e4 = tid + 256 * i;
+      const int j = e4 >> 5, k = 4 * (e4 & 31);
+      UT[k][j] = ut[i][0];
+      UT[k + 1][j] = ut[i][1];
+      UT[k + 2][j] = ut[i][2];
+      UT[k + 3][j] = ut[i][3];
+    }
+#pragma unroll
+    for (int k4 = 0; k4 < 8; ++k4) {
+      Ws[q * 32 + 4 * k4 + 0][rr] = wv[k4][0];
+      Ws[q * 32 + 4 * k4 + 1][rr] = wv[k4][1];
+      Ws[q * 32 + 4 * k4 + 2][rr] = wv[k4][2];
+      Ws[q * 32 + 4 * k4 + 3][rr] = wv[k4][3];
+    }
+    if (tid < kBlk) rdiag[tid] = 1.0f / dg;
   }
   __syncthreads();
 
-  // Group parameters from the block-entry values (group = block).
   constexpr float maxq = static_cast<float>((1 << BITS) - 1);
-  float xmin = 0.0f, xmax = 0.0f;
-  for (int k = 0; k < kBlk; ++k) {
-    const float v = Ws[k][lane];
-    xmin = fminf(xmin, v);
-    xmax = fmaxf(xmax, v);
-  }
-  if (xmin == 0.0f && xmax == 0.0f) {
-    xmin = -1.0f;
-    xmax = 1.0f;
-  }
-  float s, z;
-  if constexpr (SYM) {
-    const float a = fmaxf(-xmin, xmax);
-    s = a / static_cast<float>((1 << (BITS - 1)) - 1);
-    z = static_cast<float>(1 << (BITS - 1));
-  } else {
-    s = (xmax - xmin) / maxq;
-    z = rintf(-xmin / s);
-  }
   const float lo = SYM ? 1.0f : 0.0f;
-
+  float sv = 1.0f, zv = 0.0f, rs = 1.0f;
   double loss = 0.0;
+  if (wave == 0) {
+    // group parameters from the block-entry values (group = block)
+    float xmin = 0.0f, xmax = 0.0f;
+    for (int k = 0; k < kBlk; ++k) {
+      const float v = Ws[k][lane];
+      xmin = fminf(xmin, v);
+      xmax = fmaxf(xmax, v);
+    }
+    if (xmin == 0.0f && xmax == 0.0f) {
+      xmin = -1.0f;
+      xmax = 1.0f;
+    }
+    if constexpr (SYM) {
+      const float a = fmaxf(-xmin, xmax);
+      sv = a / static_cast<float>((1 << (BITS - 1)) - 1);
+      zv = static_cast<float>(1 << (BITS - 1));
+    } else {
+      sv = (xmax - xmin) / maxq;
+      zv = rintf(-xmin / sv);
+    }
+    rs = 1.0f / sv;
+  }
+
   float* erow = E + static_cast<int64_t>(valid ? r : 0) * kBlk;
   uint8_t* crow = codes + static_cast<int64_t>(valid ? r : 0) * n + i1;
-  for (int sb = 0; sb < kBlk / kSub; ++sb) {
+  for (int sb = 0; sb < kSubs; ++sb) {
     const int j0 = sb * kSub;
-    float w[kSub], e[kSub];
+    if (wave == 0) {
+      float w0[kSub];
 #pragma unroll
-    for (int t = 0; t < kSub; ++t) w[t] = Ws[j0 + t][lane];
+      for (int t = 0; t < kSub; ++t) w0[t] = Ws[j0 + t][lane];
+      // The 16x16 diagonal sub-block of U in registers (uniform values), read
+      // as LDS broadcasts: ub[t][u] = U[j0+t][j0+u] = UT[j0+u][j0+t].
+      float ub[kSub][kSub];
 #pragma unroll
-    for (int t = 0; t < kSub; ++t) {
-      const int j = j0 + t;
-      const float c = fminf(fmaxf(rintf(w[t] / s) + z, lo), maxq);
-      const float q = s * (c - z);
-      const float et = (w[t] - q) / UT[j][j];
-      e[t] = et;
-      loss += static_cast<double>(et) * static_cast<double>(et);
-      if (valid) crow[j] = static_cast<uint8_t>(c);
+      for (int u = 1; u < kSub; ++u) {
 #pragma unroll
-      for (int u = t + 1; u < kSub; ++u) w[u] = fmaf(-et, UT[j0 + u][j], w[u]);
-    }
-    if (valid) {
+        for (int t4 = 0; t4 < kSub / 4; ++t4) {
+          if (4 * t4 >= u) continue;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&UT[j0 + u][j0 + 4 * t4]);
+          ub[4 * t4][u] = v[0];
+          ub[4 * t4 + 1][u] = v[1];
+          ub[4 * t4 + 2][u] = v[2];
+          ub[4 * t4 + 3][u] = v[3];
+        }
+      }
+      // The chain of one sub-block.  EXACT = false forms w / s as w * (1/s)
+      // and reports whether any quotient came within 2^-18 of a rounding
+      // midpoint; EXACT = true uses IEEE division throughout.
+      auto chain = [&](auto exact_tag, uint32_t (&cw)[kSub / 4], float& lsum) -> bool {
+        constexpr bool EXACT = decltype(exact_tag)::value;
+        float w[kSub];
 #pragma unroll
-      for (int t = 0; t < kSub; t += 4) {
-        *reinterpret_cast<f32x4*>(erow + j0 + t) = f32x4{e[t], e[t + 1], e[t + 2], e[t + 3]};
+        for (int t = 0; t < kSub; ++t) w[t] = w0[t];
+        bool near = false;
+#pragma unroll
+        for (int t = 0; t < kSub; ++t) {
+          float qt;
+          if constexpr (EXACT) {
+            qt = w[t] / sv;
+          } else {
+            qt = w[t] * rs;
+            near |= fabsf(fabsf(qt - rintf(qt)) - 0.5f) < 3.814697265625e-06f;
+          }
+          const float c = fminf(fmaxf(rintf(qt) + zv, lo), maxq);
+          const float q = sv * (c - zv);
+          const float et = (w[t] - q) * rdiag[j0 + t];
+          Es[sb & 1][t][lane] = et;
+          lsum = fmaf(et, et, lsum);
+          cw[t >> 2] |= static_cast<uint32_t>(c) << (8 * (t & 3));
+#pragma unroll
+          for (int u = t + 1; u < kSub; ++u) w[u] = fmaf(-et, ub[t][u], w[u]);
+        }
+        return near;
+      };
+      uint32_t cw[kSub / 4] = {0u, 0u, 0u, 0u};
+      float lsum = 0.0f;
+      const bool near = chain(std::false_type{}, cw, lsum);
+      if (__builtin_expect(__any(near), 0)) {  // rare: replay with IEEE division
+#pragma unroll
+        for (int t4 = 0; t4 < kSub / 4; ++t4) cw[t4] = 0u;
+        lsum = 0.0f;
+        chain(std::true_type{}, cw, lsum);
+      }
+      loss += static_cast<double>(lsum);
+      if (valid) {
+#pragma unroll
+        for (int t4 = 0; t4 < kSub / 4; ++t4) {
+          *reinterpret_cast<uint32_t*>(crow + j0 + 4 * t4) = cw[t4];
+          *reinterpret_cast<f32x4*>(erow + j0 + 4 * t4) =
+              f32x4{Es[sb & 1][4 * t4][lane], Es[sb & 1][4 * t4 + 1][lane], Es[sb & 1][4 * t4 + 2][lane],
+                    Es[sb & 1][4 * t4 + 3][lane]};
+        }
+      }
+    } else if (sb >= 1) {
+      // far update: errors of sub-block sb-1 onto columns >= j0 + 16
+      const int jp = j0 - kSub;
+      float ep[kSub];
+#pragma unroll
+      for (int t = 0; t < kSub; ++t) ep[t] = Es[(sb - 1) & 1][t][lane];
+      // columns k = j0 + 16 + (wave-1) + 3m, four per pass with the loads first
+      for (int k = j0 + kSub + (wave - 1); k < kBlk; k += 12) {
+        float acc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = (k + 3 * q < kBlk) ? Ws[k + 3 * q][lane] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int kq = (k + 3 * q < kBlk) ? k + 3 * q : k;
+          const f32x4* uc = reinterpret_cast<const f32x4*>(&UT[kq][jp]);
+#pragma unroll
+          for (int t4 = 0; t4 < kSub / 4; ++t4) {
+            const f32x4 u = uc[t4];
+            acc[q] = fmaf(-ep[4 * t4 + 0], u[0], acc[q]);
+            acc[q] = fmaf(-ep[4 * t4 + 1], u[1], acc[q]);
+            acc[q] = fmaf(-ep[4 * t4 + 2], u[2], acc[q]);
+            acc[q] = fmaf(-ep[4 * t4 + 3], u[3], acc[q]);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (k + 3 * q < kBlk) Ws[k + 3 * q][lane] = acc[q];
       }
     }
-    // Apply this sub-block's errors to the rest of the block.
-    for (int k = j0 + kSub; k < kBlk; ++k) {
-      float acc = Ws[k][lane];
-      const f32x4* ucol = reinterpret_cast<const f32x4*>(&UT[k][j0]);
+    __syncthreads();
+    if (sb + 1 < kSubs) {
+      // near update: errors of sub-block sb onto the 16 columns of sub-block sb+1
+      float ec[kSub];
 #pragma unroll
-      for (int t4 = 0; t4 < kSub / 4; ++t4) {
-        const f32x4 u = ucol[t4];
-        acc = fmaf(-e[4 * t4 + 0], u[0], acc);
-        acc = fmaf(-e[4 * t4 + 1], u[1], acc);
-        acc = fmaf(-e[4 * t4 + 2], u[2], acc);
-        acc = fmaf(-e[4 * t4 + 3], u[3], acc);
+      for (int t = 0; t < kSub; ++t) ec[t] = Es[sb & 1][t][lane];
+      const int kn = j0 + kSub + wave * (kSub / 4);
+      float acc[kSub / 4];
+#pragma unroll
+      for (int kk = 0; kk < kSub / 4; ++kk) acc[kk] = Ws[kn + kk][lane];
+#pragma unroll
+      for (int kk = 0; kk < kSub / 4; ++kk) {
+        const f32x4* uc = reinterpret_cast<const f32x4*>(&UT[kn + kk][j0]);
+#pragma unroll
+        for (int t4 = 0; t4 < kSub / 4; ++t4) {
+          const f32x4 u = uc[t4];
+          acc[kk] = fmaf(-ec[4 * t4 + 0], u[0], acc[kk]);
+          acc[kk] = fmaf(-ec[4 * t4 + 1], u[1], acc[kk]);
+          acc[kk] = fmaf(-ec[4 * t4 + 2], u[2], acc[kk]);
+          acc[kk] = fmaf(-ec[4 * t4 + 3], u[3], acc[kk]);
+        }
       }
-      Ws[k][lane] = acc;
+#pragma unroll
+      for (int kk = 0; kk < kSub / 4; ++kk) Ws[kn + kk][lane] = acc[kk];
+      __syncthreads();
     }
   }
-  if (valid) {
+  if (wave == 0 && valid) {
     const int g = i1 / kBlk;
-    scales[static_cast<int64_t>(g) * rows + r] = float_to_half_bits(s);
-    zeros[static_cast<int64_t>(g) * rows + r] = float_to_half_bits(z);
+    scales[static_cast<int64_t>(g) * rows + r] = float_to_half_bits(sv);
+    zeros[static_cast<int64_t>(g) * rows + r] = float_to_half_bits(zv);
     rowloss[r] += 0.5 * loss;
   }
 }
 
 // ---------------------------------------------------------------- trailing update
 // Wk[r0:r0+128, c0:c0+128] -= E[r0:r0+128, 0:128] U[i1:i1+128, c0:c0+128],
-// c0 = i2 + 128*blockIdx.x, r0 = 128*blockIdx.y.  256 threads; wave (wm, wn)
-// owns a 64x64 quarter = 2x2 tiles of v_mfma_f32_32x32x2f32 (lane l supplies
-// A[l%32][l/32] and B[l/32][l%32]; accumulator r is D[8(r/4)+4(l/32)+r%4][l%32]).
+// c0 = i2 + 128*blockIdx.x, r0 = 128*blockIdx.y.
+// Split-bf16 product on the bf16 MFMA: each fp32 operand x = hi + lo with
+// hi = bf16(x), lo = bf16(x - hi) (round to nearest even), and
+//   E U ~ Ehi Uhi + Ehi Ulo + Elo Uhi   (fp32 accumulation),
+// which leaves a relative error near 2^-16 per product (the dropped Elo Ulo
+// term and the rounding of lo), against 2^-24 for an fp32 product.
+// K = 128 runs as two chunks of 64 staged in LDS as bf16 hi/lo planes: E as
+// [row][k], U transposed as [col][k], so each MFMA operand fragment (8
+// consecutive k) is one 16-byte read.  The 16-byte chunk c of a 128-byte row
+// r sits at slot c ^ (r & 7), which keeps the fragment reads conflict-free.
+// 256 threads; wave (wm, wn) owns a 64x64 quarter = 2x2 v_mfma_f32_32x32x16_bf16
+// tiles (accumulator q of lane l is row 8(q/4) + 4(l/32) + q%4, column l%32).
+constexpr int kTK = 64;
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// 8 fp32 values -> hi and lo bf16 planes (16 bytes each).
+__device__ __forceinline__ void split8(const float (&v)[8], u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t h0 = bf16_rne_bits(v[2 * d]), h1 = bf16_rne_bits(v[2 * d + 1]);
+    const uint32_t l0 = bf16_rne_bits(v[2 * d] - __uint_as_float(h0 << 16));
+    const uint32_t l1 = bf16_rne_bits(v[2 * d + 1] - __uint_as_float(h1 << 16));
+    hi[d] = h0 | (h1 << 16);
+    lo[d] = l0 | (l1 << 16);
+  }
+}
+
+__device__ __forceinline__ int tk_offset(int row, int c) { return row * (kTK * 2) + ((c ^ (row & 7)) << 4); }
+
+__device__ __forceinline__ f32x16 mfma_bf16(const u32x4& a, const u32x4& b, f32x16 c) {
+  bf16x8 av, bv;
+  __builtin_memcpy(&av, &a, 16);
+  __builtin_memcpy(&bv, &b, 16);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
+}
+
 __global__ void __launch_bounds__(256) trailing_kernel(float* __restrict__ Wk, const float* __restrict__ E,
                                                        const float* __restrict__ U, int n, int rows, int i1,
                                                        int i2) {
-  __shared__ float sE[128][33];
-  __shared__ float sU[32][129];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4][128 * kTK * 2];  // Ehi, Elo, Uhi, Ulo: 64 KB
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
@@ -182,33 +351,84 @@ __global__ void __launch_bounds__(256) trailing_kernel(float* __restrict__ Wk, c
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  for (int kc = 0; kc < kBlk; kc += 32) {
-    __syncthreads();
-    for (int e = tid; e < 128 * 32; e += 256) {
-      const int m = e >> 5, kk = e & 31;
-      const int rr = r0 + m;
-      sE[m][kk] = (rr < rows) ? E[static_cast<int64_t>(rr) * kBlk + kc + kk] : 0.0f;
-    }
-    for (int e = tid; e < 32 * 128; e += 256) {
-      const int kk = e >> 7, c = e & 127;
-      const int cc = c0 + c;
-      sU[kk][c] = (cc < n) ? U[static_cast<int64_t>(i1 + kc + kk) * n + cc] : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int ks = 0; ks < 16; ++ks) {
-      const int kk = ks * 2 + (lane >> 5);
-      float fa[2], fb[2];
+  for (int kc = 0; kc < kBlk; kc += kTK) {
+    // Staging: all global loads of the chunk first, then split and store.
+    float ev[4][8], uv[4][8];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = sE[wm * 64 + i * 32 + (lane & 31)][kk];
+    for (int q = 0; q < 4; ++q) {
+      // E: unit -> (row, k-octet); 8 consecutive k of one row
+      const int u = tid + 256 * q;
+      const int row = u >> 3, ko = u & 7;
+      if (r0 + row < rows) {
+        const float* src = E + static_cast<int64_t>(r0 + row) * kBlk + kc + 8 * ko;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+        ev[q][0] = a[0]; ev[q][1] = a[1]; ev[q][2] = a[2]; ev[q][3] = a[3];
+        ev[q][4] = b[0]; ev[q][5] = b[1]; ev[q][6] = b[2]; ev[q][7] = b[3];
+      } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = sU[kk][wn * 64 + j * 32 + (lane & 31)];
+        for (int e = 0; e < 8; ++e) ev[q][e] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // U: unit -> (col, k-octet); 8 rows of U at one column, transposed into LDS
+      const int u = tid + 256 * q;
+      const int col = u & 127, ko = u >> 7;
+      const bool ok = c0 + col < n;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        uv[q][e] = ok ? U[static_cast<int64_t>(i1 + kc + 8 * ko + e) * n + c0 + col] : 0.0f;
+    }
+    if (kc) __syncthreads();  // the previous chunk's fragments have been read
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int u = tid + 256 * q;
+      const int row = u >> 3, ko = u & 7;
+      u32x4 hi, lo;
+      split8(ev[q], hi, lo);
+      *reinterpret_cast<u32x4*>(lds[0] + tk_offset(row, ko)) = hi;
+      *reinterpret_cast<u32x4*>(lds[1] + tk_offset(row, ko)) = lo;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int u = tid + 256 * q;
+      const int col = u & 127, ko = u >> 7;
+      u32x4 hi, lo;
+      split8(uv[q], hi, lo);
+      *reinterpret_cast<u32x4*>(lds[2] + tk_offset(col, ko)) = hi;
+      *reinterpret_cast<u32x4*>(lds[3] + tk_offset(col, ko)) = lo;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kTK / 16; ++kk) {
+      const int c = kk * 2 + (lane >> 5);
+      u32x4 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int m = wm * 64 + i * 32 + (lane & 31);
+        ah[i] = *reinterpret_cast<const u32x4*>(lds[0] + tk_offset(m, c));
+        al[i] = *reinterpret_cast<const u32x4*>(lds[1] + tk_offset(m, c));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int cc = wn * 64 + j * 32 + (lane & 31);
+        bh[j] = *reinterpret_cast<const u32x4*>(lds[2] + tk_offset(cc, c));
+        bl[j] = *reinterpret_cast<const u32x4*>(lds[3] + tk_offset(cc, c));
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = mfma_bf16(al[i], bh[j], acc[i][j]);
+          acc[i][j] = mfma_bf16(ah[i], bl[j], acc[i][j]);
+          acc[i][j] = mfma_bf16(ah[i], bh[j], acc[i][j]);
+        }
     }
   }
+  // Epilogue: all 64 loads of this lane's W values are issued before any store
+  // (a load after a store to the same array would otherwise wait for it).
+  float old[2][2][16];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -217,7 +437,17 @@ __global__ void __launch_bounds__(256) trailing_kernel(float* __restrict__ Wk, c
       for (int q = 0; q < 16; ++q) {
         const int rr = r0 + wm * 64 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
         const int cc = c0 + wn * 64 + j * 32 + (lane & 31);
-        if (rr < rows && cc < n) Wk[static_cast<int64_t>(rr) * n + cc] -= acc[i][j][q];
+        old[i][j][q] = (rr < rows && cc < n) ? Wk[static_cast<int64_t>(rr) * n + cc] : 0.0f;
+      }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int rr = r0 + wm * 64 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+        const int cc = c0 + wn * 64 + j * 32 + (lane & 31);
+        if (rr < rows && cc < n) Wk[static_cast<int64_t>(rr) * n + cc] = old[i][j][q] - acc[i][j][q];
       }
 }
 
@@ -276,7 +506,7 @@ size_t quantize_workspace(int64_t rows, int64_t n) {
 template <int BITS, bool SYM>
 static void launch_sweep(dim3 g, hipStream_t s, float* Wk, const float* U, int n, int rows, int i1, uint8_t* codes,
                          float* E, uint16_t* scales, uint16_t* zeros, double* rowloss) {
-  hipLaunchKernelGGL((sweep_block_kernel<BITS, SYM>), g, dim3(64), 0, s, Wk, U, n, rows, i1, codes, E, scales,
+  hipLaunchKernelGGL((sweep_block_kernel<BITS, SYM>), g, dim3(256), 0, s, Wk, U, n, rows, i1, codes, E, scales,
                      zeros, rowloss);
 }
 
