@@ -222,3 +222,39 @@ def test_abi_edge_cases(g):
     with pytest.raises(g.GptqError) as ei:
         g.quantize_layer(U, perm, dead, g.Config(bits=2), W)
     assert ei.value.status == g.GPTQ_ERR_UNSUPPORTED
+
+
+def _midpoint_cases(count, seed=0):
+    """(xmax, w) pairs, 0 <= w <= xmax, for which rint(w * (1/s)) != rint(w / s)
+    in fp32 with s = xmax / 15: the reciprocal form would pick the other code."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    out = []
+    while len(out) < count:
+        xmax = f32(rng.uniform(0.01, 0.05))
+        s = f32(xmax) / f32(15)
+        k = rng.integers(0, 15, size=4000)
+        w = ((k + 0.5) * np.float64(s)).astype(np.float32)
+        bad = np.nonzero(np.rint(w / s) != np.rint(w * (f32(1) / s)))[0]
+        out += [(xmax, w[b]) for b in bad[:1] if w[b] <= xmax]
+    return out
+
+
+def test_quantizer_exact_division_near_midpoints(g):
+    import torch
+    rows, n = 24, 256
+    rng = np.random.default_rng(5)
+    W = (rng.random((rows, n)) * 0.01).astype(np.float32)       # all >= 0: xmin = 0, z = 0
+    for r, (xmax, w) in enumerate(_midpoint_cases(rows)):
+        W[r, :128] = np.minimum(W[r, :128], xmax)
+        W[r, 0] = xmax                                          # group max -> s = xmax / 15
+        W[r, 77] = w                                            # a quotient the reciprocal rounds wrong
+    cfg = g.Config(bits=4, sym=False)
+    U, perm, dead = g.prepare(torch.eye(n, dtype=torch.float64, device="cuda"), cfg)
+    out = g.quantize_layer(U, perm, dead, cfg, torch.from_numpy(W).cuda())
+    r = oracle.rtn(W.astype(np.float64), oracle.QuantConfig(bits=4), qdtype=np.float32)
+    codes = oracle.unpack(out["qweight"].cpu().numpy(), 4, n)
+    s = r["S"][0]
+    fast = np.rint(W[:, 77] * (np.float32(1) / s))
+    assert np.all(fast != np.rint(W[:, 77] / s))                # the planted cases are real
+    assert np.array_equal(codes, r["codes"])
