@@ -5,18 +5,19 @@
 // (kept here as a running mean over tokens).
 //
 // Design
-//   * A workgroup (4 waves) computes 128x128 tiles (I, J), I <= J, of the upper
-//     triangle over the whole token range.  Each wave computes a 64x64 quarter
-//     with bf16/fp16 MFMA (v_mfma_f32_32x32x16, 2x2 MFMA tiles).  The launch is
-//     persistent and balanced (see syrk_mfma_kernel).
+//   * A workgroup of 8 waves (two per SIMD, so one wave's MFMAs overlap the
+//     other's LDS and memory work) computes 128x128 tiles (I, J), I <= J, of
+//     the upper triangle over the whole token range.  Each wave computes a
+//     64x32 block with bf16/fp16 MFMA (v_mfma_f32_32x32x16, 2x1 MFMA tiles).
+//     The launch is balanced over the compute units (see syrk_mfma_kernel).
 //   * Precision: the fp32 MFMA accumulators are flushed into an fp64 master
-//     copy (in registers) every kFlushSteps stages of 64 tokens, so no fp32
+//     copy (in registers) every kFlushSteps stages of 128 tokens, so no fp32
 //     accumulation chain is longer than 256 tokens.  The codes GPTQ
 //     produces are very sensitive to Hessian error (one flipped code changes
 //     the rest of its row), and long fp32 chains measurably lower agreement
 //     with an exact Hessian; short chains summed in fp64 do not.  H is stored
 //     in fp64 for the same reason.
-//   * Operand staging: per stage of 64 tokens every thread loads 8 tokens x 8
+//   * Operand staging: per stage of 128 tokens every thread loads 8 tokens x 8
 //     features (eight 16-byte loads), transposes the 8x8 block of 16-bit
 //     values in registers and stores 8 feature rows of 8 consecutive tokens
 //     into LDS, so each MFMA operand fragment (8 consecutive tokens of one
@@ -30,17 +31,18 @@
 namespace gptq {
 
 constexpr int kTile = 128;       // output tile edge (features)
-constexpr int kKStep = 64;       // tokens per LDS stage
-constexpr int kFlushSteps = 4;   // stages per fp32 chain: 4 x 64 = 256 tokens (16 MFMAs)
+constexpr int kKStep = 128;      // tokens per LDS stage
+constexpr int kFlushSteps = 2;   // stages per fp32 chain: 2 x 128 = 256 tokens (16 MFMAs)
+constexpr int kThreads = 512;    // 8 waves
 
-// LDS panel: kTile features x kKStep tokens of 16-bit values = 16 KB; a feature
-// row is 128 bytes = eight 16-byte chunks of 8 tokens.  Chunk c of feature f
-// sits at 16-byte unit f*8 + (c ^ s(f)), s(f) = ((f >> 1) ^ (f >> 3)) & 7:
-// fragment reads (16 lanes on consecutive features) touch 16 distinct bank
-// groups, the transposed stores (16 lanes on features 8l + i) at most two per
-// group.
+// LDS panel: kTile features x kKStep tokens of 16-bit values = 32 KB; a feature
+// row is 256 bytes = sixteen 16-byte chunks of 8 tokens.  Chunk c of feature f
+// sits at 16-byte unit f*16 + (c ^ s(f)), s(f) = (f ^ (f >> 4)) & 15: fragment
+// reads (16 lanes on 16 consecutive features, one chunk) and the transposed
+// stores (16 lanes on features 8l + q, one chunk) each touch 16 distinct
+// 16-byte bank groups.
 __device__ __forceinline__ int panel_offset_bytes(int f, int c) {
-  return ((f << 3) | (c ^ (((f >> 1) ^ (f >> 3)) & 7))) << 4;
+  return ((f << 4) | (c ^ ((f ^ (f >> 4)) & 15))) << 4;
 }
 
 // Upper-triangle tile enumeration: t -> (ti, tj), ti <= tj, row by row.
@@ -117,33 +119,47 @@ struct TileCtx {
   int64_t ldx;
   int n;
   int vec_ok;
-  uint8_t* lds;  // 2 buffers x 2 panels x 16 KB
+  uint8_t* lds;  // 2 buffers x 2 panels x 32 KB
 };
 
-// master (this wave's 64x64 quarter, fp64) += X[t0:t1, I]^T X[t0:t1, J] for
+// Wave w of the workgroup owns rows 64*(w & 1) .. +63 and columns
+// 32*(w >> 1) .. +31 of the 128x128 tile.  MFMA 32x32 output layout:
+// accumulator r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+__device__ __forceinline__ int acc_row(int i, int r, int lane) {
+  return i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+}
+
+// master (this wave's 64x32 block, fp64) += X[t0:t1, I]^T X[t0:t1, J] for
 // tile (ti, tj).  Pipeline: stage s computes from LDS buffer s%2 while stage
 // s+1 waits in LDS and stage s+2 is in flight into registers; fp32 chains are
 // flushed every 256 tokens.
 template <int DT>
 __device__ __forceinline__ void tile_accumulate(const TileCtx& cx, int ti, int tj, int64_t t0, int64_t t1,
-                                                double (&master)[2][2][16]) {
+                                                double (&master)[2][16]) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const bool diag = (ti == tj);
   const int n = cx.n;
-  const int fo = tid & 15;
-  const int ld_p = (tid >> 4) & 1;
-  const int to = tid >> 5;
+  const int fo = tid & 15;          // 8-feature chunk this thread loads
+  const int to = (tid >> 4) & 15;   // 8-token group this thread loads
+  const int ld_p = tid >> 8;        // panel: 0 = rows (I), 1 = columns (J)
   const int ld_feat = (ld_p ? tj : ti) * kTile + 8 * fo;
   const bool ld_on = !(diag && ld_p == 1);
-  const bool ld_vec = cx.vec_ok && (ld_feat + 8 <= n);
+  const bool ld_vec = ld_on && cx.vec_ok && (ld_feat + 8 <= n);
   auto panel = [&](int buf, int p) { return cx.lds + (buf * 2 + p) * (kTile * kKStep * 2); };
 
   auto global_load = [&](u32x4 (&regs)[8], int64_t ts) {
+    const int64_t tb = ts + to * 8;
+    if (ld_vec && tb + 8 <= t1) {
+      const uint16_t* p = cx.X + tb * cx.ldx + ld_feat;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) regs[e] = *reinterpret_cast<const u32x4*>(p + e * cx.ldx);
+      return;
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int64_t t = ts + to * 8 + e;
+      const int64_t t = tb + e;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (ld_on && t < t1) {
         const uint16_t* p = cx.X + t * cx.ldx + ld_feat;
@@ -168,15 +184,13 @@ __device__ __forceinline__ void tile_accumulate(const TileCtx& cx, int ti, int t
     for (int f = 0; f < 8; ++f) *reinterpret_cast<u32x4*>(base + panel_offset_bytes(8 * fo + f, to)) = out[f];
   };
 
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  f32x16 acc[2][2];
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+  f32x16 acc[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
   const int b_panel = diag ? 0 : 1;
   auto compute = [&](int buf) {
     const uint8_t* pa = panel(buf, 0);
@@ -184,17 +198,13 @@ __device__ __forceinline__ void tile_accumulate(const TileCtx& cx, int ti, int t
 #pragma unroll
     for (int kk = 0; kk < kKStep / 16; ++kk) {
       const int c = kk * 2 + (lane >> 5);
-      u32x4 fa[2], fb[2];
+      u32x4 fa[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         fa[i] = *reinterpret_cast<const u32x4*>(pa + panel_offset_bytes(wm * 64 + i * 32 + (lane & 31), c));
+      const u32x4 fb = *reinterpret_cast<const u32x4*>(pb + panel_offset_bytes(wn * 32 + (lane & 31), c));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = *reinterpret_cast<const u32x4*>(pb + panel_offset_bytes(wn * 64 + j * 32 + (lane & 31), c));
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16<DT>(fa[i], fb[j], acc[i][j]);
+      for (int i = 0; i < 2; ++i) acc[i] = mfma_32x32x16<DT>(fa[i], fb, acc[i]);
     }
   };
   int step = 0;
@@ -202,12 +212,10 @@ __device__ __forceinline__ void tile_accumulate(const TileCtx& cx, int ti, int t
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          master[i][j][r] += static_cast<double>(acc[i][j][r]);
-          acc[i][j][r] = 0.0f;
-        }
+      for (int r = 0; r < 16; ++r) {
+        master[i][r] += static_cast<double>(acc[i][r]);
+        acc[i][r] = 0.0f;
+      }
   };
 
   const int64_t nstages = (t1 - t0 + kKStep - 1) / kKStep;
@@ -235,75 +243,58 @@ __device__ __forceinline__ void tile_accumulate(const TileCtx& cx, int ti, int t
 }
 
 // H <- beta*H + alpha*master for tile (ti, tj): each element written once, the
-// mirror staged through LDS (64x64 fp64 per wave quarter) so both writes coalesce.
-// MFMA 32x32 output layout: accumulator r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
-// column l%32 of the 32x32 block.
-__device__ __forceinline__ void tile_epilogue(const double (&master)[2][2][16], int ti, int tj, int n,
-                                              double alpha, double beta, double* __restrict__ H, uint8_t* lds) {
+// mirror staged through LDS (the whole 128x128 fp64 tile, transposed, 128 KB)
+// so both writes coalesce.
+__device__ __forceinline__ void tile_epilogue(const double (&master)[2][16], int ti, int tj, int n, double alpha,
+                                              double beta, double* __restrict__ H, uint8_t* lds) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const bool diag = (ti == tj);
-  double* stage = reinterpret_cast<double*>(lds);  // 32 KB
-  for (int w = 0; w < 4; ++w) {
-    const int rw = (w >> 1) * 64, cw = (w & 1) * 64;
-    if (wave == w) {
-      double old[2][2][16];  // previous H, all loads issued before any store
+  const int rw = (wave & 1) * 64, cw = (wave >> 1) * 32;
+  double* stage = reinterpret_cast<double*>(lds);  // [column][row ^ column], 128 KB
+  const int lc = cw + (lane & 31);
+  const int gj = tj * kTile + lc;
+  double old[2][16];  // previous H, all loads issued before any store
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int lr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            const int lc = j * 32 + (lane & 31);
-            const int gi = ti * kTile + rw + lr, gj = tj * kTile + cw + lc;
-            const bool own = gi < n && gj < n && !(diag && gi > gj);
-            old[i][j][r] = (beta != 0.0 && own) ? H[static_cast<int64_t>(gi) * n + gj] : 0.0;
-          }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int lr = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            const int lc = j * 32 + (lane & 31);
-            const int gi = ti * kTile + rw + lr, gj = tj * kTile + cw + lc;
-            double v = alpha * master[i][j][r];
-            const bool own = gi < n && gj < n && !(diag && gi > gj);
-            if (own) {
-              if (beta != 0.0) v += beta * old[i][j][r];
-              H[static_cast<int64_t>(gi) * n + gj] = v;
-            }
-            stage[lc * 64 + (lr ^ (lc & 63))] = v;
-          }
+    for (int r = 0; r < 16; ++r) {
+      const int gi = ti * kTile + rw + acc_row(i, r, lane);
+      const bool own = gi < n && gj < n && !(diag && gi > gj);
+      old[i][r] = (beta != 0.0 && own) ? H[static_cast<int64_t>(gi) * n + gj] : 0.0;
     }
-    __syncthreads();
-    for (int e = tid; e < 64 * 64; e += 256) {
-      const int lc = e >> 6, lr = e & 63;
-      const int gi = ti * kTile + rw + lr, gj = tj * kTile + cw + lc;
-      if (gi < n && gj < n && gi < gj) H[static_cast<int64_t>(gj) * n + gi] = stage[lc * 64 + (lr ^ (lc & 63))];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int lr = rw + acc_row(i, r, lane);
+      const int gi = ti * kTile + lr;
+      double v = alpha * master[i][r];
+      const bool own = gi < n && gj < n && !(diag && gi > gj);
+      if (own) {
+        if (beta != 0.0) v += beta * old[i][r];
+        H[static_cast<int64_t>(gi) * n + gj] = v;
+      }
+      stage[lc * kTile + (lr ^ lc)] = v;
     }
-    __syncthreads();
+  __syncthreads();
+  for (int e = tid; e < kTile * kTile; e += kThreads) {
+    const int c = e >> 7, r = e & 127;
+    const int gi = ti * kTile + r, gjj = tj * kTile + c;
+    if (gi < n && gjj < n && gi < gjj) H[static_cast<int64_t>(gjj) * n + gi] = stage[c * kTile + (r ^ c)];
   }
 }
 
 // Raw fp64 partial tile (row-major 128x128) for a token piece of a leftover tile.
-__device__ __forceinline__ void tile_store_partial(const double (&master)[2][2][16], double* __restrict__ dst) {
+__device__ __forceinline__ void tile_store_partial(const double (&master)[2][16], double* __restrict__ dst) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int rw = (wave & 1) * 64, cw = (wave >> 1) * 32;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int col = wn * 64 + j * 32 + (lane & 31);
-        dst[row * kTile + col] = master[i][j][r];
-      }
+    for (int r = 0; r < 16; ++r) dst[(rw + acc_row(i, r, lane)) * kTile + cw + (lane & 31)] = master[i][r];
 }
 
 // Balanced launch over T = nt(nt+1)/2 tiles with P = min(T, #CUs): a first
@@ -319,11 +310,11 @@ struct HessSched {
 };
 
 template <int DT>
-__global__ void __launch_bounds__(256) syrk_mfma_kernel(const uint16_t* __restrict__ X, int64_t ldx, int n,
-                                                        int64_t tokens, HessSched sc, int pieces, int vec_ok,
-                                                        double alpha, double beta, double* __restrict__ H,
-                                                        double* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 2 * kTile * kKStep * 2];  // 64 KB
+__global__ void __launch_bounds__(kThreads) syrk_mfma_kernel(const uint16_t* __restrict__ X, int64_t ldx, int n,
+                                                             int64_t tokens, HessSched sc, int pieces, int vec_ok,
+                                                             double alpha, double beta, double* __restrict__ H,
+                                                             double* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 2 * kTile * kKStep * 2];  // 128 KB
   const TileCtx cx{X, ldx, n, vec_ok, lds};
   const int b = blockIdx.x;
   int idx;
@@ -342,13 +333,11 @@ __global__ void __launch_bounds__(256) syrk_mfma_kernel(const uint16_t* __restri
   }
   int ti, tj;
   sched_tile(idx, sc.nt, ti, tj);
-  double master[2][2][16];
+  double master[2][16];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) master[i][j][e] = 0.0;
+    for (int e = 0; e < 16; ++e) master[i][e] = 0.0;
   tile_accumulate<DT>(cx, ti, tj, p0, p1, master);
   if (partial_out) tile_store_partial(master, partial + static_cast<int64_t>(b) * kTile * kTile);
   else tile_epilogue(master, ti, tj, n, alpha, beta, H, lds);
@@ -487,11 +476,11 @@ hipError_t launch_hessian(double* H, int64_t n, const void* X, int dt, int64_t t
   double* partial = static_cast<double*>(ws);
   auto kern = (dt == DT_BF16) ? syrk_mfma_kernel<DT_BF16> : syrk_mfma_kernel<DT_FP16>;
   const uint16_t* Xp = static_cast<const uint16_t*>(X);
-  hipLaunchKernelGGL(kern, dim3(sc.R * sc.P), dim3(256), 0, s, Xp, ldx, static_cast<int>(n), tokens, sc, 0, vec_ok,
+  hipLaunchKernelGGL(kern, dim3(sc.R * sc.P), dim3(kThreads), 0, s, Xp, ldx, static_cast<int>(n), tokens, sc, 0, vec_ok,
                      alpha, beta, H, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sc.L == 0) return e;
-  hipLaunchKernelGGL(kern, dim3(sc.L * sc.S), dim3(256), 0, s, Xp, ldx, static_cast<int>(n), tokens, sc, 1, vec_ok,
+  hipLaunchKernelGGL(kern, dim3(sc.L * sc.S), dim3(kThreads), 0, s, Xp, ldx, static_cast<int>(n), tokens, sc, 1, vec_ok,
                      alpha, beta, H, partial);
   e = hipGetLastError();
   if (e != hipSuccess || sc.S <= 1) return e;
