@@ -32,6 +32,7 @@
 namespace gptq {
 
 constexpr int kBlk = 128;     // lazy-batch block = group size
+constexpr int kSuper = 512;   // columns per outer lazy batch (a multiple of kBlk)
 constexpr int kSub = 16;      // sub-block kept in registers inside the sweep
 constexpr int kRowsSweep = 64;
 
@@ -82,7 +83,7 @@ constexpr int kSubs = kBlk / kSub;  // 8
 template <int BITS, bool SYM>
 __global__ void __launch_bounds__(256) sweep_block_kernel(
     float* __restrict__ Wk, const float* __restrict__ U, int n, int rows, int i1,
-    uint8_t* __restrict__ codes, float* __restrict__ E, uint16_t* __restrict__ scales,
+    uint8_t* __restrict__ codes, float* __restrict__ E, int ldE, uint16_t* __restrict__ scales,
     uint16_t* __restrict__ zeros, double* __restrict__ rowloss) {
   __shared__ __attribute__((aligned(16))) float UT[kBlk][kBlk + 4];
   __shared__ float Ws[kBlk][kRowsSweep];
@@ -157,7 +158,7 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
     rs = 1.0f / sv;
   }
 
-  float* erow = E + static_cast<int64_t>(valid ? r : 0) * kBlk;
+  float* erow = E + static_cast<int64_t>(valid ? r : 0) * ldE;
   uint8_t* crow = codes + static_cast<int64_t>(valid ? r : 0) * n + i1;
   for (int sb = 0; sb < kSubs; ++sb) {
     const int j0 = sb * kSub;
@@ -293,17 +294,19 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
 }
 
 // ---------------------------------------------------------------- trailing update
-// Wk[r0:r0+128, c0:c0+128] -= E[r0:r0+128, 0:128] U[i1:i1+128, c0:c0+128],
-// c0 = i2 + 128*blockIdx.x, r0 = 128*blockIdx.y.
+// Wk[r0:r0+128, c0:c0+128] -= E[r0:r0+128, 0:K] U[i1:i1+K, c0:c0+128] for
+// columns c < ce, c0 = cb + 128*blockIdx.x, r0 = 128*blockIdx.y; E has row
+// stride ldE.
 // Split-bf16 product on the bf16 MFMA: each fp32 operand x = hi + lo with
 // hi = bf16(x), lo = bf16(x - hi) (round to nearest even), and
 //   E U ~ Ehi Uhi + Ehi Ulo + Elo Uhi   (fp32 accumulation),
 // which leaves a relative error near 2^-16 per product (the dropped Elo Ulo
 // term and the rounding of lo), against 2^-24 for an fp32 product.
-// K = 128 runs as two chunks of 64 staged in LDS as bf16 hi/lo planes: E as
-// [row][k], U transposed as [col][k], so each MFMA operand fragment (8
-// consecutive k) is one 16-byte read.  The 16-byte chunk c of a 128-byte row
-// r sits at slot c ^ (r & 7), which keeps the fragment reads conflict-free.
+// K runs in chunks of 64 staged in LDS as bf16 hi/lo planes: E as [row][k], U
+// transposed as [col][k], so each MFMA operand fragment (8 consecutive k) is
+// one 16-byte read; the next chunk's global loads are in flight during the
+// current chunk's MFMAs.  The 16-byte chunk c of a 128-byte row r sits at slot
+// c ^ (r & 7), which keeps the fragment reads conflict-free.
 // 256 threads; wave (wm, wn) owns a 64x64 quarter = 2x2 v_mfma_f32_32x32x16_bf16
 // tiles (accumulator q of lane l is row 8(q/4) + 4(l/32) + q%4, column l%32).
 constexpr int kTK = 64;
@@ -334,15 +337,15 @@ __device__ __forceinline__ f32x16 mfma_bf16(const u32x4& a, const u32x4& b, f32x
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
 }
 
-__global__ void __launch_bounds__(256) trailing_kernel(float* __restrict__ Wk, const float* __restrict__ E,
-                                                       const float* __restrict__ U, int n, int rows, int i1,
-                                                       int i2) {
+__global__ void __launch_bounds__(256, 2) trailing_kernel(float* __restrict__ Wk, const float* __restrict__ E,
+                                                       int ldE, const float* __restrict__ U, int n, int rows,
+                                                       int i1, int K, int cb, int ce) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[4][128 * kTK * 2];  // Ehi, Elo, Uhi, Ulo: 64 KB
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int r0 = blockIdx.y * 128;
-  const int c0 = i2 + blockIdx.x * 128;
+  const int c0 = cb + blockIdx.x * 128;
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -351,16 +354,15 @@ __global__ void __launch_bounds__(256) trailing_kernel(float* __restrict__ Wk, c
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  for (int kc = 0; kc < kBlk; kc += kTK) {
-    // Staging: all global loads of the chunk first, then split and store.
-    float ev[4][8], uv[4][8];
+  float ev[4][8], uv[4][8];
+  auto gload = [&](int kc) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       // E: unit -> (row, k-octet); 8 consecutive k of one row
       const int u = tid + 256 * q;
       const int row = u >> 3, ko = u & 7;
       if (r0 + row < rows) {
-        const float* src = E + static_cast<int64_t>(r0 + row) * kBlk + kc + 8 * ko;
+        const float* src = E + static_cast<int64_t>(r0 + row) * ldE + kc + 8 * ko;
         const f32x4 a = *reinterpret_cast<const f32x4*>(src);
         const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
         ev[q][0] = a[0]; ev[q][1] = a[1]; ev[q][2] = a[2]; ev[q][3] = a[3];
@@ -375,11 +377,14 @@ __global__ void __launch_bounds__(256) trailing_kernel(float* __restrict__ Wk, c
       // U: unit -> (col, k-octet); 8 rows of U at one column, transposed into LDS
       const int u = tid + 256 * q;
       const int col = u & 127, ko = u >> 7;
-      const bool ok = c0 + col < n;
+      const bool ok = c0 + col < ce;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         uv[q][e] = ok ? U[static_cast<int64_t>(i1 + kc + 8 * ko + e) * n + c0 + col] : 0.0f;
     }
+  };
+  gload(0);
+  for (int kc = 0; kc < K; kc += kTK) {
     if (kc) __syncthreads();  // the previous chunk's fragments have been read
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -400,6 +405,7 @@ __global__ void __launch_bounds__(256) trailing_kernel(float* __restrict__ Wk, c
       *reinterpret_cast<u32x4*>(lds[3] + tk_offset(col, ko)) = lo;
     }
     __syncthreads();
+    if (kc + kTK < K) gload(kc + kTK);
 #pragma unroll
     for (int kk = 0; kk < kTK / 16; ++kk) {
       const int c = kk * 2 + (lane >> 5);
@@ -437,7 +443,7 @@ __global__ void __launch_bounds__(256) trailing_kernel(float* __restrict__ Wk, c
       for (int q = 0; q < 16; ++q) {
         const int rr = r0 + wm * 64 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
         const int cc = c0 + wn * 64 + j * 32 + (lane & 31);
-        old[i][j][q] = (rr < rows && cc < n) ? Wk[static_cast<int64_t>(rr) * n + cc] : 0.0f;
+        old[i][j][q] = (rr < rows && cc < ce) ? Wk[static_cast<int64_t>(rr) * n + cc] : 0.0f;
       }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -447,7 +453,7 @@ __global__ void __launch_bounds__(256) trailing_kernel(float* __restrict__ Wk, c
       for (int q = 0; q < 16; ++q) {
         const int rr = r0 + wm * 64 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
         const int cc = c0 + wn * 64 + j * 32 + (lane & 31);
-        if (rr < rows && cc < n) Wk[static_cast<int64_t>(rr) * n + cc] = old[i][j][q] - acc[i][j][q];
+        if (rr < rows && cc < ce) Wk[static_cast<int64_t>(rr) * n + cc] = old[i][j][q] - acc[i][j][q];
       }
 }
 
@@ -496,7 +502,7 @@ static inline size_t al256(size_t b) { return (b + 255) & ~static_cast<size_t>(2
 
 size_t quantize_workspace(int64_t rows, int64_t n) {
   return al256(static_cast<size_t>(rows) * n * 4)      // Wk
-         + al256(static_cast<size_t>(rows) * kBlk * 4) // E block
+         + al256(static_cast<size_t>(rows) * kSuper * 4) // E of a super-block
          + al256(static_cast<size_t>(rows) * n)        // codes
          + al256(static_cast<size_t>(rows) * 8)        // rowloss
          + al256(static_cast<size_t>(n) * 4)           // invperm
@@ -505,8 +511,8 @@ size_t quantize_workspace(int64_t rows, int64_t n) {
 
 template <int BITS, bool SYM>
 static void launch_sweep(dim3 g, hipStream_t s, float* Wk, const float* U, int n, int rows, int i1, uint8_t* codes,
-                         float* E, uint16_t* scales, uint16_t* zeros, double* rowloss) {
-  hipLaunchKernelGGL((sweep_block_kernel<BITS, SYM>), g, dim3(256), 0, s, Wk, U, n, rows, i1, codes, E, scales,
+                         float* E, int ldE, uint16_t* scales, uint16_t* zeros, double* rowloss) {
+  hipLaunchKernelGGL((sweep_block_kernel<BITS, SYM>), g, dim3(256), 0, s, Wk, U, n, rows, i1, codes, E, ldE, scales,
                      zeros, rowloss);
 }
 
@@ -519,7 +525,7 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
   float* Wk = reinterpret_cast<float*>(p);
   p += al256(static_cast<size_t>(rows) * n * 4);
   float* E = reinterpret_cast<float*>(p);
-  p += al256(static_cast<size_t>(rows) * kBlk * 4);
+  p += al256(static_cast<size_t>(rows) * kSuper * 4);
   uint8_t* codes = p;
   p += al256(static_cast<size_t>(rows) * n);
   double* rowloss = reinterpret_cast<double*>(p);
@@ -544,17 +550,32 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
   hipLaunchKernelGGL(gidx_kernel, dim3((n + 255) / 256), dim3(256), 0, s, perm, n, kBlk, g_idx, invperm);
   GPTQ_CHECK_LAUNCH();
 
+  // Two-level lazy batching: inside a super-block of kSuper columns each
+  // 128-column block updates only the rest of its super-block; the columns
+  // beyond it receive the whole super-block's errors in one K = kSuper update,
+  // so the working weights are read and written once per super-block rather
+  // than once per block.  E holds the super-block's scaled errors [rows, kSuper].
   const dim3 gs((rows + kRowsSweep - 1) / kRowsSweep);
-  for (int i1 = 0; i1 < n; i1 += kBlk) {
-    const int i2 = i1 + kBlk;
-    if (bits == 4 && !sym) launch_sweep<4, false>(gs, s, Wk, U, n, rows, i1, codes, E, scales, zeros, rowloss);
-    else if (bits == 4 && sym) launch_sweep<4, true>(gs, s, Wk, U, n, rows, i1, codes, E, scales, zeros, rowloss);
-    else if (bits == 3 && !sym) launch_sweep<3, false>(gs, s, Wk, U, n, rows, i1, codes, E, scales, zeros, rowloss);
-    else launch_sweep<3, true>(gs, s, Wk, U, n, rows, i1, codes, E, scales, zeros, rowloss);
-    GPTQ_CHECK_LAUNCH();
-    if (i2 < n) {
-      dim3 gt((n - i2 + 127) / 128, (rows + 127) / 128);
-      hipLaunchKernelGGL(trailing_kernel, gt, dim3(256), 0, s, Wk, E, U, n, rows, i1, i2);
+  const int rt = (rows + 127) / 128;
+  for (int s1 = 0; s1 < n; s1 += kSuper) {
+    const int s2 = (s1 + kSuper < n) ? s1 + kSuper : n;
+    for (int i1 = s1; i1 < s2; i1 += kBlk) {
+      const int i2 = i1 + kBlk;
+      float* Eb = E + (i1 - s1);
+      if (bits == 4 && !sym) launch_sweep<4, false>(gs, s, Wk, U, n, rows, i1, codes, Eb, kSuper, scales, zeros, rowloss);
+      else if (bits == 4 && sym) launch_sweep<4, true>(gs, s, Wk, U, n, rows, i1, codes, Eb, kSuper, scales, zeros, rowloss);
+      else if (bits == 3 && !sym) launch_sweep<3, false>(gs, s, Wk, U, n, rows, i1, codes, Eb, kSuper, scales, zeros, rowloss);
+      else launch_sweep<3, true>(gs, s, Wk, U, n, rows, i1, codes, Eb, kSuper, scales, zeros, rowloss);
+      GPTQ_CHECK_LAUNCH();
+      if (i2 < s2) {
+        hipLaunchKernelGGL(trailing_kernel, dim3((s2 - i2 + 127) / 128, rt), dim3(256), 0, s, Wk, Eb, kSuper, U, n,
+                           rows, i1, kBlk, i2, s2);
+        GPTQ_CHECK_LAUNCH();
+      }
+    }
+    if (s2 < n) {
+      hipLaunchKernelGGL(trailing_kernel, dim3((n - s2 + 127) / 128, rt), dim3(256), 0, s, Wk, E, kSuper, U, n, rows,
+                         s1, s2 - s1, s2, n);
       GPTQ_CHECK_LAUNCH();
     }
   }
