@@ -23,6 +23,10 @@ FLAGS = [
     # hipcc -O3 forms packed fp32 instructions from scalar code on its own; they
     # are kept out of every kernel here.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Register-resident arrays (the 64-row factorization keeps a row per lane)
+    # need their loops fully unrolled; the default size limit on explicitly
+    # unrolled loops would leave some rolled and move the arrays to scratch.
+    "-mllvm", "-pragma-unroll-threshold=500000",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}",
 ]

@@ -13,11 +13,16 @@
 // an fp32 factorization of these Hessians (condition numbers ~1e5) changes
 // enough codes to matter; U is rounded to fp32 at the end.
 //
-// Blocked right-looking Cholesky with 64x64 blocks, per block column k:
-//   chol_diag  one wave factors A_kk (rows in registers),
-//   diag_inv   one wave inverts L_kk into the diagonal block of Linv,
-//   chol_trsm  L_ik = A_ik inv(L_kk)^T for every block row i > k  (fp64 MFMA),
-//   chol_syrk  A_ij -= L_ik L_jk^T for k < j <= i                   (fp64 MFMA).
+// Blocked Cholesky with 64x64 blocks, panels taken in groups of kGroup.
+// Inside a group (left-looking), per block column k:
+//   chol_update    column k receives the group's earlier panels,
+//                  A_ik -= sum_{k0 <= q < k} L_iq L_kq^T           (fp64 MFMA),
+//   chol_diag_inv  one wave factors A_kk (rows in registers) and writes
+//                  inv(L_kk) into the diagonal block of Linv,
+//   chol_trsm      L_ik = A_ik inv(L_kk)^T for every block row i > k (fp64 MFMA);
+// after the group (right-looking), one chol_update pass applies all of the
+// group's panels to the trailing matrix with K = 64 kGroup, so the trailing
+// matrix is read and written once per group instead of once per panel.
 // Triangular inverse by recursive doubling: with the diagonal blocks already
 // inverted, each level joins pairs of inverted blocks of size s,
 //   inv([L11 0; L21 L22]) = [X11 0; -X22 L21 X11  X22],
@@ -29,7 +34,8 @@
 
 namespace gptq {
 
-constexpr int kB = 64;  // block edge of the factorization
+constexpr int kB = 64;     // block edge of the factorization
+constexpr int kGroup = 4;  // panels whose trailing update is applied in one pass
 
 // ---------------------------------------------------------------- small kernels
 // dd[i] = H_ii, or 1 for a dead column (H_ii == 0); dead flag; a NaN/inf or
@@ -108,12 +114,14 @@ __global__ void prep_gather_kernel(const double* __restrict__ H, const int32_t* 
 }
 
 // ---------------------------------------------------------------- diagonal block
-// Factor the 64x64 diagonal block k (rows/cols beyond n are identity) and
-// write L_kk back to A; a second kernel writes inv(L_kk) to the diagonal block
-// of Linv.  One wave each.
-// Factorization, right-looking, lane i keeps row i in registers: for column j
-// the pivot comes from lane j (readlane), each lane scales its entry, the
-// column goes through LDS and every lane applies the rank-1 update to its row.
+// Factor the 64x64 diagonal block k in place (rows/cols beyond n are identity)
+// and write inv(L_kk) into the diagonal block of Linv.  One wave.
+// Factorization, right-looking, lane i keeps row i in registers.  Columns go
+// in panels of four: inside a panel the pivots and the panel's own updates
+// take the needed entries of the pivot rows by readlane; then the four
+// columns go through LDS once and every lane applies the rank-4 update to the
+// rest of its row.  1/sqrt(pivot) is the hardware estimate refined by two
+// Newton steps.
 // Inverse, lane c keeps column c of inv(L) in registers:
 //   x_r = (delta_rc - sum_{q<r} l_rq x_q) / l_rr, rows of L read as LDS broadcasts.
 __device__ __forceinline__ double readlane_f64(double v, int lane) {
@@ -123,77 +131,178 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
   return __longlong_as_double((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-__global__ void __launch_bounds__(64) chol_diag_kernel(double* __restrict__ A, int n, int k,
-                                                       int* __restrict__ info) {
-  __shared__ __attribute__((aligned(16))) double col[2][kB];
+// A zero the compiler cannot see through: LDS addresses formed as
+// base + opaque_zero() + constant compile to one base register plus immediate
+// offsets instead of one register per address.
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
+__device__ __forceinline__ double rsqrt_refined(double x) {
+  double r = __builtin_amdgcn_rsq(x);
+  const double h = 0.5 * x;
+  r = r * fma(-(h * r), r, 1.5);
+  r = r * fma(-(h * r), r, 1.5);
+  return r;
+}
+
+__global__ void __launch_bounds__(64) chol_diag_inv_kernel(double* __restrict__ A, double* __restrict__ Linv,
+                                                           int n, int k, int* __restrict__ info) {
+  __shared__ double Ls[kB][kB + 1];                             // the block, row-major, padded
+  __shared__ __attribute__((aligned(16))) double pan[2][kB][4];  // panel columns, [row][column]
+  __shared__ double rinv[kB];
+  __shared__ double Xs[kB][kB + 1];                             // inv(L), lower blocks
   const int i = threadIdx.x;
   const int r0 = k * kB;
   const int m = (n - r0 < kB) ? n - r0 : kB;
-  const double* arow = A + static_cast<int64_t>(r0 + i) * n + r0;
+  // coalesced load of the lower block (all 64 loads of a lane in flight at
+  // once), identity padding beyond n
+  {
+    double v[kB];
+#pragma unroll
+    for (int r = 0; r < kB; ++r) v[r] = (r < m && i < m) ? A[static_cast<int64_t>(r0 + r) * n + r0 + i] : 0.0;
+#pragma unroll
+    for (int r = 0; r < kB; ++r) Ls[r][i] = (r >= m || i >= m) ? ((r == i) ? 1.0 : 0.0) : ((i <= r) ? v[r] : 0.0);
+  }
+  __syncthreads();
   double a[kB];
 #pragma unroll
-  for (int c = 0; c < kB; ++c) {
-    double v = (i == c) ? 1.0 : 0.0;
-    if (i < m && c < m && c <= i) v = arow[c];
-    a[c] = v;
-  }
+  for (int c = 0; c < kB; ++c) a[c] = Ls[i][c];
   int bad = 0;
+  const int z0 = opaque_zero();
+  // Column j = jpn + q of panel jpn: the panel's earlier columns by readlane,
+  // then the pivot.
+  auto pivot_step = [&](int jpn, int q) {
+    const int j = jpn + q;
 #pragma unroll
-  for (int j = 0; j < kB; ++j) {
+    for (int p = 0; p < q; ++p) a[j] = fma(-a[jpn + p], readlane_f64(a[jpn + p], j), a[j]);
     double piv = readlane_f64(a[j], j);
     if (!(piv > 0.0) || !(piv < INFINITY)) {  // uniform across the wave
       bad = 1;
       piv = 1.0;
     }
-    const double rs = 1.0 / sqrt(piv);
-    const double l = a[j] * rs;
-    a[j] = l;
-    col[j & 1][i] = l;
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the column is in LDS
-    __builtin_amdgcn_wave_barrier();
+    const double rs = rsqrt_refined(piv);
+    a[j] = (i >= j) ? a[j] * rs : 0.0;
+  };
 #pragma unroll
-    for (int c = j + 1; c < kB; ++c) a[c] = fma(-l, col[j & 1][c], a[c]);
+  for (int q = 0; q < 4; ++q) pivot_step(0, q);
+#pragma unroll
+  for (int jp = 0; jp + 4 < kB; jp += 4) {
+    double(*pp)[4] = reinterpret_cast<double(*)[4]>(&pan[(jp >> 2) & 1][0][0] + z0);
+    *reinterpret_cast<double2*>(&pp[i][0]) = double2{a[jp], a[jp + 1]};
+    *reinterpret_cast<double2*>(&pp[i][2]) = double2{a[jp + 2], a[jp + 3]};
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the panel is in LDS
+    __builtin_amdgcn_wave_barrier();
+    // Rank-4 update in batches of 4 rows of the panel, double buffered: the
+    // next batch's 8 LDS reads are issued before the current batch's FMAs.
+    // Batch 0 covers the next panel's columns; the next panel's four pivot
+    // steps then run between the later batches, whose FMAs fill the pivot
+    // chain's latency.
+    double2 bu[2][4], bv[2][4];
+    auto load_batch = [&](int c0, int slot) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bu[slot][t] = *reinterpret_cast<const double2*>(&pp[c0 + t][0]);
+        bv[slot][t] = *reinterpret_cast<const double2*>(&pp[c0 + t][2]);
+      }
+    };
+    const int nb = (kB - jp - 4) / 4;
+    load_batch(jp + 4, 0);
+#pragma unroll
+    for (int bt = 0; bt < nb; ++bt) {
+      const int c0 = jp + 4 + 4 * bt;
+      const int cur = bt & 1;
+      if (bt + 1 < nb) load_batch(c0 + 4, cur ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = c0 + t;
+        double x0 = fma(-a[jp], bu[cur][t].x, a[c]);
+        x0 = fma(-a[jp + 1], bu[cur][t].y, x0);
+        x0 = fma(-a[jp + 2], bv[cur][t].x, x0);
+        a[c] = fma(-a[jp + 3], bv[cur][t].y, x0);
+      }
+      if (bt >= 1 && bt <= 4) pivot_step(jp + 4, bt - 1);
+    }
+    const int done = (nb - 1 < 4) ? nb - 1 : 4;
+#pragma unroll
+    for (int q = done; q < 4; ++q) pivot_step(jp + 4, q);
   }
   if (bad && i == 0) atomicOr(info, 1);
-  double* wrow = A + static_cast<int64_t>(r0 + i) * n + r0;
+  // L back to LDS (row i, zeros above the diagonal), 1/l_ii
 #pragma unroll
-  for (int c = 0; c < kB; ++c)
-    if (i < m && c < m && c <= i) wrow[c] = a[c];
-}
-
-// inv(L_kk) into the diagonal block of Linv; lane c keeps column c in registers.
-__global__ void __launch_bounds__(64) diag_inv_kernel(const double* __restrict__ A, double* __restrict__ Linv,
-                                                      int n, int k) {
-  __shared__ __attribute__((aligned(16))) double Ls[kB][kB];
-  __shared__ double rinv[kB];
-  const int i = threadIdx.x;
-  const int r0 = k * kB;
-  const int m = (n - r0 < kB) ? n - r0 : kB;
-  for (int c = 0; c < kB; ++c) {
-    double v = (i == c) ? 1.0 : 0.0;
-    if (i < m && c < m && c <= i) v = A[static_cast<int64_t>(r0 + i) * n + r0 + c];
-    Ls[i][c] = v;
-  }
+  for (int c = 0; c < kB; ++c) Ls[i][c] = (c <= i) ? a[c] : 0.0;
   rinv[i] = 1.0 / Ls[i][i];
   __syncthreads();
-  const int cc = i;
-  double x[kB];
+  {
+    double v[kB];  // all LDS reads first, then the guarded stores
 #pragma unroll
-  for (int r = 0; r < kB; ++r) {
-    double acc0 = (r == cc) ? 1.0 : 0.0, acc1 = 0.0;
+    for (int r = 0; r < kB; ++r) v[r] = Ls[r][i];
 #pragma unroll
-    for (int q = 0; q < r; q += 2) {
-      acc0 = fma(-Ls[r][q], x[q], acc0);
-      if (q + 1 < r) acc1 = fma(-Ls[r][q + 1], x[q + 1], acc1);
-    }
-    x[r] = (r >= cc) ? (acc0 + acc1) * rinv[r] : 0.0;
+    for (int r = 0; r < kB; ++r)
+      if (r < m && i <= r) A[static_cast<int64_t>(r0 + r) * n + r0 + i] = v[r];
   }
-  __syncthreads();  // L no longer needed: the block goes out through LDS
+  // Inverse by 16x16 blocks, X = inv(L):
+  //   X_bb = inv(L_bb)          forward substitution, lane = (b, column),
+  //   X_ij = -X_ii sum_{k=j}^{i-1} L_ik X_kj   for i > j, by block distance,
+  // the products on v_mfma_f64_16x16x4 (lane l supplies A[l%16][l/16] and
+  // B[l/16][l%16]; accumulator r of lane l is D[l/16 + 4r][l%16], which is
+  // also the B-operand layout, so L_ik X_kj feeds the product with X_ii
+  // straight from the accumulators).
+  {
+    const int b = i >> 4, c = i & 15, o = 16 * b;
+    double x[16];
 #pragma unroll
-  for (int r = 0; r < kB; ++r) Ls[r][cc] = x[r];
-  __syncthreads();
-  for (int r = 0; r < m; ++r)
-    if (cc < m) Linv[static_cast<int64_t>(r0 + r) * n + r0 + cc] = Ls[r][cc];
+    for (int r = 0; r < 16; ++r) {
+      double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+      for (int q = 0; q < r; q += 2) {
+        s0 = fma(Ls[o + r][o + q], x[q], s0);
+        if (q + 1 < r) s1 = fma(Ls[o + r][o + q + 1], x[q + 1], s1);
+      }
+      const double t = ((r == c) ? 1.0 : 0.0) - (s0 + s1);
+      x[r] = (r >= c) ? t * rinv[o + r] : 0.0;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Xs[o + r][o + c] = x[r];
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  {
+    const int lr = i & 15, lk = i >> 4;
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+#pragma unroll
+      for (int bi = d; bi < 4; ++bi) {
+        const int bj = bi - d;
+        f64x4 t = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int bk = bj; bk < bi; ++bk)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            t = __builtin_amdgcn_mfma_f64_16x16x4f64(Ls[16 * bi + lr][16 * bk + 4 * ks + lk],
+                                                     Xs[16 * bk + 4 * ks + lk][16 * bj + lr], t, 0, 0, 0);
+        f64x4 u = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          u = __builtin_amdgcn_mfma_f64_16x16x4f64(Xs[16 * bi + lr][16 * bi + 4 * ks + lk], t[ks], u, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Xs[16 * bi + lk + 4 * r][16 * bj + lr] = -u[r];
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  {
+    double v[kB];  // all LDS reads first, then the guarded stores
+#pragma unroll
+    for (int r = 0; r < kB; ++r) v[r] = ((r >> 4) >= (i >> 4)) ? Xs[r][i] : 0.0;
+#pragma unroll
+    for (int r = 0; r < kB; ++r)
+      if (r < m && i < m) Linv[static_cast<int64_t>(r0 + r) * n + r0 + i] = v[r];
+  }
 }
 
 // ---------------------------------------------------------------- fp64 MFMA tile
@@ -204,9 +313,14 @@ __global__ void __launch_bounds__(64) diag_inv_kernel(const double* __restrict__
 // accumulator r of lane l is D[l/16 + 4*r][l%16] (rows interleaved across the
 // four accumulators; measured on gfx950).  Wave (wm, wn) owns the
 // 32x32 quarter (wm*32.., wn*32..): 2x2 MFMA tiles.
+// K runs in chunks of 64: each chunk is loaded into registers (coalesced rows
+// of 64 consecutive k), stored to LDS, and the next chunk's loads are issued
+// before the current chunk's 64 MFMAs per wave.  LDS rows are padded to 65
+// doubles.
+constexpr int kKC = 64;
 struct TileSmem {
-  double a[kB][17];
-  double b[16][kB + 1];
+  double a[kB][kKC + 1];  // a[m][k]
+  double b[kKC][kB + 1];  // b[k][n]
 };
 
 template <bool BT>
@@ -216,31 +330,44 @@ __device__ __forceinline__ void tile_gemm_f64(const double* __restrict__ A, int6
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  for (int kc = k0; kc < k1; kc += 16) {
-    __syncthreads();
+  double ra[16], rb[16];
+  auto gload = [&](int kc) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 16; ++q) {
       const int e = tid + 256 * q;
-      const int r = e >> 4, kk = e & 15;
+      const int r = e >> 6, kk = e & 63;  // A: row r, k = kc + kk
       const int kg = kc + kk;
-      sm.a[r][kk] = (r < mv && kg < k1) ? A[static_cast<int64_t>(r) * lda + kg] : 0.0;
+      ra[q] = (r < mv && kg < k1) ? A[static_cast<int64_t>(r) * lda + kg] : 0.0;
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 16; ++q) {
       const int e = tid + 256 * q;
       if (!BT) {
-        const int kk = e >> 6, c = e & 63;
+        const int kk = e >> 6, c = e & 63;  // B[k][c]
         const int kg = kc + kk;
-        sm.b[kk][c] = (c < nv && kg < k1) ? B[static_cast<int64_t>(kg) * ldb + c] : 0.0;
+        rb[q] = (c < nv && kg < k1) ? B[static_cast<int64_t>(kg) * ldb + c] : 0.0;
       } else {
-        const int c = e >> 4, kk = e & 15;
+        const int c = e >> 6, kk = e & 63;  // B[c][k]
         const int kg = kc + kk;
-        sm.b[kk][c] = (c < nv && kg < k1) ? B[static_cast<int64_t>(c) * ldb + kg] : 0.0;
+        rb[q] = (c < nv && kg < k1) ? B[static_cast<int64_t>(c) * ldb + kg] : 0.0;
       }
     }
-    __syncthreads();
+  };
+  if (k0 >= k1) return;
+  gload(k0);
+  for (int kc = k0; kc < k1; kc += kKC) {
+    __syncthreads();  // the previous chunk's operands have been read
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * q;
+      sm.a[e >> 6][e & 63] = ra[q];
+      if (!BT) sm.b[e >> 6][e & 63] = rb[q];
+      else sm.b[e & 63][e >> 6] = rb[q];
+    }
+    __syncthreads();
+    if (kc + kKC < k1) gload(kc + kKC);
+#pragma unroll
+    for (int ks = 0; ks < kKC / 4; ++ks) {
       const int kk = ks * 4 + (lane >> 4);
       double fa[2], fb[2];
 #pragma unroll
@@ -329,32 +456,238 @@ __global__ void __launch_bounds__(256) chol_trsm_kernel(double* __restrict__ A, 
   });
 }
 
-// A_ij -= L_ik L_jk^T for all lower tiles k < j <= i; blockIdx.x enumerates them.
-__global__ void __launch_bounds__(256) chol_syrk_kernel(double* __restrict__ A, int n, int k, int nblk) {
+// A_ij -= sum_{q0 <= q < q1} L_iq L_jq^T (K = 64 (q1 - q0)) over the tiles
+// of one launch: mode 0, the lower triangle j0 <= j <= i < nblk, row by row;
+// mode 1, the block column j = j0, rows i = j0 + blockIdx.x.
+__global__ void __launch_bounds__(256) chol_update_kernel(double* __restrict__ A, int n, int q0, int q1, int j0,
+                                                          int mode) {
   __shared__ TileSmem sm;
-  // lower tiles of the trailing (nblk-k-1)^2 block, row by row
-  int t = blockIdx.x;
-  int ii = 0;
-  while (t > ii) {
-    t -= ii + 1;
-    ++ii;
+  int i, j;
+  if (mode == 0) {
+    int t = blockIdx.x;
+    int ii = 0;
+    while (t > ii) {
+      t -= ii + 1;
+      ++ii;
+    }
+    i = j0 + ii;
+    j = j0 + t;
+  } else {
+    i = j0 + blockIdx.x;
+    j = j0;
   }
-  const int i = k + 1 + ii, j = k + 1 + t;
-  const int r0 = i * kB, cc0 = j * kB, k0 = k * kB;
+  const int r0 = i * kB, cc0 = j * kB, k0 = q0 * kB;
   const int mv = (n - r0 < kB) ? n - r0 : kB;
   const int nv = (n - cc0 < kB) ? n - cc0 : kB;
-  const int kv = (n - k0 < kB) ? n - k0 : kB;
+  const int kv = (q1 - q0) * kB;
+  // the tile's previous values are loaded first, in flight during the GEMM
+  f64x4 old[2][2];
+  tile_load(old, A + static_cast<int64_t>(r0) * n + cc0, n, mv, nv);
   f64x4 acc[2][2];
   zero_acc(acc);
   tile_gemm_f64<true>(A + static_cast<int64_t>(r0) * n + k0, n, A + static_cast<int64_t>(cc0) * n + k0, n,
                       mv, nv, 0, kv, acc, sm);
-  __syncthreads();
-  // all loads of the tile issued before any store (see tile_load)
-  f64x4 old[2][2];
-  tile_load(old, A + static_cast<int64_t>(r0) * n + cc0, n, mv, nv);
   tile_foreach2(acc, old, [&](int r, int c, double v, double o) {
     if (r < mv && c < nv && (i != j || c <= r)) A[static_cast<int64_t>(r0 + r) * n + cc0 + c] = o - v;
   });
+}
+
+// ---------------------------------------------------------------- fp64 MFMA, 128x128 tiles
+// acc += A[0:128, k0:k1] * B[k0:k1, 0:128], 256 threads, wave (wm, wn) owns
+// the 64x64 quarter (wm*64.., wn*64..) as 4x4 v_mfma_f64_16x16x4 tiles.
+// A is addressed A[m*lda + k]; B as B[k*ldb + n] (BT = false) or B[n*ldb + k]
+// (BT = true).  Rows >= mv, columns >= nv and k >= k1 read as 0.  K runs in
+// chunks of 16 staged as [row][k] planes (odd row stride, 17 doubles: the
+// fragment reads and the stores are free of LDS bank conflicts), LDS double buffered, the next chunk's global loads
+// in flight in registers during the current chunk's 64 MFMAs per wave.
+constexpr int kT2 = 128;
+constexpr int kKC2 = 16;
+constexpr int kS2 = 17;
+// 128x128 tiles pay off only with enough of them to keep every compute unit
+// busy with two; below that the 64x64 kernels run more tiles in parallel.
+constexpr int kBigTiles = 512;
+struct BigSmem {
+  double a[2][kT2][kS2];
+  double b[2][kT2][kS2];
+};
+
+template <bool BT>
+__device__ __forceinline__ void gemm128(const double* __restrict__ A, int64_t lda, const double* __restrict__ B,
+                                        int64_t ldb, int mv, int nv, int k0, int k1, f64x4 (&acc)[4][4],
+                                        BigSmem& sm) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  double ra[8], rb[8];
+  // A (and B^T): thread -> row tid/2, k = 8*(tid%2) .. +7 (64 contiguous bytes)
+  // B: thread -> column tid%128, k = 8*(tid/128) .. +7 (rows of B, coalesced)
+  auto gload = [&](int kc) {
+    const int m = tid >> 1, kb = kc + 8 * (tid & 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int kg = kb + e;
+      ra[e] = (m < mv && kg < k1) ? A[static_cast<int64_t>(m) * lda + kg] : 0.0;
+    }
+    if (BT) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kg = kb + e;
+        rb[e] = (m < nv && kg < k1) ? B[static_cast<int64_t>(m) * ldb + kg] : 0.0;
+      }
+    } else {
+      const int c = tid & 127, kb2 = kc + 8 * (tid >> 7);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kg = kb2 + e;
+        rb[e] = (c < nv && kg < k1) ? B[static_cast<int64_t>(kg) * ldb + c] : 0.0;
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    const int m = tid >> 1, kh = 8 * (tid & 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm.a[buf][m][kh + e] = ra[e];
+    if (BT) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm.b[buf][m][kh + e] = rb[e];
+    } else {
+      const int c = tid & 127, kh2 = 8 * (tid >> 7);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm.b[buf][c][kh2 + e] = rb[e];
+    }
+  };
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < kKC2 / 4; ++ks) {
+      const int kk = ks * 4 + (lane >> 4);
+      double fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = sm.a[buf][wm * 64 + i * 16 + (lane & 15)][kk];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = sm.b[buf][wn * 64 + j * 16 + (lane & 15)][kk];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  if (k0 >= k1) return;
+  const int nch = (k1 - k0 + kKC2 - 1) / kKC2;
+  gload(k0);
+  lstore(0);
+  if (nch > 1) gload(k0 + kKC2);
+  __syncthreads();
+  int buf = 0;
+  for (int c = 0; c < nch; ++c) {
+    compute(buf);
+    if (c + 1 >= nch) break;
+    lstore(buf ^ 1);
+    if (c + 2 < nch) gload(k0 + (c + 2) * kKC2);
+    __syncthreads();
+    buf ^= 1;
+  }
+  __syncthreads();  // LDS free for the caller
+}
+
+__device__ __forceinline__ void zero_acc4(f64x4 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+}
+
+// Visit this thread's elements of the 128x128 tile: f(i, j, r, row, col).
+template <typename F>
+__device__ __forceinline__ void big_foreach(F f) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) f(i, j, r, wm * 64 + i * 16 + (lane >> 4) + 4 * r, wn * 64 + j * 16 + (lane & 15));
+}
+
+// Trailing pass on 128x128 tiles: A_IJ -= sum_{q0 <= q < q1} L_Iq L_Jq^T over
+// the lower triangle of tiles of the square [s0, n) x [s0, n).
+__global__ void __launch_bounds__(256, 2) chol_trail_kernel(double* __restrict__ A, int n, int q0, int q1, int s0) {
+  __shared__ BigSmem sm;
+  int t = blockIdx.x;
+  int I = 0;
+  while (t > I) {
+    t -= I + 1;
+    ++I;
+  }
+  const int J = t;
+  const int r0 = s0 + I * kT2, c0 = s0 + J * kT2, k0 = q0 * kB;
+  const int mv = (n - r0 < kT2) ? n - r0 : kT2;
+  const int nv = (n - c0 < kT2) ? n - c0 : kT2;
+  f64x4 acc[4][4];
+  zero_acc4(acc);
+  gemm128<true>(A + static_cast<int64_t>(r0) * n + k0, n, A + static_cast<int64_t>(c0) * n + k0, n, mv, nv, 0,
+                (q1 - q0) * kB, acc, sm);
+  // read-modify-write one 16x16 column strip at a time: its 16 loads first
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    double old[4][4];
+    big_foreach([&](int ii, int j, int r, int row, int col) {
+      if (ii == i) old[j][r] = (row < mv && col < nv) ? A[static_cast<int64_t>(r0 + row) * n + c0 + col] : 0.0;
+    });
+    big_foreach([&](int ii, int j, int r, int row, int col) {
+      if (ii == i && row < mv && col < nv && (I != J || col <= row))
+        A[static_cast<int64_t>(r0 + row) * n + c0 + col] = old[j][r] - acc[ii][j][r];
+    });
+  }
+}
+
+// One recursive-doubling level (see trtri_level_kernel) on 128x128 tiles, s >= 128.
+__global__ void __launch_bounds__(256, 2) trtri_big_kernel(double* __restrict__ L, double* __restrict__ Linv, int n,
+                                                        int s, int phase) {
+  __shared__ BigSmem sm;
+  const int b1 = blockIdx.x * 2 * s;
+  const int b2 = b1 + s;
+  if (b2 >= n) return;
+  const int s2 = (n - b2 < s) ? n - b2 : s;
+  // longest K first (see trtri_level_kernel)
+  const int tcols = s / kT2;
+  const int yq = blockIdx.y / tcols, yr = blockIdx.y % tcols;
+  const int tr = (phase == 0) ? yr : tcols - 1 - yq;
+  const int tc = (phase == 0) ? yq : yr;
+  const int rows0 = tr * kT2, cols0 = tc * kT2;
+  if (rows0 >= s2) return;
+  const int mv = (s2 - rows0 < kT2) ? s2 - rows0 : kT2;
+  f64x4 acc[4][4];
+  zero_acc4(acc);
+  if (phase == 0) {
+    // T = L21 X11 over q >= cols0, written transposed (T^T) into the strict
+    // upper triangle of A through LDS, 64 columns at a time, so rows coalesce.
+    gemm128<false>(L + static_cast<int64_t>(b2 + rows0) * n + b1, n, Linv + static_cast<int64_t>(b1) * n + b1 + cols0,
+                   n, mv, kT2, cols0, s, acc, sm);
+    double* st = &sm.a[0][0][0];  // [64 columns][128 rows + 1]
+    constexpr int kSt = kT2 + 1;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      big_foreach([&](int i, int j, int r, int row, int col) {
+        if ((col >> 6) == half) st[(col & 63) * kSt + row] = acc[i][j][r];
+      });
+      __syncthreads();
+      for (int e = threadIdx.x; e < 64 * kT2; e += 256) {
+        const int c = e >> 7, r = e & 127;
+        if (r < mv) L[static_cast<int64_t>(b1 + cols0 + 64 * half + c) * n + b2 + rows0 + r] = st[c * kSt + r];
+      }
+      __syncthreads();
+    }
+  } else {
+    // X21 = -X22 T over q < rows0 + 128, T read back from its transposed copy.
+    const int kend = (rows0 + kT2 < s2) ? rows0 + kT2 : s2;
+    gemm128<true>(Linv + static_cast<int64_t>(b2 + rows0) * n + b2, n, L + static_cast<int64_t>(b1 + cols0) * n + b2,
+                  n, mv, kT2, 0, kend, acc, sm);
+    big_foreach([&](int i, int j, int r, int row, int col) {
+      if (row < mv) Linv[static_cast<int64_t>(b2 + rows0 + row) * n + b1 + cols0 + col] = -acc[i][j][r];
+    });
+  }
 }
 
 // One level of the recursive-doubling inverse.  Pair p joins blocks
@@ -368,8 +701,13 @@ __global__ void __launch_bounds__(256) trtri_level_kernel(double* __restrict__ L
   const int b2 = b1 + s;
   if (b2 >= n) return;
   const int s2 = (n - b2 < s) ? n - b2 : s;
+  // Tiles are dispatched longest K first: phase 0 sums over q >= cols0
+  // (longest for the first tile column), phase 1 over q < rows0 + 64 (longest
+  // for the last tile row).
   const int tcols = s / kB;
-  const int tr = blockIdx.y / tcols, tc = blockIdx.y % tcols;
+  const int yq = blockIdx.y / tcols, yr = blockIdx.y % tcols;
+  const int tr = (phase == 0) ? yr : tcols - 1 - yq;
+  const int tc = (phase == 0) ? yq : yr;
   const int rows0 = tr * kB, cols0 = tc * kB;  // within the s2 x s output
   if (rows0 >= s2) return;
   const int mv = (s2 - rows0 < kB) ? s2 - rows0 : kB;
@@ -453,26 +791,46 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
   GPTQ_CHECK_LAUNCH();
 
   const int nblk = (n + kB - 1) / kB;
-  for (int k = 0; k < nblk; ++k) {
-    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(64), 0, s, A, n, k, info);
-    GPTQ_CHECK_LAUNCH();
-    hipLaunchKernelGGL(diag_inv_kernel, dim3(1), dim3(64), 0, s, A, Linv, n, k);
-    GPTQ_CHECK_LAUNCH();
-    const int rest = nblk - k - 1;
-    if (rest > 0) {
-      hipLaunchKernelGGL(chol_trsm_kernel, dim3(rest), dim3(256), 0, s, A, Linv, n, k);
+  for (int k0 = 0; k0 < nblk; k0 += kGroup) {
+    const int ke = (k0 + kGroup < nblk) ? k0 + kGroup : nblk;
+    for (int k = k0; k < ke; ++k) {
+      if (k > k0) {  // block column k receives the group's earlier panels
+        hipLaunchKernelGGL(chol_update_kernel, dim3(nblk - k), dim3(256), 0, s, A, n, k0, k, k, 1);
+        GPTQ_CHECK_LAUNCH();
+      }
+      hipLaunchKernelGGL(chol_diag_inv_kernel, dim3(1), dim3(64), 0, s, A, Linv, n, k, info);
       GPTQ_CHECK_LAUNCH();
-      hipLaunchKernelGGL(chol_syrk_kernel, dim3(rest * (rest + 1) / 2), dim3(256), 0, s, A, n, k, nblk);
+      if (k + 1 < nblk) {
+        hipLaunchKernelGGL(chol_trsm_kernel, dim3(nblk - k - 1), dim3(256), 0, s, A, Linv, n, k);
+        GPTQ_CHECK_LAUNCH();
+      }
+    }
+    if (ke < nblk) {  // everything right of the group, K = 64 * group width
+      const int nt = (n - ke * kB + kT2 - 1) / kT2;
+      if (nt * (nt + 1) / 2 >= kBigTiles) {
+        hipLaunchKernelGGL(chol_trail_kernel, dim3(nt * (nt + 1) / 2), dim3(256), 0, s, A, n, k0, ke, ke * kB);
+      } else {
+        const int rest = nblk - ke;
+        hipLaunchKernelGGL(chol_update_kernel, dim3(rest * (rest + 1) / 2), dim3(256), 0, s, A, n, k0, ke, ke, 0);
+      }
       GPTQ_CHECK_LAUNCH();
     }
   }
   for (int sz = kB; sz < n; sz *= 2) {
     const int pairs = (n + 2 * sz - 1) / (2 * sz);
-    const int tiles = (sz / kB) * (sz / kB);
-    hipLaunchKernelGGL(trtri_level_kernel, dim3(pairs, tiles), dim3(256), 0, s, A, Linv, n, sz, 0);
-    GPTQ_CHECK_LAUNCH();
-    hipLaunchKernelGGL(trtri_level_kernel, dim3(pairs, tiles), dim3(256), 0, s, A, Linv, n, sz, 1);
-    GPTQ_CHECK_LAUNCH();
+    if (sz < kT2 || pairs * (sz / kT2) * (sz / kT2) < kBigTiles) {
+      const int tiles = (sz / kB) * (sz / kB);
+      hipLaunchKernelGGL(trtri_level_kernel, dim3(pairs, tiles), dim3(256), 0, s, A, Linv, n, sz, 0);
+      GPTQ_CHECK_LAUNCH();
+      hipLaunchKernelGGL(trtri_level_kernel, dim3(pairs, tiles), dim3(256), 0, s, A, Linv, n, sz, 1);
+      GPTQ_CHECK_LAUNCH();
+    } else {
+      const int tiles = (sz / kT2) * (sz / kT2);
+      hipLaunchKernelGGL(trtri_big_kernel, dim3(pairs, tiles), dim3(256), 0, s, A, Linv, n, sz, 0);
+      GPTQ_CHECK_LAUNCH();
+      hipLaunchKernelGGL(trtri_big_kernel, dim3(pairs, tiles), dim3(256), 0, s, A, Linv, n, sz, 1);
+      GPTQ_CHECK_LAUNCH();
+    }
   }
   hipLaunchKernelGGL(write_u_kernel, dim3((n + 255) / 256, gy), dim3(256), 0, s, Linv, n, U);
   GPTQ_CHECK_LAUNCH();
