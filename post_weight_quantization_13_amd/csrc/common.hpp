@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace gptq {
 
 // ---------------------------------------------------------------- vector types
@@ -48,5 +50,58 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float x) {
 }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Zero `words` 8-byte words at p.  A kernel rather than hipMemsetAsync, so the
+// clearing also replays correctly when a caller captures the stream in a graph.
+static __global__ void zero_words_kernel(uint64_t* __restrict__ p, size_t words) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < words;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = 0;
+}
+
+static inline hipError_t zero_words(void* p, size_t words, hipStream_t s) {
+  if (words == 0) return hipSuccess;
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<uint64_t*>(p), words);
+  return hipGetLastError();
+}
+
+// One extra stream per device for work that overlaps the caller's stream,
+// created on first use and kept until the process ends.  Calls may share it;
+// each call orders its own work with its own events.
+static inline hipError_t side_stream(hipStream_t* out) {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[dev]) {
+    e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      streams[dev] = nullptr;
+      return e;
+    }
+  }
+  *out = streams[dev];
+  return hipSuccess;
+}
+
+// A pair of timing-free events, destroyed with the object.
+struct EventPair {
+  hipEvent_t fork = nullptr, join = nullptr;
+  hipError_t create() {
+    hipError_t e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&join, hipEventDisableTiming);
+    return e;
+  }
+  ~EventPair() {
+    if (fork) (void)hipEventDestroy(fork);
+    if (join) (void)hipEventDestroy(join);
+  }
+};
 
 }  // namespace gptq

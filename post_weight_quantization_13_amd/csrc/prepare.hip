@@ -115,7 +115,8 @@ __global__ void prep_gather_kernel(const double* __restrict__ H, const int32_t* 
 
 // ---------------------------------------------------------------- diagonal block
 // Factor the 64x64 diagonal block k in place (rows/cols beyond n are identity)
-// and write inv(L_kk) into the diagonal block of Linv.  One wave.
+// and write inv(L_kk) into the diagonal block of Linv.  Wave 0 computes; all
+// four waves load and store the block.
 // Factorization, right-looking, lane i keeps row i in registers.  Columns go
 // in panels of four: inside a panel the pivots and the panel's own updates
 // take the needed entries of the pivot rows by readlane; then the four
@@ -148,25 +149,34 @@ __device__ __forceinline__ double rsqrt_refined(double x) {
   return r;
 }
 
-__global__ void __launch_bounds__(64) chol_diag_inv_kernel(double* __restrict__ A, double* __restrict__ Linv,
-                                                           int n, int k, int* __restrict__ info) {
+__global__ void __launch_bounds__(256) chol_diag_inv_kernel(double* __restrict__ A, double* __restrict__ Linv,
+                                                            int n, int k, int* __restrict__ info) {
   __shared__ double Ls[kB][kB + 1];                             // the block, row-major, padded
   __shared__ __attribute__((aligned(16))) double pan[2][kB][4];  // panel columns, [row][column]
   __shared__ double rinv[kB];
   __shared__ double Xs[kB][kB + 1];                             // inv(L), lower blocks
-  const int i = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int i = tid & 63;
   const int r0 = k * kB;
   const int m = (n - r0 < kB) ? n - r0 : kB;
-  // coalesced load of the lower block (all 64 loads of a lane in flight at
-  // once), identity padding beyond n
+  // All four waves move the block in and out (16 coalesced rows each, loads
+  // in flight together); wave 0 factors and inverts.  Identity padding beyond n.
   {
-    double v[kB];
+    double v[16];
 #pragma unroll
-    for (int r = 0; r < kB; ++r) v[r] = (r < m && i < m) ? A[static_cast<int64_t>(r0 + r) * n + r0 + i] : 0.0;
+    for (int q = 0; q < 16; ++q) {
+      const int r = wave * 16 + q;
+      v[q] = (r < m && i < m) ? A[static_cast<int64_t>(r0 + r) * n + r0 + i] : 0.0;
+    }
 #pragma unroll
-    for (int r = 0; r < kB; ++r) Ls[r][i] = (r >= m || i >= m) ? ((r == i) ? 1.0 : 0.0) : ((i <= r) ? v[r] : 0.0);
+    for (int q = 0; q < 16; ++q) {
+      const int r = wave * 16 + q;
+      Ls[r][i] = (r >= m || i >= m) ? ((r == i) ? 1.0 : 0.0) : ((i <= r) ? v[q] : 0.0);
+    }
   }
   __syncthreads();
+  if (wave == 0) {
   double a[kB];
 #pragma unroll
   for (int c = 0; c < kB; ++c) a[c] = Ls[i][c];
@@ -235,15 +245,21 @@ __global__ void __launch_bounds__(64) chol_diag_inv_kernel(double* __restrict__ 
 #pragma unroll
   for (int c = 0; c < kB; ++c) Ls[i][c] = (c <= i) ? a[c] : 0.0;
   rinv[i] = 1.0 / Ls[i][i];
-  __syncthreads();
-  {
-    double v[kB];  // all LDS reads first, then the guarded stores
-#pragma unroll
-    for (int r = 0; r < kB; ++r) v[r] = Ls[r][i];
-#pragma unroll
-    for (int r = 0; r < kB; ++r)
-      if (r < m && i <= r) A[static_cast<int64_t>(r0 + r) * n + r0 + i] = v[r];
   }
+  __syncthreads();
+  if (wave > 0) {  // waves 1-3 store L while wave 0 inverts
+    double v[22];
+#pragma unroll
+    for (int q = 0; q < 22; ++q) {
+      const int r = (wave - 1) + 3 * q;
+      v[q] = (r < kB) ? Ls[r][i] : 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < 22; ++q) {
+      const int r = (wave - 1) + 3 * q;
+      if (r < m && i <= r) A[static_cast<int64_t>(r0 + r) * n + r0 + i] = v[q];
+    }
+  } else {
   // Inverse by 16x16 blocks, X = inv(L):
   //   X_bb = inv(L_bb)          forward substitution, lane = (b, column),
   //   X_ij = -X_ii sum_{k=j}^{i-1} L_ik X_kj   for i > j, by block distance,
@@ -295,13 +311,20 @@ __global__ void __launch_bounds__(64) chol_diag_inv_kernel(double* __restrict__ 
       __builtin_amdgcn_wave_barrier();
     }
   }
+  }
+  __syncthreads();
   {
-    double v[kB];  // all LDS reads first, then the guarded stores
+    double v[16];  // all LDS reads first, then the guarded stores
 #pragma unroll
-    for (int r = 0; r < kB; ++r) v[r] = ((r >> 4) >= (i >> 4)) ? Xs[r][i] : 0.0;
+    for (int q = 0; q < 16; ++q) {
+      const int r = wave * 16 + q;
+      v[q] = ((r >> 4) >= (i >> 4)) ? Xs[r][i] : 0.0;
+    }
 #pragma unroll
-    for (int r = 0; r < kB; ++r)
-      if (r < m && i < m) Linv[static_cast<int64_t>(r0 + r) * n + r0 + i] = v[r];
+    for (int q = 0; q < 16; ++q) {
+      const int r = wave * 16 + q;
+      if (r < m && i < m) Linv[static_cast<int64_t>(r0 + r) * n + r0 + i] = v[q];
+    }
   }
 }
 
@@ -458,9 +481,10 @@ __global__ void __launch_bounds__(256) chol_trsm_kernel(double* __restrict__ A, 
 
 // A_ij -= sum_{q0 <= q < q1} L_iq L_jq^T (K = 64 (q1 - q0)) over the tiles
 // of one launch: mode 0, the lower triangle j0 <= j <= i < nblk, row by row;
-// mode 1, the block column j = j0, rows i = j0 + blockIdx.x.
+// mode 1, the block column j = j0, rows i = j0 + blockIdx.x; mode 2, the
+// block columns j0 <= j < j0 + w, rows j <= i < nblk, column by column.
 __global__ void __launch_bounds__(256) chol_update_kernel(double* __restrict__ A, int n, int q0, int q1, int j0,
-                                                          int mode) {
+                                                          int mode, int nblk, int w) {
   __shared__ TileSmem sm;
   int i, j;
   if (mode == 0) {
@@ -472,9 +496,17 @@ __global__ void __launch_bounds__(256) chol_update_kernel(double* __restrict__ A
     }
     i = j0 + ii;
     j = j0 + t;
-  } else {
+  } else if (mode == 1) {
     i = j0 + blockIdx.x;
     j = j0;
+  } else {
+    int t = blockIdx.x;
+    j = j0;
+    for (int c = 0; c + 1 < w && t >= nblk - j; ++c) {
+      t -= nblk - j;
+      ++j;
+    }
+    i = j + t;
   }
   const int r0 = i * kB, cc0 = j * kB, k0 = q0 * kB;
   const int mv = (n - r0 < kB) ? n - r0 : kB;
@@ -775,9 +807,9 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
     e = hipGetLastError();           \
     if (e != hipSuccess) return e;   \
   } while (0)
-  e = hipMemsetAsync(info, 0, sizeof(int), s);
+  e = zero_words(info, 1, s);
   if (e != hipSuccess) return e;
-  e = hipMemsetAsync(Linv, 0, static_cast<size_t>(n) * n * 8, s);
+  e = zero_words(Linv, static_cast<size_t>(n) * n, s);
   if (e != hipSuccess) return e;
   const int nb = (n + 255) / 256;
   hipLaunchKernelGGL(prep_diag_kernel, dim3(nb), dim3(256), 0, s, H, n, dd, dead, info);
@@ -791,30 +823,74 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
   GPTQ_CHECK_LAUNCH();
 
   const int nblk = (n + kB - 1) / kB;
+  // Look-ahead: after a group, only the next group's block columns are
+  // updated on the caller's stream (the strip); the rest of the trailing
+  // matrix is updated on a second stream while the next group's
+  // latency-bound chain (column update, diagonal block, panel solve) runs.
+  // The strip of group g+1 waits for the side pass of group g, which covers
+  // its columns; nothing else the chain touches overlaps the side pass.
+  hipStream_t side = nullptr;
+  EventPair ev;
+  if (nblk > 2 * kGroup) {
+    e = side_stream(&side);
+    if (e == hipSuccess) e = ev.create();
+    if (e != hipSuccess) return e;
+  }
+  hipEvent_t ev_fork = ev.fork, ev_join = ev.join;
+  bool pending = false;  // a side pass is in flight
   for (int k0 = 0; k0 < nblk; k0 += kGroup) {
     const int ke = (k0 + kGroup < nblk) ? k0 + kGroup : nblk;
     for (int k = k0; k < ke; ++k) {
       if (k > k0) {  // block column k receives the group's earlier panels
-        hipLaunchKernelGGL(chol_update_kernel, dim3(nblk - k), dim3(256), 0, s, A, n, k0, k, k, 1);
+        hipLaunchKernelGGL(chol_update_kernel, dim3(nblk - k), dim3(256), 0, s, A, n, k0, k, k, 1, nblk, 1);
         GPTQ_CHECK_LAUNCH();
       }
-      hipLaunchKernelGGL(chol_diag_inv_kernel, dim3(1), dim3(64), 0, s, A, Linv, n, k, info);
+      hipLaunchKernelGGL(chol_diag_inv_kernel, dim3(1), dim3(256), 0, s, A, Linv, n, k, info);
       GPTQ_CHECK_LAUNCH();
       if (k + 1 < nblk) {
         hipLaunchKernelGGL(chol_trsm_kernel, dim3(nblk - k - 1), dim3(256), 0, s, A, Linv, n, k);
         GPTQ_CHECK_LAUNCH();
       }
     }
-    if (ke < nblk) {  // everything right of the group, K = 64 * group width
-      const int nt = (n - ke * kB + kT2 - 1) / kT2;
+    if (ke >= nblk) break;
+    const int ne = (ke + kGroup < nblk) ? ke + kGroup : nblk;
+    // the rest (block columns >= ne), K = 64 * group width
+    if (ne < nblk) {
+      hipStream_t st = side ? side : s;
+      if (side) {
+        e = hipEventRecord(ev_fork, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(side, ev_fork, 0);
+        if (e != hipSuccess) return e;
+      }
+      const int nt = (n - ne * kB + kT2 - 1) / kT2;
       if (nt * (nt + 1) / 2 >= kBigTiles) {
-        hipLaunchKernelGGL(chol_trail_kernel, dim3(nt * (nt + 1) / 2), dim3(256), 0, s, A, n, k0, ke, ke * kB);
+        hipLaunchKernelGGL(chol_trail_kernel, dim3(nt * (nt + 1) / 2), dim3(256), 0, st, A, n, k0, ke, ne * kB);
       } else {
-        const int rest = nblk - ke;
-        hipLaunchKernelGGL(chol_update_kernel, dim3(rest * (rest + 1) / 2), dim3(256), 0, s, A, n, k0, ke, ke, 0);
+        const int rest = nblk - ne;
+        hipLaunchKernelGGL(chol_update_kernel, dim3(rest * (rest + 1) / 2), dim3(256), 0, st, A, n, k0, ke, ne, 0,
+                           nblk, 1);
       }
       GPTQ_CHECK_LAUNCH();
     }
+    // the strip (block columns ke .. ne-1), after the previous side pass
+    if (pending) {
+      e = hipStreamWaitEvent(s, ev_join, 0);
+      if (e != hipSuccess) return e;
+      pending = false;
+    }
+    if (side && ne < nblk) {
+      e = hipEventRecord(ev_join, side);
+      if (e != hipSuccess) return e;
+      pending = true;
+    }
+    int strip = 0;
+    for (int j = ke; j < ne; ++j) strip += nblk - j;
+    hipLaunchKernelGGL(chol_update_kernel, dim3(strip), dim3(256), 0, s, A, n, k0, ke, ke, 2, nblk, ne - ke);
+    GPTQ_CHECK_LAUNCH();
+  }
+  if (pending) {
+    e = hipStreamWaitEvent(s, ev_join, 0);
+    if (e != hipSuccess) return e;
   }
   for (int sz = kB; sz < n; sz *= 2) {
     const int pairs = (n + 2 * sz - 1) / (2 * sz);
