@@ -540,7 +540,7 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
     e = hipGetLastError();         \
     if (e != hipSuccess) return e; \
   } while (0)
-  e = hipMemsetAsync(rowloss, 0, static_cast<size_t>(rows) * 8, s);
+  e = zero_words(rowloss, static_cast<size_t>(rows), s);
   if (e != hipSuccess) return e;
   dim3 gg((n + 255) / 256, rows < 65535 ? rows : 65535);
   if (wdt == DT_BF16) hipLaunchKernelGGL(gather_w_kernel<DT_BF16>, gg, dim3(256), 0, s, W, ldw, perm, dead, rows, n, Wk);
