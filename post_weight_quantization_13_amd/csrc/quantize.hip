@@ -59,11 +59,177 @@ __global__ void gidx_kernel(const int32_t* __restrict__ perm, int n, int gs, int
   invperm[p] = j;
 }
 
+// ---------------------------------------------------------------- split-bf16 helpers
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// 8 fp32 values -> hi and lo bf16 planes (16 bytes each).
+__device__ __forceinline__ void split8(const float (&v)[8], u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t h0 = bf16_rne_bits(v[2 * d]), h1 = bf16_rne_bits(v[2 * d + 1]);
+    const uint32_t l0 = bf16_rne_bits(v[2 * d] - __uint_as_float(h0 << 16));
+    const uint32_t l1 = bf16_rne_bits(v[2 * d + 1] - __uint_as_float(h1 << 16));
+    hi[d] = h0 | (h1 << 16);
+    lo[d] = l0 | (l1 << 16);
+  }
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16(const u32x4& a, const u32x4& b, f32x16 c) {
+  bf16x8 av, bv;
+  __builtin_memcpy(&av, &a, 16);
+  __builtin_memcpy(&bv, &b, 16);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- pre-split operands
+// The block updates multiply fp32 errors E by rows of U on the bf16 MFMA as
+// E U ~ Ehi Uhi + Ehi Ulo + Elo Uhi (see the trailing update).  Both operands
+// are split once, not per tile: U is transposed and split at the start of a
+// layer (UTh/UTl [n][n], UT[c][k] = U[k][c], so a column's k values are
+// contiguous), and the sweep writes its errors already split (Eh/El).  The
+// update kernels then stage 16-byte copies into LDS, no arithmetic.
+__global__ void __launch_bounds__(256) split_ut_kernel(const float* __restrict__ U, int n, uint16_t* __restrict__ UTh,
+                                                       uint16_t* __restrict__ UTl) {
+  __shared__ float t[64][65];
+  const int k0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) t[ty + 4 * q][tx] = U[static_cast<int64_t>(k0 + ty + 4 * q) * n + c0 + tx];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int c = ty + 4 * q;
+    const float v = t[tx][c];
+    const uint32_t h = bf16_rne_bits(v);
+    const uint32_t l = bf16_rne_bits(v - __uint_as_float(h << 16));
+    UTh[static_cast<int64_t>(c0 + c) * n + k0 + tx] = static_cast<uint16_t>(h);
+    UTl[static_cast<int64_t>(c0 + c) * n + k0 + tx] = static_cast<uint16_t>(l);
+  }
+}
+
+// Staged operand planes: rows of 64 bf16 values (128 bytes = eight 16-byte
+// units of 8 k); unit u of row r sits at slot u ^ (r & 7), so the 16-byte
+// stores (8 lanes on one row) and the fragment reads (8 lanes on 8
+// consecutive rows) each touch 8 distinct 16-byte bank groups.
+constexpr int kTK = 64;
+__device__ __forceinline__ int tk_offset(int row, int c) { return row * (kTK * 2) + ((c ^ (row & 7)) << 4); }
+
+// ---------------------------------------------------------------- pending block update
+// Before its chain, a sweep workgroup applies to its own 64 rows x 128
+// columns of the working weights (held in LDS) the updates of earlier blocks
+// that have not been written to memory: Ws -= Ea Ua + Eb Ub, split-bf16 MFMA
+// with fp32 accumulation.  Each segment is split errors (Eh/El [rows, K], row
+// stride ldE) and the K matching rows of U at this block's columns (from
+// UTh/UTl).  K runs in chunks of 64 staged in LDS, the next two chunks' copies
+// in flight in registers during the current chunk's MFMAs.  Wave w owns columns
+// 32w..32w+31 as two v_mfma_f32_32x32x16_bf16 tiles (rows 0-31 and 32-63);
+// accumulator q of lane l is row 8(q/4) + 4(l/32) + q%4, column l%32.
+struct PendSmem {
+  uint8_t eh[kRowsSweep * kTK * 2], el[kRowsSweep * kTK * 2];
+  uint8_t uh[kBlk * kTK * 2], ul[kBlk * kTK * 2];
+};
+struct PendSeg {
+  const uint16_t* Eh;  // split errors, columns 0 .. K-1
+  const uint16_t* El;
+  int K;               // a multiple of kTK
+  int urow;            // first row of U matching column 0 of E
+};
+
+__device__ __forceinline__ void pending_update(float (*Ws)[kRowsSweep], const uint16_t* __restrict__ UTh,
+                                               const uint16_t* __restrict__ UTl, int n, int rows, int rbase, int i1,
+                                               int ldE, const PendSeg& sa, const PendSeg& sb, PendSmem& sm) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nca = sa.K / kTK, nc = nca + sb.K / kTK;
+  if (nc == 0) return;
+  // two register sets: while one chunk is in LDS, the next two are in flight
+  u32x4 re[2][2][2], ru[2][2][4];  // [set][plane][unit]
+  auto gload = [&](int c, int set) {
+    const bool first = c < nca;
+    const uint16_t* Eh = first ? sa.Eh : sb.Eh;
+    const uint16_t* El = first ? sa.El : sb.El;
+    const int kc = (first ? c : c - nca) * kTK;
+    const int ur = (first ? sa.urow : sb.urow) + kc;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int u = tid + 256 * q, row = u >> 3, unit = u & 7;
+      const int r = rbase + row;
+      const int64_t off = static_cast<int64_t>(r) * ldE + kc + 8 * unit;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      re[set][0][q] = (r < rows) ? *reinterpret_cast<const u32x4*>(Eh + off) : z;
+      re[set][1][q] = (r < rows) ? *reinterpret_cast<const u32x4*>(El + off) : z;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int u = tid + 256 * q, col = u >> 3, unit = u & 7;
+      const int64_t off = static_cast<int64_t>(i1 + col) * n + ur + 8 * unit;
+      ru[set][0][q] = *reinterpret_cast<const u32x4*>(UTh + off);
+      ru[set][1][q] = *reinterpret_cast<const u32x4*>(UTl + off);
+    }
+  };
+  f32x16 acc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[i][q] = 0.0f;
+  auto step = [&](int c, int set) {
+    if (c) __syncthreads();  // the previous chunk's fragments have been read
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int u = tid + 256 * q;
+      *reinterpret_cast<u32x4*>(sm.eh + tk_offset(u >> 3, u & 7)) = re[set][0][q];
+      *reinterpret_cast<u32x4*>(sm.el + tk_offset(u >> 3, u & 7)) = re[set][1][q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int u = tid + 256 * q;
+      *reinterpret_cast<u32x4*>(sm.uh + tk_offset(u >> 3, u & 7)) = ru[set][0][q];
+      *reinterpret_cast<u32x4*>(sm.ul + tk_offset(u >> 3, u & 7)) = ru[set][1][q];
+    }
+    __syncthreads();
+    if (c + 2 < nc) gload(c + 2, set);
+#pragma unroll
+    for (int ks = 0; ks < kTK / 16; ++ks) {
+      const int unit = 2 * ks + (lane >> 5);
+      u32x4 ah[2], al[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = 32 * i + (lane & 31);
+        ah[i] = *reinterpret_cast<const u32x4*>(sm.eh + tk_offset(row, unit));
+        al[i] = *reinterpret_cast<const u32x4*>(sm.el + tk_offset(row, unit));
+      }
+      const int col = 32 * wave + (lane & 31);
+      const u32x4 bh = *reinterpret_cast<const u32x4*>(sm.uh + tk_offset(col, unit));
+      const u32x4 bl = *reinterpret_cast<const u32x4*>(sm.ul + tk_offset(col, unit));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        acc[i] = mfma_bf16(al[i], bh, acc[i]);
+        acc[i] = mfma_bf16(ah[i], bl, acc[i]);
+        acc[i] = mfma_bf16(ah[i], bh, acc[i]);
+      }
+    }
+  };
+  gload(0, 0);
+  if (nc > 1) gload(1, 1);
+  for (int c = 0; c < nc; c += 2) {
+    step(c, 0);
+    if (c + 1 < nc) step(c + 1, 1);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      Ws[32 * wave + (lane & 31)][32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)] -= acc[i][q];
+}
+
 // ---------------------------------------------------------------- sweep
 // One workgroup (4 waves) per strip of 64 rows and one block of 128 columns;
 // lane = row in every wave.  LDS: UT[k][j] = U[i1+j][i1+k] (the block of U,
 // transposed), the 64x128 block of Wk column-major over rows, and the errors
-// of the last two 16-column sub-blocks.
+// of the last two 16-column sub-blocks.  The block first receives its pending
+// updates (pending_update above), then the chain runs.
 // Sub-block s (16 columns), two barriers:
 //   wave 0   : the sequential chain -- quantize column j, e_j = (w - q) / U_jj,
 //              rank-1 update of the remaining columns of the sub-block (the
@@ -82,11 +248,13 @@ constexpr int kSubs = kBlk / kSub;  // 8
 
 template <int BITS, bool SYM>
 __global__ void __launch_bounds__(256) sweep_block_kernel(
-    float* __restrict__ Wk, const float* __restrict__ U, int n, int rows, int i1,
-    uint8_t* __restrict__ codes, float* __restrict__ E, int ldE, uint16_t* __restrict__ scales,
-    uint16_t* __restrict__ zeros, double* __restrict__ rowloss) {
+    const float* __restrict__ Wk, const float* __restrict__ U, const uint16_t* __restrict__ UTh,
+    const uint16_t* __restrict__ UTl, int n, int rows, int i1, uint8_t* __restrict__ codes,
+    uint16_t* __restrict__ Eh, uint16_t* __restrict__ El, int ldE, PendSeg sa, PendSeg sb,
+    uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, double* __restrict__ rowloss) {
   __shared__ __attribute__((aligned(16))) float UT[kBlk][kBlk + 4];
   __shared__ float Ws[kBlk][kRowsSweep];
+  __shared__ __attribute__((aligned(16))) PendSmem psm;
   __shared__ float Es[2][kSub][kRowsSweep];
   __shared__ float rdiag[kBlk];
   const int tid = threadIdx.x;
@@ -130,6 +298,8 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
     if (tid < kBlk) rdiag[tid] = 1.0f / dg;
   }
   __syncthreads();
+  pending_update(Ws, UTh, UTl, n, rows, blockIdx.x * kRowsSweep, i1, ldE, sa, sb, psm);
+  __syncthreads();
 
   constexpr float maxq = static_cast<float>((1 << BITS) - 1);
   const float lo = SYM ? 1.0f : 0.0f;
@@ -158,7 +328,8 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
     rs = 1.0f / sv;
   }
 
-  float* erow = E + static_cast<int64_t>(valid ? r : 0) * ldE;
+  uint16_t* ehrow = Eh + static_cast<int64_t>(valid ? r : 0) * ldE;
+  uint16_t* elrow = El + static_cast<int64_t>(valid ? r : 0) * ldE;
   uint8_t* crow = codes + static_cast<int64_t>(valid ? r : 0) * n + i1;
   for (int sb = 0; sb < kSubs; ++sb) {
     const int j0 = sb * kSub;
@@ -224,9 +395,15 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
 #pragma unroll
         for (int t4 = 0; t4 < kSub / 4; ++t4) {
           *reinterpret_cast<uint32_t*>(crow + j0 + 4 * t4) = cw[t4];
-          *reinterpret_cast<f32x4*>(erow + j0 + 4 * t4) =
-              f32x4{Es[sb & 1][4 * t4][lane], Es[sb & 1][4 * t4 + 1][lane], Es[sb & 1][4 * t4 + 2][lane],
-                    Es[sb & 1][4 * t4 + 3][lane]};
+          uint32_t h[4], l[4];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const float v = Es[sb & 1][4 * t4 + d][lane];
+            h[d] = bf16_rne_bits(v);
+            l[d] = bf16_rne_bits(v - __uint_as_float(h[d] << 16));
+          }
+          *reinterpret_cast<uint2*>(ehrow + j0 + 4 * t4) = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+          *reinterpret_cast<uint2*>(elrow + j0 + 4 * t4) = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
         }
       }
     } else if (sb >= 1) {
@@ -295,8 +472,8 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
 
 // ---------------------------------------------------------------- trailing update
 // Wk[r0:r0+128, c0:c0+128] -= E[r0:r0+128, 0:K] U[i1:i1+K, c0:c0+128] for
-// columns c < ce, c0 = cb + 128*blockIdx.x, r0 = 128*blockIdx.y; E has row
-// stride ldE.
+// columns c < ce, c0 = cb + 128*blockIdx.x, r0 = 128*blockIdx.y; E given
+// split (Eh/El, row stride ldE), U as its split transpose (UTh/UTl).
 // Split-bf16 product on the bf16 MFMA: each fp32 operand x = hi + lo with
 // hi = bf16(x), lo = bf16(x - hi) (round to nearest even), and
 //   E U ~ Ehi Uhi + Ehi Ulo + Elo Uhi   (fp32 accumulation),
@@ -304,42 +481,15 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
 // term and the rounding of lo), against 2^-24 for an fp32 product.
 // K runs in chunks of 64 staged in LDS as bf16 hi/lo planes: E as [row][k], U
 // transposed as [col][k], so each MFMA operand fragment (8 consecutive k) is
-// one 16-byte read; the next chunk's global loads are in flight during the
-// current chunk's MFMAs.  The 16-byte chunk c of a 128-byte row r sits at slot
-// c ^ (r & 7), which keeps the fragment reads conflict-free.
+// one 16-byte read; the next chunk's copies are in flight during the current
+// chunk's MFMAs.
 // 256 threads; wave (wm, wn) owns a 64x64 quarter = 2x2 v_mfma_f32_32x32x16_bf16
 // tiles (accumulator q of lane l is row 8(q/4) + 4(l/32) + q%4, column l%32).
-constexpr int kTK = 64;
-
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
-  const uint32_t b = __float_as_uint(x);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
-
-// 8 fp32 values -> hi and lo bf16 planes (16 bytes each).
-__device__ __forceinline__ void split8(const float (&v)[8], u32x4& hi, u32x4& lo) {
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t h0 = bf16_rne_bits(v[2 * d]), h1 = bf16_rne_bits(v[2 * d + 1]);
-    const uint32_t l0 = bf16_rne_bits(v[2 * d] - __uint_as_float(h0 << 16));
-    const uint32_t l1 = bf16_rne_bits(v[2 * d + 1] - __uint_as_float(h1 << 16));
-    hi[d] = h0 | (h1 << 16);
-    lo[d] = l0 | (l1 << 16);
-  }
-}
-
-__device__ __forceinline__ int tk_offset(int row, int c) { return row * (kTK * 2) + ((c ^ (row & 7)) << 4); }
-
-__device__ __forceinline__ f32x16 mfma_bf16(const u32x4& a, const u32x4& b, f32x16 c) {
-  bf16x8 av, bv;
-  __builtin_memcpy(&av, &a, 16);
-  __builtin_memcpy(&bv, &b, 16);
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, c, 0, 0, 0);
-}
-
-__global__ void __launch_bounds__(256, 2) trailing_kernel(float* __restrict__ Wk, const float* __restrict__ E,
-                                                       int ldE, const float* __restrict__ U, int n, int rows,
-                                                       int i1, int K, int cb, int ce) {
+__global__ void __launch_bounds__(256, 2) trailing_kernel(float* __restrict__ Wk, const uint16_t* __restrict__ Eh,
+                                                       const uint16_t* __restrict__ El, int ldE,
+                                                       const uint16_t* __restrict__ UTh,
+                                                       const uint16_t* __restrict__ UTl, int n, int rows, int i1,
+                                                       int K, int cb, int ce) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[4][128 * kTK * 2];  // Ehi, Elo, Uhi, Ulo: 64 KB
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -354,33 +504,24 @@ __global__ void __launch_bounds__(256, 2) trailing_kernel(float* __restrict__ Wk
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  float ev[4][8], uv[4][8];
+  u32x4 re[2][4], ru[2][4];  // [plane][unit]: unit u = tid + 256q -> (row or column u/8, k-octet u%8)
   auto gload = [&](int kc) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      // E: unit -> (row, k-octet); 8 consecutive k of one row
-      const int u = tid + 256 * q;
-      const int row = u >> 3, ko = u & 7;
-      if (r0 + row < rows) {
-        const float* src = E + static_cast<int64_t>(r0 + row) * ldE + kc + 8 * ko;
-        const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
-        ev[q][0] = a[0]; ev[q][1] = a[1]; ev[q][2] = a[2]; ev[q][3] = a[3];
-        ev[q][4] = b[0]; ev[q][5] = b[1]; ev[q][6] = b[2]; ev[q][7] = b[3];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ev[q][e] = 0.0f;
-      }
+      const int u = tid + 256 * q, row = u >> 3, unit = u & 7;
+      const bool ok = r0 + row < rows;
+      const int64_t off = static_cast<int64_t>(r0 + row) * ldE + kc + 8 * unit;
+      re[0][q] = ok ? *reinterpret_cast<const u32x4*>(Eh + off) : z;
+      re[1][q] = ok ? *reinterpret_cast<const u32x4*>(El + off) : z;
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      // U: unit -> (col, k-octet); 8 rows of U at one column, transposed into LDS
-      const int u = tid + 256 * q;
-      const int col = u & 127, ko = u >> 7;
+      const int u = tid + 256 * q, col = u >> 3, unit = u & 7;
       const bool ok = c0 + col < ce;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        uv[q][e] = ok ? U[static_cast<int64_t>(i1 + kc + 8 * ko + e) * n + c0 + col] : 0.0f;
+      const int64_t off = static_cast<int64_t>(c0 + col) * n + i1 + kc + 8 * unit;
+      ru[0][q] = ok ? *reinterpret_cast<const u32x4*>(UTh + off) : z;
+      ru[1][q] = ok ? *reinterpret_cast<const u32x4*>(UTl + off) : z;
     }
   };
   gload(0);
@@ -389,20 +530,10 @@ __global__ void __launch_bounds__(256, 2) trailing_kernel(float* __restrict__ Wk
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int u = tid + 256 * q;
-      const int row = u >> 3, ko = u & 7;
-      u32x4 hi, lo;
-      split8(ev[q], hi, lo);
-      *reinterpret_cast<u32x4*>(lds[0] + tk_offset(row, ko)) = hi;
-      *reinterpret_cast<u32x4*>(lds[1] + tk_offset(row, ko)) = lo;
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int u = tid + 256 * q;
-      const int col = u & 127, ko = u >> 7;
-      u32x4 hi, lo;
-      split8(uv[q], hi, lo);
-      *reinterpret_cast<u32x4*>(lds[2] + tk_offset(col, ko)) = hi;
-      *reinterpret_cast<u32x4*>(lds[3] + tk_offset(col, ko)) = lo;
+      *reinterpret_cast<u32x4*>(lds[0] + tk_offset(u >> 3, u & 7)) = re[0][q];
+      *reinterpret_cast<u32x4*>(lds[1] + tk_offset(u >> 3, u & 7)) = re[1][q];
+      *reinterpret_cast<u32x4*>(lds[2] + tk_offset(u >> 3, u & 7)) = ru[0][q];
+      *reinterpret_cast<u32x4*>(lds[3] + tk_offset(u >> 3, u & 7)) = ru[1][q];
     }
     __syncthreads();
     if (kc + kTK < K) gload(kc + kTK);
@@ -501,19 +632,21 @@ __global__ void __launch_bounds__(256) loss_reduce_kernel(const double* __restri
 static inline size_t al256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 size_t quantize_workspace(int64_t rows, int64_t n) {
-  return al256(static_cast<size_t>(rows) * n * 4)      // Wk
-         + al256(static_cast<size_t>(rows) * kSuper * 4) // E of a super-block
-         + al256(static_cast<size_t>(rows) * n)        // codes
-         + al256(static_cast<size_t>(rows) * 8)        // rowloss
-         + al256(static_cast<size_t>(n) * 4)           // invperm
-         + 256;                                        // loss scalar
+  return al256(static_cast<size_t>(rows) * n * 4)           // Wk
+         + 4 * al256(static_cast<size_t>(rows) * kSuper * 2) // Eh, El of two super-blocks
+         + 2 * al256(static_cast<size_t>(n) * n * 2)         // UTh, UTl
+         + al256(static_cast<size_t>(rows) * n)             // codes
+         + al256(static_cast<size_t>(rows) * 8)             // rowloss
+         + al256(static_cast<size_t>(n) * 4)                // invperm
+         + 256;                                             // loss scalar
 }
 
 template <int BITS, bool SYM>
-static void launch_sweep(dim3 g, hipStream_t s, float* Wk, const float* U, int n, int rows, int i1, uint8_t* codes,
-                         float* E, int ldE, uint16_t* scales, uint16_t* zeros, double* rowloss) {
-  hipLaunchKernelGGL((sweep_block_kernel<BITS, SYM>), g, dim3(256), 0, s, Wk, U, n, rows, i1, codes, E, ldE, scales,
-                     zeros, rowloss);
+static void launch_sweep(dim3 g, hipStream_t s, const float* Wk, const float* U, const uint16_t* UTh,
+                         const uint16_t* UTl, int n, int rows, int i1, uint8_t* codes, uint16_t* Eh, uint16_t* El,
+                         const PendSeg& sa, const PendSeg& sb, uint16_t* scales, uint16_t* zeros, double* rowloss) {
+  hipLaunchKernelGGL((sweep_block_kernel<BITS, SYM>), g, dim3(256), 0, s, Wk, U, UTh, UTl, n, rows, i1, codes, Eh, El,
+                     kSuper, sa, sb, scales, zeros, rowloss);
 }
 
 hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* dead, int64_t n64, int bits,
@@ -524,8 +657,15 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
   uint8_t* p = static_cast<uint8_t*>(ws);
   float* Wk = reinterpret_cast<float*>(p);
   p += al256(static_cast<size_t>(rows) * n * 4);
-  float* E = reinterpret_cast<float*>(p);
-  p += al256(static_cast<size_t>(rows) * kSuper * 4);
+  uint16_t* Ebuf[4];  // Eh, El of super-block parity 0, then parity 1
+  for (int q = 0; q < 4; ++q) {
+    Ebuf[q] = reinterpret_cast<uint16_t*>(p);
+    p += al256(static_cast<size_t>(rows) * kSuper * 2);
+  }
+  uint16_t* UTh = reinterpret_cast<uint16_t*>(p);
+  p += al256(static_cast<size_t>(n) * n * 2);
+  uint16_t* UTl = reinterpret_cast<uint16_t*>(p);
+  p += al256(static_cast<size_t>(n) * n * 2);
   uint8_t* codes = p;
   p += al256(static_cast<size_t>(rows) * n);
   double* rowloss = reinterpret_cast<double*>(p);
@@ -549,34 +689,85 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
   GPTQ_CHECK_LAUNCH();
   hipLaunchKernelGGL(gidx_kernel, dim3((n + 255) / 256), dim3(256), 0, s, perm, n, kBlk, g_idx, invperm);
   GPTQ_CHECK_LAUNCH();
+  hipLaunchKernelGGL(split_ut_kernel, dim3(n / 64, n / 64), dim3(256), 0, s, U, n, UTh, UTl);
+  GPTQ_CHECK_LAUNCH();
 
-  // Two-level lazy batching: inside a super-block of kSuper columns each
-  // 128-column block updates only the rest of its super-block; the columns
-  // beyond it receive the whole super-block's errors in one K = kSuper update,
-  // so the working weights are read and written once per super-block rather
-  // than once per block.  E holds the super-block's scaled errors [rows, kSuper].
+  // Lazy updates in super-blocks of kSuper columns.  A block's sweep applies
+  // to its own rows and columns the errors of the earlier blocks of its
+  // super-block and of the whole previous super-block (pending_update); the
+  // errors of super-block j reach the columns from super-block j+2 on in one
+  // wide update (K = kSuper) on a second stream, overlapping the sweeps of
+  // super-block j+1.  Super-block j+2 waits for that update before it starts.
+  // E holds the errors of two super-blocks (alternating), [rows, kSuper] each.
   const dim3 gs((rows + kRowsSweep - 1) / kRowsSweep);
   const int rt = (rows + 127) / 128;
-  for (int s1 = 0; s1 < n; s1 += kSuper) {
+  const int nsb = (n + kSuper - 1) / kSuper;
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join[2] = {nullptr, nullptr};
+  struct Events {
+    hipEvent_t* e[3];
+    ~Events() {
+      for (hipEvent_t* p : e)
+        if (*p) (void)hipEventDestroy(*p);
+    }
+  } events{{&ev_fork, &ev_join[0], &ev_join[1]}};
+  if (nsb > 2) {
+    e = side_stream(&side);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_join[0], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_join[1], hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+  }
+  bool joined[2] = {true, true};  // no wide update of that parity in flight
+  for (int j = 0; j < nsb; ++j) {
+    const int s1 = j * kSuper;
     const int s2 = (s1 + kSuper < n) ? s1 + kSuper : n;
+    uint16_t* Ejh = Ebuf[2 * (j & 1)];
+    uint16_t* Ejl = Ebuf[2 * (j & 1) + 1];
+    const uint16_t* Eph = Ebuf[2 * ((j + 1) & 1)];
+    const uint16_t* Epl = Ebuf[2 * ((j + 1) & 1) + 1];
+    if (!joined[j & 1]) {  // the wide update of super-block j-2 (columns >= s1; reads E[j & 1])
+      e = hipStreamWaitEvent(s, ev_join[j & 1], 0);
+      if (e != hipSuccess) return e;
+      joined[j & 1] = true;
+    }
+    const PendSeg sa{Eph, Epl, (j > 0) ? kSuper : 0, s1 - kSuper};
     for (int i1 = s1; i1 < s2; i1 += kBlk) {
-      const int i2 = i1 + kBlk;
-      float* Eb = E + (i1 - s1);
-      if (bits == 4 && !sym) launch_sweep<4, false>(gs, s, Wk, U, n, rows, i1, codes, Eb, kSuper, scales, zeros, rowloss);
-      else if (bits == 4 && sym) launch_sweep<4, true>(gs, s, Wk, U, n, rows, i1, codes, Eb, kSuper, scales, zeros, rowloss);
-      else if (bits == 3 && !sym) launch_sweep<3, false>(gs, s, Wk, U, n, rows, i1, codes, Eb, kSuper, scales, zeros, rowloss);
-      else launch_sweep<3, true>(gs, s, Wk, U, n, rows, i1, codes, Eb, kSuper, scales, zeros, rowloss);
+      const PendSeg sb{Ejh, Ejl, i1 - s1, s1};
+      uint16_t* Ebh = Ejh + (i1 - s1);
+      uint16_t* Ebl = Ejl + (i1 - s1);
+      if (bits == 4 && !sym)
+        launch_sweep<4, false>(gs, s, Wk, U, UTh, UTl, n, rows, i1, codes, Ebh, Ebl, sa, sb, scales, zeros, rowloss);
+      else if (bits == 4 && sym)
+        launch_sweep<4, true>(gs, s, Wk, U, UTh, UTl, n, rows, i1, codes, Ebh, Ebl, sa, sb, scales, zeros, rowloss);
+      else if (bits == 3 && !sym)
+        launch_sweep<3, false>(gs, s, Wk, U, UTh, UTl, n, rows, i1, codes, Ebh, Ebl, sa, sb, scales, zeros, rowloss);
+      else
+        launch_sweep<3, true>(gs, s, Wk, U, UTh, UTl, n, rows, i1, codes, Ebh, Ebl, sa, sb, scales, zeros, rowloss);
       GPTQ_CHECK_LAUNCH();
-      if (i2 < s2) {
-        hipLaunchKernelGGL(trailing_kernel, dim3((s2 - i2 + 127) / 128, rt), dim3(256), 0, s, Wk, Eb, kSuper, U, n,
-                           rows, i1, kBlk, i2, s2);
-        GPTQ_CHECK_LAUNCH();
+    }
+    const int wide = s2 + kSuper;  // first column of super-block j+2
+    if (wide < n) {
+      hipStream_t st = side ? side : s;
+      if (side) {
+        e = hipEventRecord(ev_fork, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(side, ev_fork, 0);
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL(trailing_kernel, dim3((n - wide + 127) / 128, rt), dim3(256), 0, st, Wk, Ejh, Ejl, kSuper,
+                         UTh, UTl, n, rows, s1, s2 - s1, wide, n);
+      GPTQ_CHECK_LAUNCH();
+      if (side) {
+        e = hipEventRecord(ev_join[j & 1], side);
+        if (e != hipSuccess) return e;
+        joined[j & 1] = false;
       }
     }
-    if (s2 < n) {
-      hipLaunchKernelGGL(trailing_kernel, dim3((n - s2 + 127) / 128, rt), dim3(256), 0, s, Wk, E, kSuper, U, n, rows,
-                         s1, s2 - s1, s2, n);
-      GPTQ_CHECK_LAUNCH();
+  }
+  for (int par = 0; par < 2; ++par) {
+    if (!joined[par]) {
+      e = hipStreamWaitEvent(s, ev_join[par], 0);
+      if (e != hipSuccess) return e;
     }
   }
   dim3 gp((rows + 255) / 256, n / 32);  // n <= 65535 * 32 is checked by the caller

@@ -150,6 +150,10 @@ def test_identity_hessian_is_rtn_bit_exact(g, bits, sym):
 CASES = [
     ("toy256", None),
     ("attn4096", dict(rows=200, n=512, tokens=4096)),
+    # three super-blocks of 512 columns: the first one's errors reach the
+    # third through the wide update (the second stream); 200 rows leave a
+    # ragged row tile
+    ("attn4096", dict(rows=200, n=1536, tokens=4096)),
     ("mlpdown11008", dict(rows=136, n=640, tokens=4096)),
     ("down28672", dict(rows=72, n=768, tokens=8192)),
 ]
@@ -180,6 +184,42 @@ def test_layer_end_to_end(g, name, size):
     assert abs(out["loss"] - ref["L"]) <= 0.01 * ref["L"]
     rtn = oracle.rtn(wv.astype(np.float64), _ocfg(wl))
     assert rel < oracle.rel_loss(wv, rtn["What"], Href)
+
+
+def test_shared_hessian_several_layers(g):
+    """One Hessian and one prepare serve several linears with the same inputs
+    (q, k, v of a decoder block); each quantize call matches the oracle."""
+    import dataclasses
+    import torch
+    base = synth.get("llama2block")
+    n = 384
+    wl = dataclasses.replace(
+        base, name="llama2block@qkv", tokens=4096, xsets=((n, "factor", 0, 1.0),),
+        linears=tuple(dataclasses.replace(lin, rows=r, n=n) for lin, r in zip(base.linears[:3], (96, 128, 160))))
+    x_raw = synth.activations_raw(wl, 0)
+    xv = synth.bf16_value(x_raw)
+    cfg = _cfg(g, wl)
+    H = torch.empty((n, n), dtype=torch.float64, device="cuda")
+    g.gptq_hessian_accumulate(H, 0, to_device(x_raw, "bf16"))
+    U, perm, dead = g.prepare(H, cfg)
+    Href, _ = oracle.hessian(xv)
+    p = oracle.prepare(Href, wl.damp, wl.desc_act)
+    for li, lin in enumerate(wl.linears):
+        w_raw = synth.weights_raw(wl, li)
+        wv = synth.bf16_value(w_raw)
+        wd = to_device(w_raw, "bf16")
+        out = g.quantize_layer(U, perm, dead, cfg, wd)
+        rel = g.layer_loss(H, wd, out, cfg)
+        ref = oracle.quantize_layer(wv.astype(np.float64), p["U"], p["perm"], p["dead"], _ocfg(wl),
+                                    qdtype=np.float32, block=128)
+        What16 = oracle.dequantize(ref["qweight"], ref["scales"], ref["zeros"], ref["g_idx"], wl.bits, lin.rows, n)
+        ref["rel_loss"] = oracle.rel_loss(wv, What16, Href)
+        m = compare_layer(out, ref, wl.bits, n, wv, Href, rel)
+        print(f"{lin.name}: {m}")
+        assert m["agree"] >= 0.999
+        assert m["s_frac"] >= 0.999 and m["z_frac"] >= 0.999
+        assert m["gidx_ok"] and m["pack_ok"]
+        assert m["loss_rel"] <= 0.01
 
 
 def test_quantize_deterministic_and_rows_independent(g):
