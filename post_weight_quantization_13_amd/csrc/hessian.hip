@@ -81,7 +81,8 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
     for (int d = 0; d < 4; ++d) {
       const uint32_t lo = in[2 * d][f >> 1];      // token 2d
       const uint32_t hi = in[2 * d + 1][f >> 1];  // token 2d+1
-      out[f][d] = (f & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+      // one v_perm_b32: bytes {lo.0, lo.1, hi.0, hi.1} for even f, {lo.2, lo.3, hi.2, hi.3} for odd f
+      out[f][d] = __builtin_amdgcn_perm(hi, lo, (f & 1) ? 0x07060302u : 0x05040100u);
     }
   }
 }
@@ -192,19 +193,25 @@ __device__ __forceinline__ void tile_accumulate(const TileCtx& cx, int ti, int t
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
   const int b_panel = diag ? 0 : 1;
+  // The stage's 8 slices of 16 tokens; the next slice's fragments are read
+  // from LDS while the current slice's two MFMAs run.
   auto compute = [&](int buf) {
     const uint8_t* pa = panel(buf, 0);
     const uint8_t* pb = panel(buf, b_panel);
-#pragma unroll
-    for (int kk = 0; kk < kKStep / 16; ++kk) {
+    u32x4 fa[2][2], fb[2];
+    auto frag = [&](int kk, int slot) {
       const int c = kk * 2 + (lane >> 5);
-      u32x4 fa[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        fa[i] = *reinterpret_cast<const u32x4*>(pa + panel_offset_bytes(wm * 64 + i * 32 + (lane & 31), c));
-      const u32x4 fb = *reinterpret_cast<const u32x4*>(pb + panel_offset_bytes(wn * 32 + (lane & 31), c));
+        fa[slot][i] = *reinterpret_cast<const u32x4*>(pa + panel_offset_bytes(wm * 64 + i * 32 + (lane & 31), c));
+      fb[slot] = *reinterpret_cast<const u32x4*>(pb + panel_offset_bytes(wn * 32 + (lane & 31), c));
+    };
+    frag(0, 0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) acc[i] = mfma_32x32x16<DT>(fa[i], fb, acc[i]);
+    for (int kk = 0; kk < kKStep / 16; ++kk) {
+      if (kk + 1 < kKStep / 16) frag(kk + 1, (kk + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i] = mfma_32x32x16<DT>(fa[kk & 1][i], fb[kk & 1], acc[i]);
     }
   };
   int step = 0;
