@@ -14,12 +14,13 @@
 // enough codes to matter; U is rounded to fp32 at the end.
 //
 // Blocked Cholesky with 64x64 blocks, panels taken in groups of kGroup.
-// Inside a group (left-looking), per block column k:
-//   chol_update    column k receives the group's earlier panels,
-//                  A_ik -= sum_{k0 <= q < k} L_iq L_kq^T           (fp64 MFMA),
-//   chol_diag_inv  one wave factors A_kk (rows in registers) and writes
-//                  inv(L_kk) into the diagonal block of Linv,
-//   chol_trsm      L_ik = A_ik inv(L_kk)^T for every block row i > k (fp64 MFMA);
+// Inside a group (left-looking), one launch per block column k:
+//   chol_step      every work-group factors and inverts A_kk with one wave
+//                  (rows in registers) while its other waves apply the
+//                  group's earlier panels to its block A_ik,
+//                  A_ik -= sum_{k0 <= q < k} L_iq L_kq^T   (fp64 MFMA),
+//                  then forms L_ik = A_ik inv(L_kk)^T; work-group 0 writes
+//                  inv(L_kk) into the diagonal block of Linv;
 // after the group (right-looking), one chol_update pass applies all of the
 // group's panels to the trailing matrix with K = 64 kGroup, so the trailing
 // matrix is read and written once per group instead of once per panel.
@@ -114,9 +115,7 @@ __global__ void prep_gather_kernel(const double* __restrict__ H, const int32_t* 
 }
 
 // ---------------------------------------------------------------- diagonal block
-// Factor the 64x64 diagonal block k in place (rows/cols beyond n are identity)
-// and write inv(L_kk) into the diagonal block of Linv.  Wave 0 computes; all
-// four waves load and store the block.
+// A 64x64 diagonal block is factored and inverted by one wave.
 // Factorization, right-looking, lane i keeps row i in registers.  Columns go
 // in panels of four: inside a panel the pivots and the panel's own updates
 // take the needed entries of the pivot rows by readlane; then the four
@@ -149,37 +148,21 @@ __device__ __forceinline__ double rsqrt_refined(double x) {
   return r;
 }
 
-__global__ void __launch_bounds__(256) chol_diag_inv_kernel(double* __restrict__ A, double* __restrict__ Linv,
-                                                            int n, int k, int* __restrict__ info) {
-  __shared__ double Ls[kB][kB + 1];                             // the block, row-major, padded
-  __shared__ __attribute__((aligned(16))) double pan[2][kB][4];  // panel columns, [row][column]
-  __shared__ double rinv[kB];
-  __shared__ double Xs[kB][kB + 1];                             // inv(L), lower blocks
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int i = tid & 63;
-  const int r0 = k * kB;
-  const int m = (n - r0 < kB) ? n - r0 : kB;
-  // All four waves move the block in and out (16 coalesced rows each, loads
-  // in flight together); wave 0 factors and inverts.  Identity padding beyond n.
-  {
-    double v[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int r = wave * 16 + q;
-      v[q] = (r < m && i < m) ? A[static_cast<int64_t>(r0 + r) * n + r0 + i] : 0.0;
-    }
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int r = wave * 16 + q;
-      Ls[r][i] = (r >= m || i >= m) ? ((r == i) ? 1.0 : 0.0) : ((i <= r) ? v[q] : 0.0);
-    }
-  }
-  __syncthreads();
-  if (wave == 0) {
+struct DiagSmem {
+  double L[kB][kB + 1];                      // the block, then its factor, row-major, padded
+  alignas(16) double pan[2][kB][4];          // panel columns, [row][column]
+  double rinv[kB];                           // 1 / l_ii
+  double X[kB][kB + 1];                      // inv(L)
+};
+
+// Wave 0: factors the block held in d.L, lane i keeping row i in registers;
+// writes L back (zeros above the diagonal) and 1/l_ii.  Returns nonzero when
+// a pivot is not a positive finite number (it is then taken as 1).
+__device__ __forceinline__ int factor_block(DiagSmem& d) {
+  const int i = threadIdx.x & 63;
   double a[kB];
 #pragma unroll
-  for (int c = 0; c < kB; ++c) a[c] = Ls[i][c];
+  for (int c = 0; c < kB; ++c) a[c] = d.L[i][c];
   int bad = 0;
   const int z0 = opaque_zero();
   // Column j = jpn + q of panel jpn: the panel's earlier columns by readlane,
@@ -200,7 +183,7 @@ __global__ void __launch_bounds__(256) chol_diag_inv_kernel(double* __restrict__
   for (int q = 0; q < 4; ++q) pivot_step(0, q);
 #pragma unroll
   for (int jp = 0; jp + 4 < kB; jp += 4) {
-    double(*pp)[4] = reinterpret_cast<double(*)[4]>(&pan[(jp >> 2) & 1][0][0] + z0);
+    double(*pp)[4] = reinterpret_cast<double(*)[4]>(&d.pan[(jp >> 2) & 1][0][0] + z0);
     *reinterpret_cast<double2*>(&pp[i][0]) = double2{a[jp], a[jp + 1]};
     *reinterpret_cast<double2*>(&pp[i][2]) = double2{a[jp + 2], a[jp + 3]};
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the panel is in LDS
@@ -240,26 +223,17 @@ __global__ void __launch_bounds__(256) chol_diag_inv_kernel(double* __restrict__
 #pragma unroll
     for (int q = done; q < 4; ++q) pivot_step(jp + 4, q);
   }
-  if (bad && i == 0) atomicOr(info, 1);
   // L back to LDS (row i, zeros above the diagonal), 1/l_ii
 #pragma unroll
-  for (int c = 0; c < kB; ++c) Ls[i][c] = (c <= i) ? a[c] : 0.0;
-  rinv[i] = 1.0 / Ls[i][i];
-  }
-  __syncthreads();
-  if (wave > 0) {  // waves 1-3 store L while wave 0 inverts
-    double v[22];
-#pragma unroll
-    for (int q = 0; q < 22; ++q) {
-      const int r = (wave - 1) + 3 * q;
-      v[q] = (r < kB) ? Ls[r][i] : 0.0;
-    }
-#pragma unroll
-    for (int q = 0; q < 22; ++q) {
-      const int r = (wave - 1) + 3 * q;
-      if (r < m && i <= r) A[static_cast<int64_t>(r0 + r) * n + r0 + i] = v[q];
-    }
-  } else {
+  for (int c = 0; c < kB; ++c) d.L[i][c] = (c <= i) ? a[c] : 0.0;
+  d.rinv[i] = 1.0 / d.L[i][i];
+  return bad;
+}
+
+// Wave 0: d.X = inv(L) for the factor in d.L.  The strictly upper 16x16
+// blocks of d.X are left unwritten.
+__device__ __forceinline__ void invert_block(DiagSmem& d) {
+  const int i = threadIdx.x & 63;
   // Inverse by 16x16 blocks, X = inv(L):
   //   X_bb = inv(L_bb)          forward substitution, lane = (b, column),
   //   X_ij = -X_ii sum_{k=j}^{i-1} L_ik X_kj   for i > j, by block distance,
@@ -275,55 +249,40 @@ __global__ void __launch_bounds__(256) chol_diag_inv_kernel(double* __restrict__
       double s0 = 0.0, s1 = 0.0;
 #pragma unroll
       for (int q = 0; q < r; q += 2) {
-        s0 = fma(Ls[o + r][o + q], x[q], s0);
-        if (q + 1 < r) s1 = fma(Ls[o + r][o + q + 1], x[q + 1], s1);
+        s0 = fma(d.L[o + r][o + q], x[q], s0);
+        if (q + 1 < r) s1 = fma(d.L[o + r][o + q + 1], x[q + 1], s1);
       }
       const double t = ((r == c) ? 1.0 : 0.0) - (s0 + s1);
-      x[r] = (r >= c) ? t * rinv[o + r] : 0.0;
+      x[r] = (r >= c) ? t * d.rinv[o + r] : 0.0;
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) Xs[o + r][o + c] = x[r];
+    for (int r = 0; r < 16; ++r) d.X[o + r][o + c] = x[r];
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_wave_barrier();
   {
     const int lr = i & 15, lk = i >> 4;
 #pragma unroll
-    for (int d = 1; d < 4; ++d) {
+    for (int dist = 1; dist < 4; ++dist) {
 #pragma unroll
-      for (int bi = d; bi < 4; ++bi) {
-        const int bj = bi - d;
+      for (int bi = dist; bi < 4; ++bi) {
+        const int bj = bi - dist;
         f64x4 t = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
         for (int bk = bj; bk < bi; ++bk)
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks)
-            t = __builtin_amdgcn_mfma_f64_16x16x4f64(Ls[16 * bi + lr][16 * bk + 4 * ks + lk],
-                                                     Xs[16 * bk + 4 * ks + lk][16 * bj + lr], t, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f64_16x16x4f64(d.L[16 * bi + lr][16 * bk + 4 * ks + lk],
+                                                     d.X[16 * bk + 4 * ks + lk][16 * bj + lr], t, 0, 0, 0);
         f64x4 u = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          u = __builtin_amdgcn_mfma_f64_16x16x4f64(Xs[16 * bi + lr][16 * bi + 4 * ks + lk], t[ks], u, 0, 0, 0);
+          u = __builtin_amdgcn_mfma_f64_16x16x4f64(d.X[16 * bi + lr][16 * bi + 4 * ks + lk], t[ks], u, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Xs[16 * bi + lk + 4 * r][16 * bj + lr] = -u[r];
+        for (int r = 0; r < 4; ++r) d.X[16 * bi + lk + 4 * r][16 * bj + lr] = -u[r];
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_wave_barrier();
-    }
-  }
-  }
-  __syncthreads();
-  {
-    double v[16];  // all LDS reads first, then the guarded stores
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int r = wave * 16 + q;
-      v[q] = ((r >> 4) >= (i >> 4)) ? Xs[r][i] : 0.0;
-    }
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int r = wave * 16 + q;
-      if (r < m && i < m) Linv[static_cast<int64_t>(r0 + r) * n + r0 + i] = v[q];
     }
   }
 }
@@ -459,30 +418,241 @@ __device__ __forceinline__ void zero_acc(f64x4 (&acc)[2][2]) {
     for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
 }
 
-// L_ik = A_ik * inv(L_kk)^T for block rows i = k+1+blockIdx.x.
-__global__ void __launch_bounds__(256) chol_trsm_kernel(double* __restrict__ A, const double* __restrict__ Linv,
-                                                        int n, int k) {
-  __shared__ TileSmem sm;
-  const int i = k + 1 + blockIdx.x;
-  const int r0 = i * kB, c0 = k * kB;
-  const int mv = (n - r0 < kB) ? n - r0 : kB;
-  const int kv = (n - c0 < kB) ? n - c0 : kB;
+// ---------------------------------------------------------------- panel step
+// Waves 1-3: one share of a column update, rows 16 (bi0 + i) and columns
+// 16 (bj0 + j) of the 64x64 tile at (r0, c0), in accumulator layout:
+//   c = -A[r0.., c0..] + sum_{kb <= q < kb + 16 nk} A[r0 + row][q] A[c0 + col][q],
+// that is minus the updated tile.  Operands come straight from memory (the
+// panels are fresh in L2): a lane loads 4 consecutive k of its fragment row
+// per chunk of 16, and MFMA sub-step u takes the u-th of them on both
+// operands, so each product pairs equal k.  Rows >= mv read as 0; nk is even.
+template <int NI, int NJ>
+__device__ __forceinline__ void colupd_share(const double* __restrict__ A, int n, int r0, int c0, int kb, int nk,
+                                             int mv, int bi0, int bj0, f64x4 (&c)[NI][NJ]) {
+  const int lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * (bi0 + i) + lk + 4 * r, col = 16 * (bj0 + j) + lr;
+        c[i][j][r] = (row < mv) ? -A[static_cast<int64_t>(r0 + row) * n + c0 + col] : 0.0;
+      }
+  if (nk <= 0) return;
+  const double* pa[NI];
+  bool va[NI];
+  const double* pb[NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = 16 * (bi0 + i) + lr;
+    va[i] = row < mv;
+    pa[i] = A + static_cast<int64_t>(r0 + (va[i] ? row : 0)) * n + kb + 4 * lk;
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) pb[j] = A + static_cast<int64_t>(c0 + 16 * (bj0 + j) + lr) * n + kb + 4 * lk;
+  double fa[2][NI][4], fb[2][NJ][4];
+  auto load = [&](int sl, int kc) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) fa[sl][i][u] = va[i] ? pa[i][kc + u] : 0.0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) fb[sl][j][u] = pb[j][kc + u];
+  };
+  auto mma = [&](int sl) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          c[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[sl][i][u], fb[sl][j][u], c[i][j], 0, 0, 0);
+  };
+  load(0, 0);
+  for (int q = 0; q < nk; q += 2) {
+    load(1, 16 * (q + 1));
+    mma(0);
+    if (q + 2 < nk) load(0, 16 * (q + 2));
+    mma(1);
+  }
+}
+
+// One launch per block column k of a panel group [k0, ke); work-group t
+// handles block row i = k + t.  Every work-group factors and inverts the
+// diagonal block A_kk itself (wave 0), so the panel solve needs no second
+// launch; work-group 0 writes inv(L_kk) into the diagonal block of Linv.
+// For t > 0, while wave 0 factors, waves 1-3 apply the group's earlier
+// panels to A_ik (left-looking),
+//   C = A_ik - sum_{k0 <= q < k} L_iq L_kq^T,
+// keeping C in registers until the inverse is done; then the four waves form
+// L_ik = C inv(L_kk)^T and store it, and a block row inside the group also
+// takes its own diagonal block's share A_ii -= L_ik L_ik^T, so that A_kk is
+// complete when step k starts.  L_kk itself is not written back: the rest of
+// the factorization and the triangular inverse read only the blocks below the
+// diagonal and the inverted diagonal blocks.
+__global__ void __launch_bounds__(256) chol_step_kernel(double* __restrict__ A, double* __restrict__ Linv, int n,
+                                                        int k, int k0, int ke, int* __restrict__ info) {
+  __shared__ DiagSmem d;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lk = lane >> 4;
+  const int t = blockIdx.x;
+  const int bi = k + t;
+  const int c0 = k * kB, r0 = bi * kB;
+  const int m = (n - c0 < kB) ? n - c0 : kB;   // valid size of the diagonal block
+  const int mv = (n - r0 < kB) ? n - r0 : kB;  // valid rows of this block row
+  // All four waves bring in A_kk (16 coalesced rows each, loads in flight
+  // together); identity padding beyond n.
+  {
+    double v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = wave * 16 + q;
+      v[q] = (r < m && lane < m) ? A[static_cast<int64_t>(c0 + r) * n + c0 + lane] : 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = wave * 16 + q;
+      d.L[r][lane] = (r >= m || lane >= m) ? ((r == lane) ? 1.0 : 0.0) : ((lane <= r) ? v[q] : 0.0);
+    }
+  }
+  __syncthreads();
+  // minus C: waves 1-2 take block rows 2(w-1) .. +1 by block columns 0..2,
+  // wave 3 all block rows by block column 3.
+  f64x4 cw[2][3], c3[4][1];
+  // the quarter of A_ii that waves 1-3 update later: (0,0), (1,0), (1,1)
+  const int qm = (wave >= 2) ? 1 : 0, qn = (wave == 3) ? 1 : 0;
+  f64x4 old[2][2];
+  if (wave == 0) {
+    const int bad = factor_block(d);
+    if (bad && t == 0 && lane == 0) atomicOr(info, 1);
+  } else if (t > 0) {
+    if (bi < ke) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = qm * 32 + 16 * i + lk + 4 * r, col = qn * 32 + 16 * j + lr;
+            old[i][j][r] = (row < mv && col < mv) ? A[static_cast<int64_t>(r0 + row) * n + r0 + col] : 0.0;
+          }
+    }
+    const int nk = 4 * (k - k0);
+    if (wave < 3) colupd_share<2, 3>(A, n, r0, c0, k0 * kB, nk, mv, 2 * (wave - 1), 0, cw);
+    else colupd_share<4, 1>(A, n, r0, c0, k0 * kB, nk, mv, 0, 3, c3);
+  }
+  __syncthreads();
+  if (wave == 0) invert_block(d);
+  __syncthreads();
+  if (t == 0) {
+    double v[16];  // all LDS reads first, then the guarded stores
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = wave * 16 + q;
+      v[q] = ((r >> 4) >= (lane >> 4)) ? d.X[r][lane] : 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = wave * 16 + q;
+      if (r < m && lane < m) Linv[static_cast<int64_t>(c0 + r) * n + c0 + lane] = v[q];
+    }
+    return;
+  }
+  // C into d.L, which the inverse no longer needs
+  if (wave == 1 || wave == 2) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d.L[16 * (2 * (wave - 1) + i) + lk + 4 * r][16 * j + lr] = -cw[i][j][r];
+  } else if (wave == 3) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d.L[16 * i + lk + 4 * r][48 + lr] = -c3[i][0][r];
+  }
+  __syncthreads();
+  // L_ik = C inv(L_kk)^T.  inv(L_kk) is lower triangular, so result column
+  // block cb needs k blocks <= cb only (4 cb + 4 k-steps; the unwritten upper
+  // blocks of d.X are never read).  Wave (wm, wn) owns row blocks 2 wm, 2 wm + 1
+  // and column blocks {0, 3} (wn = 0) or {1, 2} (wn = 1): 40 products each.
+  const int wm = wave >> 1, wn = wave & 1;
   f64x4 acc[2][2];
   zero_acc(acc);
-  // B(q, c) = inv(L_kk)[c][q]: transposed access of the diagonal block; inv is lower
-  // triangular so only q <= c contributes, but the zero entries are stored.
-  tile_gemm_f64<true>(A + static_cast<int64_t>(r0) * n + c0, n, Linv + static_cast<int64_t>(c0) * n + c0, n,
-                      mv, kv, 0, kv, acc, sm);
-  __syncthreads();
-  tile_foreach(acc, [&](int r, int c, double v) {
-    if (r < mv && c < kv) A[static_cast<int64_t>(r0 + r) * n + c0 + c] = v;
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) {
+    if (ks < 16 - 4 * wn) {
+      const int kk = 4 * ks + lk;
+      double fa[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[i] = d.L[wm * 32 + 16 * i + lr][kk];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int cb = (j == 0) ? wn : 3 - wn;
+        if (ks < 4 * cb + 4) {
+          const double fb = d.X[16 * cb + lr][kk];
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[i], fb, acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+  auto visit = [&](auto f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          f(wm * 32 + 16 * i + lk + 4 * r, 16 * ((j == 0) ? wn : 3 - wn) + lr, acc[i][j][r]);
+  };
+  visit([&](int r, int c, double v) {
+    if (r < mv) A[static_cast<int64_t>(r0 + r) * n + c0 + c] = v;
   });
+  if (bi >= ke) return;
+  // A_ii -= L_ik L_ik^T on the lower triangle, L_ik through LDS; waves 1-3
+  // take the quarters (0,0), (1,0), (1,1) with the old values they loaded
+  // while wave 0 factored.
+  __syncthreads();
+  visit([&](int r, int c, double v) { d.L[r][c] = v; });
+  __syncthreads();
+  if (wave == 0) return;
+  f64x4 sy[2][2];
+  zero_acc(sy);
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) {
+    const int kk = 4 * ks + lk;
+    double fa[2], fb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fa[i] = d.L[qm * 32 + 16 * i + lr][kk];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[j] = d.L[qn * 32 + 16 * j + lr][kk];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sy[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[i], fb[j], sy[i][j], 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = qm * 32 + 16 * i + lk + 4 * r, col = qn * 32 + 16 * j + lr;
+        if (row < mv && col <= row) A[static_cast<int64_t>(r0 + row) * n + r0 + col] = old[i][j][r] - sy[i][j][r];
+      }
 }
 
 // A_ij -= sum_{q0 <= q < q1} L_iq L_jq^T (K = 64 (q1 - q0)) over the tiles
 // of one launch: mode 0, the lower triangle j0 <= j <= i < nblk, row by row;
-// mode 1, the block column j = j0, rows i = j0 + blockIdx.x; mode 2, the
-// block columns j0 <= j < j0 + w, rows j <= i < nblk, column by column.
+// mode 2, the block columns j0 <= j < j0 + w, rows j <= i < nblk, column by
+// column.
 __global__ void __launch_bounds__(256) chol_update_kernel(double* __restrict__ A, int n, int q0, int q1, int j0,
                                                           int mode, int nblk, int w) {
   __shared__ TileSmem sm;
@@ -496,9 +666,6 @@ __global__ void __launch_bounds__(256) chol_update_kernel(double* __restrict__ A
     }
     i = j0 + ii;
     j = j0 + t;
-  } else if (mode == 1) {
-    i = j0 + blockIdx.x;
-    j = j0;
   } else {
     int t = blockIdx.x;
     j = j0;
@@ -529,68 +696,70 @@ __global__ void __launch_bounds__(256) chol_update_kernel(double* __restrict__ A
 // the 64x64 quarter (wm*64.., wn*64..) as 4x4 v_mfma_f64_16x16x4 tiles.
 // A is addressed A[m*lda + k]; B as B[k*ldb + n] (BT = false) or B[n*ldb + k]
 // (BT = true).  Rows >= mv, columns >= nv and k >= k1 read as 0.  K runs in
-// chunks of 16 staged as [row][k] planes (odd row stride, 17 doubles: the
-// fragment reads and the stores are free of LDS bank conflicts), LDS double buffered, the next chunk's global loads
-// in flight in registers during the current chunk's 64 MFMAs per wave.
+// chunks of KC staged as [row][k] planes (odd row stride KC + 1: the fragment
+// reads and the stores are free of LDS bank conflicts), LDS double buffered,
+// the next chunk's global loads in flight in registers during the current
+// chunk's 4 KC MFMAs per wave.
 constexpr int kT2 = 128;
-constexpr int kKC2 = 16;
-constexpr int kS2 = 17;
 // 128x128 tiles pay off only with enough of them to keep every compute unit
 // busy with two; below that the 64x64 kernels run more tiles in parallel.
 constexpr int kBigTiles = 512;
-struct BigSmem {
-  double a[2][kT2][kS2];
-  double b[2][kT2][kS2];
+template <int KC>
+struct BigSmemT {
+  double a[2][kT2][KC + 1];
+  double b[2][kT2][KC + 1];
 };
+using BigSmem = BigSmemT<16>;
 
-template <bool BT>
+template <bool BT, int KC>
 __device__ __forceinline__ void gemm128(const double* __restrict__ A, int64_t lda, const double* __restrict__ B,
                                         int64_t ldb, int mv, int nv, int k0, int k1, f64x4 (&acc)[4][4],
-                                        BigSmem& sm) {
+                                        BigSmemT<KC>& sm) {
+  constexpr int E = KC / 2;  // elements of each operand per thread and chunk
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  double ra[8], rb[8];
-  // A (and B^T): thread -> row tid/2, k = 8*(tid%2) .. +7 (64 contiguous bytes)
-  // B: thread -> column tid%128, k = 8*(tid/128) .. +7 (rows of B, coalesced)
+  double ra[E], rb[E];
+  // A (and B^T): thread -> row tid/2, k = E*(tid%2) .. +E-1 (contiguous)
+  // B: thread -> column tid%128, k = E*(tid/128) .. +E-1 (rows of B, coalesced)
   auto gload = [&](int kc) {
-    const int m = tid >> 1, kb = kc + 8 * (tid & 1);
+    const int m = tid >> 1, kb = kc + E * (tid & 1);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < E; ++e) {
       const int kg = kb + e;
       ra[e] = (m < mv && kg < k1) ? A[static_cast<int64_t>(m) * lda + kg] : 0.0;
     }
     if (BT) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < E; ++e) {
         const int kg = kb + e;
         rb[e] = (m < nv && kg < k1) ? B[static_cast<int64_t>(m) * ldb + kg] : 0.0;
       }
     } else {
-      const int c = tid & 127, kb2 = kc + 8 * (tid >> 7);
+      const int c = tid & 127, kb2 = kc + E * (tid >> 7);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < E; ++e) {
         const int kg = kb2 + e;
         rb[e] = (c < nv && kg < k1) ? B[static_cast<int64_t>(kg) * ldb + c] : 0.0;
       }
     }
   };
   auto lstore = [&](int buf) {
-    const int m = tid >> 1, kh = 8 * (tid & 1);
+    const int m = tid >> 1, kh = E * (tid & 1);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm.a[buf][m][kh + e] = ra[e];
+    for (int e = 0; e < E; ++e) sm.a[buf][m][kh + e] = ra[e];
     if (BT) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm.b[buf][m][kh + e] = rb[e];
+      for (int e = 0; e < E; ++e) sm.b[buf][m][kh + e] = rb[e];
     } else {
-      const int c = tid & 127, kh2 = 8 * (tid >> 7);
+      const int c = tid & 127, kh2 = E * (tid >> 7);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm.b[buf][c][kh2 + e] = rb[e];
+      for (int e = 0; e < E; ++e) sm.b[buf][c][kh2 + e] = rb[e];
     }
   };
   auto compute = [&](int buf) {
 #pragma unroll
-    for (int ks = 0; ks < kKC2 / 4; ++ks) {
+    for (int ks = 0; ks < KC / 4; ++ks) {
       const int kk = ks * 4 + (lane >> 4);
       double fa[4], fb[4];
 #pragma unroll
@@ -604,17 +773,17 @@ __device__ __forceinline__ void gemm128(const double* __restrict__ A, int64_t ld
     }
   };
   if (k0 >= k1) return;
-  const int nch = (k1 - k0 + kKC2 - 1) / kKC2;
+  const int nch = (k1 - k0 + KC - 1) / KC;
   gload(k0);
   lstore(0);
-  if (nch > 1) gload(k0 + kKC2);
+  if (nch > 1) gload(k0 + KC);
   __syncthreads();
   int buf = 0;
   for (int c = 0; c < nch; ++c) {
     compute(buf);
     if (c + 1 >= nch) break;
     lstore(buf ^ 1);
-    if (c + 2 < nch) gload(k0 + (c + 2) * kKC2);
+    if (c + 2 < nch) gload(k0 + (c + 2) * KC);
     __syncthreads();
     buf ^= 1;
   }
@@ -646,31 +815,33 @@ __device__ __forceinline__ void big_foreach(F f) {
 // the lower triangle of tiles of the square [s0, n) x [s0, n).
 __global__ void __launch_bounds__(256, 2) chol_trail_kernel(double* __restrict__ A, int n, int q0, int q1, int s0) {
   __shared__ BigSmem sm;
-  int t = blockIdx.x;
-  int I = 0;
-  while (t > I) {
-    t -= I + 1;
-    ++I;
-  }
-  const int J = t;
-  const int r0 = s0 + I * kT2, c0 = s0 + J * kT2, k0 = q0 * kB;
-  const int mv = (n - r0 < kT2) ? n - r0 : kT2;
-  const int nv = (n - c0 < kT2) ? n - c0 : kT2;
-  f64x4 acc[4][4];
-  zero_acc4(acc);
-  gemm128<true>(A + static_cast<int64_t>(r0) * n + k0, n, A + static_cast<int64_t>(c0) * n + k0, n, mv, nv, 0,
-                (q1 - q0) * kB, acc, sm);
-  // read-modify-write one 16x16 column strip at a time: its 16 loads first
+  {
+    int t = blockIdx.x;
+    int I = 0;
+    while (t > I) {
+      t -= I + 1;
+      ++I;
+    }
+    const int J = t;
+    const int r0 = s0 + I * kT2, c0 = s0 + J * kT2, k0 = q0 * kB;
+    const int mv = (n - r0 < kT2) ? n - r0 : kT2;
+    const int nv = (n - c0 < kT2) ? n - c0 : kT2;
+    f64x4 acc[4][4];
+    zero_acc4(acc);
+    gemm128<true, 16>(A + static_cast<int64_t>(r0) * n + k0, n, A + static_cast<int64_t>(c0) * n + k0, n, mv, nv, 0,
+                  (q1 - q0) * kB, acc, sm);
+    // read-modify-write one 16x16 column strip at a time: its 16 loads first
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    double old[4][4];
-    big_foreach([&](int ii, int j, int r, int row, int col) {
-      if (ii == i) old[j][r] = (row < mv && col < nv) ? A[static_cast<int64_t>(r0 + row) * n + c0 + col] : 0.0;
-    });
-    big_foreach([&](int ii, int j, int r, int row, int col) {
-      if (ii == i && row < mv && col < nv && (I != J || col <= row))
-        A[static_cast<int64_t>(r0 + row) * n + c0 + col] = old[j][r] - acc[ii][j][r];
-    });
+    for (int i = 0; i < 4; ++i) {
+      double old[4][4];
+      big_foreach([&](int ii, int j, int r, int row, int col) {
+        if (ii == i) old[j][r] = (row < mv && col < nv) ? A[static_cast<int64_t>(r0 + row) * n + c0 + col] : 0.0;
+      });
+      big_foreach([&](int ii, int j, int r, int row, int col) {
+        if (ii == i && row < mv && col < nv && (I != J || col <= row))
+          A[static_cast<int64_t>(r0 + row) * n + c0 + col] = old[j][r] - acc[ii][j][r];
+      });
+    }
   }
 }
 
@@ -695,7 +866,7 @@ __global__ void __launch_bounds__(256, 2) trtri_big_kernel(double* __restrict__ 
   if (phase == 0) {
     // T = L21 X11 over q >= cols0, written transposed (T^T) into the strict
     // upper triangle of A through LDS, 64 columns at a time, so rows coalesce.
-    gemm128<false>(L + static_cast<int64_t>(b2 + rows0) * n + b1, n, Linv + static_cast<int64_t>(b1) * n + b1 + cols0,
+    gemm128<false, 16>(L + static_cast<int64_t>(b2 + rows0) * n + b1, n, Linv + static_cast<int64_t>(b1) * n + b1 + cols0,
                    n, mv, kT2, cols0, s, acc, sm);
     double* st = &sm.a[0][0][0];  // [64 columns][128 rows + 1]
     constexpr int kSt = kT2 + 1;
@@ -714,7 +885,7 @@ __global__ void __launch_bounds__(256, 2) trtri_big_kernel(double* __restrict__ 
   } else {
     // X21 = -X22 T over q < rows0 + 128, T read back from its transposed copy.
     const int kend = (rows0 + kT2 < s2) ? rows0 + kT2 : s2;
-    gemm128<true>(Linv + static_cast<int64_t>(b2 + rows0) * n + b2, n, L + static_cast<int64_t>(b1 + cols0) * n + b2,
+    gemm128<true, 16>(Linv + static_cast<int64_t>(b2 + rows0) * n + b2, n, L + static_cast<int64_t>(b1 + cols0) * n + b2,
                   n, mv, kT2, 0, kend, acc, sm);
     big_foreach([&](int i, int j, int r, int row, int col) {
       if (row < mv) Linv[static_cast<int64_t>(b2 + rows0 + row) * n + b1 + cols0 + col] = -acc[i][j][r];
@@ -826,7 +997,7 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
   // Look-ahead: after a group, only the next group's block columns are
   // updated on the caller's stream (the strip); the rest of the trailing
   // matrix is updated on a second stream while the next group's
-  // latency-bound chain (column update, diagonal block, panel solve) runs.
+  // latency-bound panel steps run.
   // The strip of group g+1 waits for the side pass of group g, which covers
   // its columns; nothing else the chain touches overlaps the side pass.
   hipStream_t side = nullptr;
@@ -841,20 +1012,24 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
   for (int k0 = 0; k0 < nblk; k0 += kGroup) {
     const int ke = (k0 + kGroup < nblk) ? k0 + kGroup : nblk;
     for (int k = k0; k < ke; ++k) {
-      if (k > k0) {  // block column k receives the group's earlier panels
-        hipLaunchKernelGGL(chol_update_kernel, dim3(nblk - k), dim3(256), 0, s, A, n, k0, k, k, 1, nblk, 1);
-        GPTQ_CHECK_LAUNCH();
-      }
-      hipLaunchKernelGGL(chol_diag_inv_kernel, dim3(1), dim3(256), 0, s, A, Linv, n, k, info);
+      hipLaunchKernelGGL(chol_step_kernel, dim3(nblk - k), dim3(256), 0, s, A, Linv, n, k, k0, ke, info);
       GPTQ_CHECK_LAUNCH();
-      if (k + 1 < nblk) {
-        hipLaunchKernelGGL(chol_trsm_kernel, dim3(nblk - k - 1), dim3(256), 0, s, A, Linv, n, k);
-        GPTQ_CHECK_LAUNCH();
-      }
     }
     if (ke >= nblk) break;
     const int ne = (ke + kGroup < nblk) ? ke + kGroup : nblk;
-    // the rest (block columns >= ne), K = 64 * group width
+    // the strip (block columns ke .. ne-1), after the previous side pass
+    if (pending) {
+      e = hipStreamWaitEvent(s, ev_join, 0);
+      if (e != hipSuccess) return e;
+      pending = false;
+    }
+    int strip = 0;
+    for (int j = ke; j < ne; ++j) strip += nblk - j;
+    hipLaunchKernelGGL(chol_update_kernel, dim3(strip), dim3(256), 0, s, A, n, k0, ke, ke, 2, nblk, ne - ke);
+    GPTQ_CHECK_LAUNCH();
+    // the rest (block columns >= ne), K = 64 * group width; forked after the
+    // strip so that the strip, which the next panel step waits for, is not
+    // queued behind the larger pass for compute units
     if (ne < nblk) {
       hipStream_t st = side ? side : s;
       if (side) {
@@ -871,22 +1046,12 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
                            nblk, 1);
       }
       GPTQ_CHECK_LAUNCH();
+      if (side) {
+        e = hipEventRecord(ev_join, side);
+        if (e != hipSuccess) return e;
+        pending = true;
+      }
     }
-    // the strip (block columns ke .. ne-1), after the previous side pass
-    if (pending) {
-      e = hipStreamWaitEvent(s, ev_join, 0);
-      if (e != hipSuccess) return e;
-      pending = false;
-    }
-    if (side && ne < nblk) {
-      e = hipEventRecord(ev_join, side);
-      if (e != hipSuccess) return e;
-      pending = true;
-    }
-    int strip = 0;
-    for (int j = ke; j < ne; ++j) strip += nblk - j;
-    hipLaunchKernelGGL(chol_update_kernel, dim3(strip), dim3(256), 0, s, A, n, k0, ke, ke, 2, nblk, ne - ke);
-    GPTQ_CHECK_LAUNCH();
   }
   if (pending) {
     e = hipStreamWaitEvent(s, ev_join, 0);
