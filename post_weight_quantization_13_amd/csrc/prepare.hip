@@ -115,15 +115,9 @@ __global__ void prep_gather_kernel(const double* __restrict__ H, const int32_t* 
 }
 
 // ---------------------------------------------------------------- diagonal block
-// A 64x64 diagonal block is factored and inverted by one wave.
-// Factorization, right-looking, lane i keeps row i in registers.  Columns go
-// in panels of four: inside a panel the pivots and the panel's own updates
-// take the needed entries of the pivot rows by readlane; then the four
-// columns go through LDS once and every lane applies the rank-4 update to the
-// rest of its row.  1/sqrt(pivot) is the hardware estimate refined by two
+// A 64x64 diagonal block is factored by the four waves of a work-group and
+// inverted by one.  1/sqrt(pivot) is the hardware estimate refined by two
 // Newton steps.
-// Inverse, lane c keeps column c of inv(L) in registers:
-//   x_r = (delta_rc - sum_{q<r} l_rq x_q) / l_rr, rows of L read as LDS broadcasts.
 __device__ __forceinline__ double readlane_f64(double v, int lane) {
   const uint64_t b = __double_as_longlong(v);
   const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(b), lane);
@@ -131,13 +125,12 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
   return __longlong_as_double((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// A zero the compiler cannot see through: LDS addresses formed as
-// base + opaque_zero() + constant compile to one base register plus immediate
-// offsets instead of one register per address.
-__device__ __forceinline__ int opaque_zero() {
-  int z;
-  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-  return z;
+// Barrier for exchanges through LDS only: waits for this wave's LDS accesses,
+// not for its global loads, which may stay in flight across it (the
+// column-update operands are prefetched across the whole factorization).
+// The memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ double rsqrt_refined(double x) {
@@ -150,83 +143,106 @@ __device__ __forceinline__ double rsqrt_refined(double x) {
 
 struct DiagSmem {
   double L[kB][kB + 1];                      // the block, then its factor, row-major, padded
-  alignas(16) double pan[2][kB][4];          // panel columns, [row][column]
+  alignas(16) double pan[4][kB][4];          // panel columns, [row][column]
   double rinv[kB];                           // 1 / l_ii
   double X[kB][kB + 1];                      // inv(L)
 };
 
-// Wave 0: factors the block held in d.L, lane i keeping row i in registers;
-// writes L back (zeros above the diagonal) and 1/l_ii.  Returns nonzero when
-// a pivot is not a positive finite number (it is then taken as 1).
-__device__ __forceinline__ int factor_block(DiagSmem& d) {
-  const int i = threadIdx.x & 63;
-  double a[kB];
+// All four waves: factors the block held in d.L and writes L back (zeros
+// above the diagonal).  Columns go in 16 panels of four, panel p owned by
+// wave p % 4; lane i keeps row i of its wave's 16 columns in registers.  The
+// owner finishes panel p (pivots; the panel's own updates take pivot-row
+// entries by readlane) and publishes it in LDS; after a barrier every wave
+// applies the rank-4 update to its columns beyond the panel.  The owner of
+// panel p + 1 first updates that panel, factors and publishes it, and only
+// after the next barrier applies panel p to its other columns, so the chain
+// of pivots never waits for that work.  Panels rotate through four LDS
+// buffers: panel p is read until barrier p + 2 and rewritten after barrier
+// p + 3.  Returns nonzero when a pivot is not a positive finite number (it
+// is then taken as 1).
+__device__ __forceinline__ int factor_block4(DiagSmem& d) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double a[4][4];  // slot s: panel 4 s + wave, columns 4 (4 s + wave) .. +3
 #pragma unroll
-  for (int c = 0; c < kB; ++c) a[c] = d.L[i][c];
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) a[s][t] = d.L[lane][4 * (4 * s + wave) + t];
   int bad = 0;
-  const int z0 = opaque_zero();
-  // Column j = jpn + q of panel jpn: the panel's earlier columns by readlane,
-  // then the pivot.
-  auto pivot_step = [&](int jpn, int q) {
-    const int j = jpn + q;
+  auto pivots = [&](int s) {
+    const int j0 = 4 * (4 * s + wave);
 #pragma unroll
-    for (int p = 0; p < q; ++p) a[j] = fma(-a[jpn + p], readlane_f64(a[jpn + p], j), a[j]);
-    double piv = readlane_f64(a[j], j);
-    if (!(piv > 0.0) || !(piv < INFINITY)) {  // uniform across the wave
-      bad = 1;
-      piv = 1.0;
+    for (int q = 0; q < 4; ++q) {
+      const int j = j0 + q;
+#pragma unroll
+      for (int pp = 0; pp < q; ++pp) a[s][q] = fma(-a[s][pp], readlane_f64(a[s][pp], j), a[s][q]);
+      double piv = readlane_f64(a[s][q], j);
+      if (!(piv > 0.0) || !(piv < INFINITY)) {  // uniform across the wave
+        bad = 1;
+        piv = 1.0;
+      }
+      const double rs = rsqrt_refined(piv);
+      a[s][q] = (lane >= j) ? a[s][q] * rs : 0.0;
     }
-    const double rs = rsqrt_refined(piv);
-    a[j] = (i >= j) ? a[j] * rs : 0.0;
   };
+  auto publish = [&](int s, int p) {
+    double* pp = &d.pan[p & 3][lane][0];
+    *reinterpret_cast<double2*>(pp) = double2{a[s][0], a[s][1]};
+    *reinterpret_cast<double2*>(pp + 2) = double2{a[s][2], a[s][3]};
+  };
+  // a[s] -= (row of panel p) (columns of slot s in panel p)^T
+  auto apply = [&](int p, int s, const double2 (&mine)[2]) {
+    const int c0 = 4 * (4 * s + wave);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) pivot_step(0, q);
-#pragma unroll
-  for (int jp = 0; jp + 4 < kB; jp += 4) {
-    double(*pp)[4] = reinterpret_cast<double(*)[4]>(&d.pan[(jp >> 2) & 1][0][0] + z0);
-    *reinterpret_cast<double2*>(&pp[i][0]) = double2{a[jp], a[jp + 1]};
-    *reinterpret_cast<double2*>(&pp[i][2]) = double2{a[jp + 2], a[jp + 3]};
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the panel is in LDS
-    __builtin_amdgcn_wave_barrier();
-    // Rank-4 update in batches of 4 rows of the panel, double buffered: the
-    // next batch's 8 LDS reads are issued before the current batch's FMAs.
-    // Batch 0 covers the next panel's columns; the next panel's four pivot
-    // steps then run between the later batches, whose FMAs fill the pivot
-    // chain's latency.
-    double2 bu[2][4], bv[2][4];
-    auto load_batch = [&](int c0, int slot) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        bu[slot][t] = *reinterpret_cast<const double2*>(&pp[c0 + t][0]);
-        bv[slot][t] = *reinterpret_cast<const double2*>(&pp[c0 + t][2]);
-      }
-    };
-    const int nb = (kB - jp - 4) / 4;
-    load_batch(jp + 4, 0);
-#pragma unroll
-    for (int bt = 0; bt < nb; ++bt) {
-      const int c0 = jp + 4 + 4 * bt;
-      const int cur = bt & 1;
-      if (bt + 1 < nb) load_batch(c0 + 4, cur ^ 1);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int c = c0 + t;
-        double x0 = fma(-a[jp], bu[cur][t].x, a[c]);
-        x0 = fma(-a[jp + 1], bu[cur][t].y, x0);
-        x0 = fma(-a[jp + 2], bv[cur][t].x, x0);
-        a[c] = fma(-a[jp + 3], bv[cur][t].y, x0);
-      }
-      if (bt >= 1 && bt <= 4) pivot_step(jp + 4, bt - 1);
+    for (int t = 0; t < 4; ++t) {
+      const double* col = &d.pan[p & 3][c0 + t][0];
+      const double2 u = *reinterpret_cast<const double2*>(col);
+      const double2 v = *reinterpret_cast<const double2*>(col + 2);
+      double x = fma(-mine[0].x, u.x, a[s][t]);
+      x = fma(-mine[0].y, u.y, x);
+      x = fma(-mine[1].x, v.x, x);
+      a[s][t] = fma(-mine[1].y, v.y, x);
     }
-    const int done = (nb - 1 < 4) ? nb - 1 : 4;
-#pragma unroll
-    for (int q = done; q < 4; ++q) pivot_step(jp + 4, q);
+  };
+  auto row_of = [&](int p, double2 (&mine)[2]) {
+    const double* r = &d.pan[p & 3][lane][0];
+    mine[0] = *reinterpret_cast<const double2*>(r);
+    mine[1] = *reinterpret_cast<const double2*>(r + 2);
+  };
+  if (wave == 0) {
+    pivots(0);
+    publish(0, 0);
   }
-  // L back to LDS (row i, zeros above the diagonal), 1/l_ii
+  int deferred = -1;  // a panel still to be applied to this wave's later slots
 #pragma unroll
-  for (int c = 0; c < kB; ++c) d.L[i][c] = (c <= i) ? a[c] : 0.0;
-  d.rinv[i] = 1.0 / d.L[i][i];
+  for (int p = 0; p < 16; ++p) {
+    lds_barrier();
+    double2 mine[2];
+    if (deferred >= 0) {
+      row_of(deferred, mine);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (4 * s + wave > p) apply(deferred, s, mine);
+      deferred = -1;
+    }
+    row_of(p, mine);
+    if (p + 1 < 16 && ((p + 1) & 3) == wave) {
+      const int sn = (p + 1) >> 2;
+      apply(p, sn, mine);
+      pivots(sn);
+      publish(sn, p + 1);
+      deferred = p;
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (4 * s + wave > p) apply(p, s, mine);
+    }
+  }
+  // deferred is -1 here: panel 15's owner has no next panel
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) d.L[lane][4 * (4 * s + wave) + t] = a[s][t];
+  lds_barrier();
   return bad;
 }
 
@@ -419,73 +435,12 @@ __device__ __forceinline__ void zero_acc(f64x4 (&acc)[2][2]) {
 }
 
 // ---------------------------------------------------------------- panel step
-// Waves 1-3: one share of a column update, rows 16 (bi0 + i) and columns
-// 16 (bj0 + j) of the 64x64 tile at (r0, c0), in accumulator layout:
-//   c = -A[r0.., c0..] + sum_{kb <= q < kb + 16 nk} A[r0 + row][q] A[c0 + col][q],
-// that is minus the updated tile.  Operands come straight from memory (the
-// panels are fresh in L2): a lane loads 4 consecutive k of its fragment row
-// per chunk of 16, and MFMA sub-step u takes the u-th of them on both
-// operands, so each product pairs equal k.  Rows >= mv read as 0; nk is even.
-template <int NI, int NJ>
-__device__ __forceinline__ void colupd_share(const double* __restrict__ A, int n, int r0, int c0, int kb, int nk,
-                                             int mv, int bi0, int bj0, f64x4 (&c)[NI][NJ]) {
-  const int lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * (bi0 + i) + lk + 4 * r, col = 16 * (bj0 + j) + lr;
-        c[i][j][r] = (row < mv) ? -A[static_cast<int64_t>(r0 + row) * n + c0 + col] : 0.0;
-      }
-  if (nk <= 0) return;
-  const double* pa[NI];
-  bool va[NI];
-  const double* pb[NJ];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int row = 16 * (bi0 + i) + lr;
-    va[i] = row < mv;
-    pa[i] = A + static_cast<int64_t>(r0 + (va[i] ? row : 0)) * n + kb + 4 * lk;
-  }
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) pb[j] = A + static_cast<int64_t>(c0 + 16 * (bj0 + j) + lr) * n + kb + 4 * lk;
-  double fa[2][NI][4], fb[2][NJ][4];
-  auto load = [&](int sl, int kc) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) fa[sl][i][u] = va[i] ? pa[i][kc + u] : 0.0;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) fb[sl][j][u] = pb[j][kc + u];
-  };
-  auto mma = [&](int sl) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          c[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[sl][i][u], fb[sl][j][u], c[i][j], 0, 0, 0);
-  };
-  load(0, 0);
-  for (int q = 0; q < nk; q += 2) {
-    load(1, 16 * (q + 1));
-    mma(0);
-    if (q + 2 < nk) load(0, 16 * (q + 2));
-    mma(1);
-  }
-}
-
 // One launch per block column k of a panel group [k0, ke); work-group t
-// handles block row i = k + t.  Every work-group factors and inverts the
-// diagonal block A_kk itself (wave 0), so the panel solve needs no second
-// launch; work-group 0 writes inv(L_kk) into the diagonal block of Linv.
-// For t > 0, while wave 0 factors, waves 1-3 apply the group's earlier
-// panels to A_ik (left-looking),
+// handles block row i = k + t.  Every work-group factors the diagonal block
+// A_kk itself (all four waves) and inverts it (wave 0), so the panel solve
+// needs no second launch; work-group 0 writes inv(L_kk) into the diagonal
+// block of Linv.  For t > 0, while wave 0 inverts, waves 1-3 apply the
+// group's earlier panels to A_ik (left-looking),
 //   C = A_ik - sum_{k0 <= q < k} L_iq L_kq^T,
 // keeping C in registers until the inverse is done; then the four waves form
 // L_ik = C inv(L_kk)^T and store it, and a block row inside the group also
@@ -520,16 +475,75 @@ __global__ void __launch_bounds__(256) chol_step_kernel(double* __restrict__ A, 
     }
   }
   __syncthreads();
-  // minus C: waves 1-2 take block rows 2(w-1) .. +1 by block columns 0..2,
-  // wave 3 all block rows by block column 3.
-  f64x4 cw[2][3], c3[4][1];
-  // the quarter of A_ii that waves 1-3 update later: (0,0), (1,0), (1,1)
+  // Column update, waves 1-3 of work-groups t > 0: minus C in accumulator
+  // layout, waves 1-2 on block rows 2(w-1), 2(w-1)+1 by block columns 0..2,
+  // wave 3 on block rows 0..3 by block column 3; five fragment rows each
+  // (wave 1-2: two of A_i., three of A_k.; wave 3: four of A_i., one of A_k.).
+  // Operands come straight from memory: per chunk of 16 k a lane loads 4
+  // consecutive k of its fragment row, and MFMA sub-step u takes the u-th of
+  // them on both operands, so each product pairs equal k.  Loads run three
+  // chunks ahead in a ring of four; the first three and the tile's previous
+  // values are issued before the factorization, which hides them.
+  const bool cu = (t > 0) && (wave > 0);
+  const bool wide = wave < 3;
+  const int nk = 4 * (k - k0);  // chunks of 16 in K = 64 (k - k0), a multiple of 4
+  const double* fp[5];
+#pragma unroll
+  for (int e = 0; e < 5; ++e) {
+    const bool isa = wide ? (e < 2) : (e < 4);
+    const int row = wide ? (isa ? 16 * (2 * (wave - 1) + e) + lr : 16 * (e - 2) + lr) : (isa ? 16 * e + lr : 48 + lr);
+    fp[e] = A + static_cast<int64_t>(isa ? r0 + (row < mv ? row : 0) : c0 + row) * n + k0 * kB + 4 * lk;
+  }
+  double fr[4][5][4];
+  // A row of the block row beyond the matrix (row >= mv) reads row 0 of the
+  // block row instead: it only feeds the same row of C, L_ik and A_ii, none
+  // of which is stored.  The loads are unconditional, so nothing waits for
+  // them before the factorization.
+  auto load = [&](int sl, int q) {
+#pragma unroll
+    for (int e = 0; e < 5; ++e)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) fr[sl][e][u] = fp[e][16 * q + u];
+  };
+  auto mma = [&](int sl, f64x4 (&cc)[6]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (wide) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 3; ++j)
+            cc[3 * i + j] = __builtin_amdgcn_mfma_f64_16x16x4f64(fr[sl][i][u], fr[sl][2 + j][u], cc[3 * i + j], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          cc[i] = __builtin_amdgcn_mfma_f64_16x16x4f64(fr[sl][i][u], fr[sl][4][u], cc[i], 0, 0, 0);
+      }
+    }
+  };
+  // tile x of this wave's share -> (block row, block column)
+  auto tile_rc = [&](int x, int& rb, int& cb) {
+    rb = wide ? 2 * (wave - 1) + x / 3 : x;
+    cb = wide ? x % 3 : 3;
+  };
+  f64x4 cc[6];
+  // the quarter of A_ii that waves 1-3 update last: (0,0), (1,0), (1,1)
   const int qm = (wave >= 2) ? 1 : 0, qn = (wave == 3) ? 1 : 0;
-  f64x4 old[2][2];
-  if (wave == 0) {
-    const int bad = factor_block(d);
-    if (bad && t == 0 && lane == 0) atomicOr(info, 1);
-  } else if (t > 0) {
+  double old[2][2][4];  // raw; only entries inside the block are used
+  // previous values of the tile (loads in flight through the factorization;
+  // negated into cc only after it)
+  double craw[6][4];
+  if (cu) {
+#pragma unroll
+    for (int x = 0; x < 6; ++x) {
+      int rb, cb;
+      tile_rc(x, rb, cb);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * rb + lk + 4 * r, col = 16 * cb + lr;
+        craw[x][r] = (x < (wide ? 6 : 4)) ? A[static_cast<int64_t>(r0 + (row < mv ? row : 0)) * n + c0 + col] : 0.0;
+      }
+    }
     if (bi < ke) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -538,15 +552,37 @@ __global__ void __launch_bounds__(256) chol_step_kernel(double* __restrict__ A, 
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int row = qm * 32 + 16 * i + lk + 4 * r, col = qn * 32 + 16 * j + lr;
-            old[i][j][r] = (row < mv && col < mv) ? A[static_cast<int64_t>(r0 + row) * n + r0 + col] : 0.0;
+            const bool on = row < mv && col < mv;
+            old[i][j][r] = A[static_cast<int64_t>(r0 + (on ? row : 0)) * n + r0 + (on ? col : 0)];
           }
     }
-    const int nk = 4 * (k - k0);
-    if (wave < 3) colupd_share<2, 3>(A, n, r0, c0, k0 * kB, nk, mv, 2 * (wave - 1), 0, cw);
-    else colupd_share<4, 1>(A, n, r0, c0, k0 * kB, nk, mv, 0, 3, c3);
+    if (nk > 0) {
+      load(0, 0);
+      load(1, 1);
+      load(2, 2);
+    }
   }
-  __syncthreads();
-  if (wave == 0) invert_block(d);
+  const int bad = factor_block4(d);
+  if (bad && t == 0 && lane == 0) atomicOr(info, 1);
+  if (wave == 0) {
+    d.rinv[lane] = 1.0 / d.L[lane][lane];
+    invert_block(d);
+  } else if (cu) {
+#pragma unroll
+    for (int x = 0; x < 6; ++x)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cc[x][r] = -craw[x][r];
+    for (int q = 0; q < nk; q += 4) {
+      load(3, q + 3);
+      mma(0, cc);
+      if (q + 4 < nk) load(0, q + 4);
+      mma(1, cc);
+      if (q + 5 < nk) load(1, q + 5);
+      mma(2, cc);
+      if (q + 6 < nk) load(2, q + 6);
+      mma(3, cc);
+    }
+  }
   __syncthreads();
   if (t == 0) {
     double v[16];  // all LDS reads first, then the guarded stores
@@ -563,18 +599,16 @@ __global__ void __launch_bounds__(256) chol_step_kernel(double* __restrict__ A, 
     return;
   }
   // C into d.L, which the inverse no longer needs
-  if (wave == 1 || wave == 2) {
+  if (wave > 0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int x = 0; x < 6; ++x) {
+      if (x < (wide ? 6 : 4)) {
+        int rb, cb;
+        tile_rc(x, rb, cb);
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) d.L[16 * (2 * (wave - 1) + i) + lk + 4 * r][16 * j + lr] = -cw[i][j][r];
-  } else if (wave == 3) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) d.L[16 * i + lk + 4 * r][48 + lr] = -c3[i][0][r];
+        for (int r = 0; r < 4; ++r) d.L[16 * rb + lk + 4 * r][16 * cb + lr] = -cc[x][r];
+      }
+    }
   }
   __syncthreads();
   // L_ik = C inv(L_kk)^T.  inv(L_kk) is lower triangular, so result column
