@@ -68,25 +68,25 @@ static inline hipError_t zero_words(void* p, size_t words, hipStream_t s) {
   return hipGetLastError();
 }
 
-// One extra stream per device for work that overlaps the caller's stream,
-// created on first use and kept until the process ends.  Calls may share it;
-// each call orders its own work with its own events.
-static inline hipError_t side_stream(hipStream_t* out) {
+// Extra streams per device (which = 0, 1) for work that overlaps the
+// caller's stream, created on first use and kept until the process ends.
+// Calls may share them; each call orders its own work with its own events.
+static inline hipError_t side_stream(hipStream_t* out, int which = 0) {
   static std::mutex mu;
-  static hipStream_t streams[64] = {};
+  static hipStream_t streams[64][2] = {};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (dev < 0 || dev >= 64 || which < 0 || which > 1) return hipErrorInvalidValue;
   std::lock_guard<std::mutex> lock(mu);
-  if (!streams[dev]) {
-    e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+  if (!streams[dev][which]) {
+    e = hipStreamCreateWithFlags(&streams[dev][which], hipStreamNonBlocking);
     if (e != hipSuccess) {
-      streams[dev] = nullptr;
+      streams[dev][which] = nullptr;
       return e;
     }
   }
-  *out = streams[dev];
+  *out = streams[dev][which];
   return hipSuccess;
 }
 

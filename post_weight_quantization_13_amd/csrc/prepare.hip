@@ -738,6 +738,10 @@ constexpr int kT2 = 128;
 // 128x128 tiles pay off only with enough of them to keep every compute unit
 // busy with two; below that the 64x64 kernels run more tiles in parallel.
 constexpr int kBigTiles = 512;
+// LDS requested per work-group of the overlapped top level of the inverse
+constexpr int kTopLds = 96 * 1024;
+static_assert(kTopLds >= static_cast<int>(sizeof(TileSmem)) && kTopLds + static_cast<int>(sizeof(TileSmem)) > 160 * 1024,
+              "top-level LDS");
 template <int KC>
 struct BigSmemT {
   double a[2][kT2][KC + 1];
@@ -881,9 +885,9 @@ __global__ void __launch_bounds__(256, 2) chol_trail_kernel(double* __restrict__
 
 // One recursive-doubling level (see trtri_level_kernel) on 128x128 tiles, s >= 128.
 __global__ void __launch_bounds__(256, 2) trtri_big_kernel(double* __restrict__ L, double* __restrict__ Linv, int n,
-                                                        int s, int phase) {
+                                                        int s, int phase, int pair0) {
   __shared__ BigSmem sm;
-  const int b1 = blockIdx.x * 2 * s;
+  const int b1 = (pair0 + blockIdx.x) * 2 * s;
   const int b2 = b1 + s;
   if (b2 >= n) return;
   const int s2 = (n - b2 < s) ? n - b2 : s;
@@ -927,49 +931,51 @@ __global__ void __launch_bounds__(256, 2) trtri_big_kernel(double* __restrict__ 
   }
 }
 
-// One level of the recursive-doubling inverse.  Pair p joins blocks
-// [b1, b1+s) and [b2, b2+s2), b1 = 2ps, b2 = b1+s.  phase 0: T = L21 X11,
+// One level of the recursive-doubling inverse.  Pair p = pair0 + blockIdx.x
+// joins blocks [b1, b1+s) and [b2, b2+s2), b1 = 2ps, b2 = b1+s.  phase 0: T = L21 X11,
 // stored transposed at A[b1.., b2..] (strict upper triangle of A); phase 1:
 // X21 = -X22 T.  grid.x = pairs, grid.y = output tiles of the pair (s/64 x s/64).
 __global__ void __launch_bounds__(256) trtri_level_kernel(double* __restrict__ L, double* __restrict__ Linv,
-                                                          int n, int s, int phase) {
+                                                          int n, int s, int phase, int pair0) {
   __shared__ TileSmem sm;
-  const int b1 = blockIdx.x * 2 * s;
+  const int b1 = (pair0 + blockIdx.x) * 2 * s;
   const int b2 = b1 + s;
   if (b2 >= n) return;
   const int s2 = (n - b2 < s) ? n - b2 : s;
   // Tiles are dispatched longest K first: phase 0 sums over q >= cols0
   // (longest for the first tile column), phase 1 over q < rows0 + 64 (longest
-  // for the last tile row).
+  // for the last tile row).  Work-group y takes tiles y, y + gridDim.y, ...
   const int tcols = s / kB;
-  const int yq = blockIdx.y / tcols, yr = blockIdx.y % tcols;
-  const int tr = (phase == 0) ? yr : tcols - 1 - yq;
-  const int tc = (phase == 0) ? yq : yr;
-  const int rows0 = tr * kB, cols0 = tc * kB;  // within the s2 x s output
-  if (rows0 >= s2) return;
-  const int mv = (s2 - rows0 < kB) ? s2 - rows0 : kB;
-  const int nv = kB;
-  f64x4 acc[2][2];
-  zero_acc(acc);
-  if (phase == 0) {
-    // T[r][c] = sum_q L21[r][q] X11[q][c], X11 lower: q >= c.
-    const int kbeg = cols0;
-    tile_gemm_f64<false>(L + static_cast<int64_t>(b2 + rows0) * n + b1, n,
-                         Linv + static_cast<int64_t>(b1) * n + b1 + cols0, n, mv, nv, kbeg, s, acc, sm);
-    __syncthreads();
-    tile_foreach(acc, [&](int r, int c, double v) {
-      if (r < mv) L[static_cast<int64_t>(b1 + cols0 + c) * n + b2 + rows0 + r] = v;  // T^T, upper part of A
-    });
-  } else {
-    // X21[r][c] = -sum_q X22[r][q] T[q][c], X22 lower: q <= r.  T is stored
-    // transposed: T[q][c] = A[b1 + c][b2 + q]  ->  BT access with ldb = n.
-    const int kend = (rows0 + kB < s2) ? rows0 + kB : s2;
-    tile_gemm_f64<true>(Linv + static_cast<int64_t>(b2 + rows0) * n + b2, n,
-                        L + static_cast<int64_t>(b1 + cols0) * n + b2, n, mv, nv, 0, kend, acc, sm);
-    __syncthreads();
-    tile_foreach(acc, [&](int r, int c, double v) {
-      if (r < mv) Linv[static_cast<int64_t>(b2 + rows0 + r) * n + b1 + cols0 + c] = -v;
-    });
+  for (int y = blockIdx.y; y < tcols * tcols; y += gridDim.y) {
+    const int yq = y / tcols, yr = y % tcols;
+    const int tr = (phase == 0) ? yr : tcols - 1 - yq;
+    const int tc = (phase == 0) ? yq : yr;
+    const int rows0 = tr * kB, cols0 = tc * kB;  // within the s2 x s output
+    if (rows0 >= s2) continue;
+    const int mv = (s2 - rows0 < kB) ? s2 - rows0 : kB;
+    const int nv = kB;
+    f64x4 acc[2][2];
+    zero_acc(acc);
+    if (phase == 0) {
+      // T[r][c] = sum_q L21[r][q] X11[q][c], X11 lower: q >= c.
+      const int kbeg = cols0;
+      tile_gemm_f64<false>(L + static_cast<int64_t>(b2 + rows0) * n + b1, n,
+                           Linv + static_cast<int64_t>(b1) * n + b1 + cols0, n, mv, nv, kbeg, s, acc, sm);
+      __syncthreads();
+      tile_foreach(acc, [&](int r, int c, double v) {
+        if (r < mv) L[static_cast<int64_t>(b1 + cols0 + c) * n + b2 + rows0 + r] = v;  // T^T, upper part of A
+      });
+    } else {
+      // X21[r][c] = -sum_q X22[r][q] T[q][c], X22 lower: q <= r.  T is stored
+      // transposed: T[q][c] = A[b1 + c][b2 + q]  ->  BT access with ldb = n.
+      const int kend = (rows0 + kB < s2) ? rows0 + kB : s2;
+      tile_gemm_f64<true>(Linv + static_cast<int64_t>(b2 + rows0) * n + b2, n,
+                          L + static_cast<int64_t>(b1 + cols0) * n + b2, n, mv, nv, 0, kend, acc, sm);
+      __syncthreads();
+      tile_foreach(acc, [&](int r, int c, double v) {
+        if (r < mv) Linv[static_cast<int64_t>(b2 + rows0 + r) * n + b1 + cols0 + c] = -v;
+      });
+    }
   }
 }
 
@@ -1042,12 +1048,66 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
     if (e != hipSuccess) return e;
   }
   hipEvent_t ev_fork = ev.fork, ev_join = ev.join;
+  // Triangular inverse by recursive doubling over levels sz = 64, 128, ...,
+  // h, where h (the largest such size below n) is the top level: one pair,
+  // [0, h) and [h, n).  The levels inside [0, h) and the top level's first
+  // product T = L21 X11 need only block columns < h of L, so they run on a
+  // second side stream as soon as the step for block column h/64 - 1 is done,
+  // beside the rest of the factorization, which writes nothing they read.
+  // The first product runs on 3/8 of the compute units, each held whole, so
+  // the strips and steps keep the rest.  The levels inside [h, n) and the top
+  // level's second product follow the factorization on the caller's stream.
+  auto level = [&](int sz, int phase, int pair0, int npairs, hipStream_t st) -> hipError_t {
+    if (npairs <= 0) return hipSuccess;
+    if (sz < kT2 || npairs * (sz / kT2) * (sz / kT2) < kBigTiles) {
+      hipLaunchKernelGGL(trtri_level_kernel, dim3(npairs, (sz / kB) * (sz / kB)), dim3(256), 0, st, A, Linv, n, sz,
+                         phase, pair0);
+    } else {
+      hipLaunchKernelGGL(trtri_big_kernel, dim3(npairs, (sz / kT2) * (sz / kT2)), dim3(256), 0, st, A, Linv, n, sz,
+                         phase, pair0);
+    }
+    return hipGetLastError();
+  };
+  int h = 0;
+  for (int sz = kB; sz < n; sz *= 2) h = sz;
+  hipStream_t side2 = nullptr;
+  EventPair ev2;
+  int top_wgs = 0;
+  if (side && h >= 4 * kB) {
+    int dev = 0, cus = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = side_stream(&side2, 1);
+    if (e == hipSuccess) e = ev2.create();
+    if (e != hipSuccess) return e;
+    top_wgs = (cus * 3 / 8 > 1) ? cus * 3 / 8 : 1;
+  }
   bool pending = false;  // a side pass is in flight
   for (int k0 = 0; k0 < nblk; k0 += kGroup) {
     const int ke = (k0 + kGroup < nblk) ? k0 + kGroup : nblk;
     for (int k = k0; k < ke; ++k) {
       hipLaunchKernelGGL(chol_step_kernel, dim3(nblk - k), dim3(256), 0, s, A, Linv, n, k, k0, ke, info);
       GPTQ_CHECK_LAUNCH();
+      if (side2 && k == h / kB - 1) {  // block columns < h are final
+        e = hipEventRecord(ev2.fork, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(side2, ev2.fork, 0);
+        for (int sz = kB; e == hipSuccess && sz < h; sz *= 2) {
+          e = level(sz, 0, 0, h / (2 * sz), side2);
+          if (e == hipSuccess) e = level(sz, 1, 0, h / (2 * sz), side2);
+        }
+        // the top level's first product, on a few compute units held whole
+        // (enough LDS per work-group that no step, strip or trailing-pass
+        // work-group fits beside one), long before the factorization ends
+        if (e == hipSuccess) {
+          const int tiles = (h / kB) * (h / kB);
+          const int wgs = (top_wgs < tiles) ? top_wgs : tiles;
+          hipLaunchKernelGGL(trtri_level_kernel, dim3(1, wgs), dim3(256), kTopLds - sizeof(TileSmem), side2, A, Linv, n,
+                             h, 0, 0);
+          e = hipGetLastError();
+        }
+        if (e == hipSuccess) e = hipEventRecord(ev2.join, side2);
+        if (e != hipSuccess) return e;
+      }
     }
     if (ke >= nblk) break;
     const int ne = (ke + kGroup < nblk) ? ke + kGroup : nblk;
@@ -1091,20 +1151,22 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
     e = hipStreamWaitEvent(s, ev_join, 0);
     if (e != hipSuccess) return e;
   }
-  for (int sz = kB; sz < n; sz *= 2) {
-    const int pairs = (n + 2 * sz - 1) / (2 * sz);
-    if (sz < kT2 || pairs * (sz / kT2) * (sz / kT2) < kBigTiles) {
-      const int tiles = (sz / kB) * (sz / kB);
-      hipLaunchKernelGGL(trtri_level_kernel, dim3(pairs, tiles), dim3(256), 0, s, A, Linv, n, sz, 0);
-      GPTQ_CHECK_LAUNCH();
-      hipLaunchKernelGGL(trtri_level_kernel, dim3(pairs, tiles), dim3(256), 0, s, A, Linv, n, sz, 1);
-      GPTQ_CHECK_LAUNCH();
-    } else {
-      const int tiles = (sz / kT2) * (sz / kT2);
-      hipLaunchKernelGGL(trtri_big_kernel, dim3(pairs, tiles), dim3(256), 0, s, A, Linv, n, sz, 0);
-      GPTQ_CHECK_LAUNCH();
-      hipLaunchKernelGGL(trtri_big_kernel, dim3(pairs, tiles), dim3(256), 0, s, A, Linv, n, sz, 1);
-      GPTQ_CHECK_LAUNCH();
+  if (side2) {
+    for (int sz = kB; sz < h; sz *= 2) {
+      const int p0 = h / (2 * sz), np = (n - h + 2 * sz - 1) / (2 * sz);
+      e = level(sz, 0, p0, np, s);
+      if (e == hipSuccess) e = level(sz, 1, p0, np, s);
+      if (e != hipSuccess) return e;
+    }
+    e = hipStreamWaitEvent(s, ev2.join, 0);
+    if (e == hipSuccess) e = level(h, 1, 0, 1, s);
+    if (e != hipSuccess) return e;
+  } else {
+    for (int sz = kB; sz < n; sz *= 2) {
+      const int pairs = (n + 2 * sz - 1) / (2 * sz);
+      e = level(sz, 0, 0, pairs, s);
+      if (e == hipSuccess) e = level(sz, 1, 0, pairs, s);
+      if (e != hipSuccess) return e;
     }
   }
   hipLaunchKernelGGL(write_u_kernel, dim3((n + 255) / 256, gy), dim3(256), 0, s, Linv, n, U);
