@@ -234,8 +234,8 @@ __device__ __forceinline__ void pending_update(float (*Ws)[kRowsSweep], const ui
 //   wave 0   : the sequential chain -- quantize column j, e_j = (w - q) / U_jj,
 //              rank-1 update of the remaining columns of the sub-block (the
 //              16x16 block of U is read into registers first);
-//   waves 1-3: meanwhile apply the errors of sub-block s-1 to the columns past
-//              sub-block s+1 ("far" update);
+//   waves 1-3: meanwhile apply the errors of sub-block s-1 to the columns
+//              from sub-block s+1 on ("far" update, fp32 MFMA);
 //   barrier; all waves apply the errors of sub-block s to the columns of
 //   sub-block s+1 ("near" update, which the next chain step needs); barrier.
 // Codes: c = clamp(rint(w / s) + z).  Each sub-block's chain first runs with
@@ -407,32 +407,41 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
         }
       }
     } else if (sb >= 1) {
-      // far update: errors of sub-block sb-1 onto columns >= j0 + 16
+      // far update: errors of sub-block sb-1 onto columns >= j0 + 16, on the
+      // fp32 MFMA: Ws[c][r] -= sum_t E[r][t] U[jp + t][c] over 32x32 tiles
+      // (v_mfma_f32_32x32x2_f32: lane l supplies A[l%32][l/32] and
+      // B[l/32][l%32]; accumulator q of lane l is row 8(q/4) + 4(l/32) + q%4,
+      // column l%32).  Column tiles are aligned to 32; columns of the first
+      // tile below j0 + 16 (the chain's own sub-block) read U as 0 and are not
+      // written.  Tiles (row tile, column tile) are dealt to waves 1-3.
       const int jp = j0 - kSub;
-      float ep[kSub];
+      const int cfirst = j0 + kSub, ct0 = cfirst >> 5;
+      const int ntl = 2 * (kBlk / 32 - ct0);
+      const float(*Ep)[kRowsSweep] = Es[(sb - 1) & 1];
+      for (int x = wave - 1; x < ntl; x += 3) {
+        const int rt = x & 1, ct = ct0 + (x >> 1);
+        const int col = 32 * ct + (lane & 31);
+        const bool on = col >= cfirst;
+        // every LDS read of the tile first (operands and the old weights),
+        // then the MFMAs, then the writes
+        float a[kSub / 2], b[kSub / 2], w[16];
 #pragma unroll
-      for (int t = 0; t < kSub; ++t) ep[t] = Es[(sb - 1) & 1][t][lane];
-      // columns k = j0 + 16 + (wave-1) + 3m, four per pass with the loads first
-      for (int k = j0 + kSub + (wave - 1); k < kBlk; k += 12) {
-        float acc[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = (k + 3 * q < kBlk) ? Ws[k + 3 * q][lane] : 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int kq = (k + 3 * q < kBlk) ? k + 3 * q : k;
-          const f32x4* uc = reinterpret_cast<const f32x4*>(&UT[kq][jp]);
-#pragma unroll
-          for (int t4 = 0; t4 < kSub / 4; ++t4) {
-            const f32x4 u = uc[t4];
-            acc[q] = fmaf(-ep[4 * t4 + 0], u[0], acc[q]);
-            acc[q] = fmaf(-ep[4 * t4 + 1], u[1], acc[q]);
-            acc[q] = fmaf(-ep[4 * t4 + 2], u[2], acc[q]);
-            acc[q] = fmaf(-ep[4 * t4 + 3], u[3], acc[q]);
-          }
+        for (int ks = 0; ks < kSub / 2; ++ks) {
+          const int t = 2 * ks + (lane >> 5);
+          a[ks] = Ep[t][32 * rt + (lane & 31)];
+          b[ks] = on ? UT[col][jp + t] : 0.0f;
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (k + 3 * q < kBlk) Ws[k + 3 * q][lane] = acc[q];
+        for (int q = 0; q < 16; ++q) w[q] = Ws[col][32 * rt + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)];
+        f32x16 acc;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < kSub / 2; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ks], b[ks], acc, 0, 0, 0);
+        if (on) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) Ws[col][32 * rt + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)] = w[q] - acc[q];
+        }
       }
     }
     __syncthreads();
