@@ -20,6 +20,7 @@ Usage: python bench.py [--steps K] [--warmup W] [--workload attn4096]
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -120,6 +121,12 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="attn4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    # quantize-config overrides (default: the workload's own); e.g. the pages'
+    # "maximum precision" recipe: --group-size 32 --desc-act 1 --damp 0.005
+    ap.add_argument("--group-size", type=int, default=None, choices=[32, 64, 128, -1])
+    ap.add_argument("--sym", type=int, default=None, choices=[0, 1, 2])
+    ap.add_argument("--desc-act", type=int, default=None, choices=[0, 1])
+    ap.add_argument("--damp", type=float, default=None)
     ap.add_argument("--pmc-probe", action="store_true",
                     help="copy 1 GiB (counter calibration) then 3 Hessian launches; no timing output")
     args = ap.parse_args()
@@ -135,6 +142,11 @@ def main() -> int:
     import synth
 
     wl = synth.get(args.workload)
+    over = {k: v for k, v in (("group_size", args.group_size), ("sym", args.sym),
+                              ("desc_act", None if args.desc_act is None else bool(args.desc_act)),
+                              ("damp", args.damp)) if v is not None}
+    if over:
+        wl = dataclasses.replace(wl, **over)
     if len(wl.linears) != 1:
         print("bench.py times single-layer workloads", file=sys.stderr)
         return 2

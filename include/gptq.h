@@ -58,9 +58,13 @@ typedef enum { GPTQ_BF16 = 0, GPTQ_FP16 = 1, GPTQ_FP32 = 2 } gptq_dtype;
 /* The quantize config of the pages ("Configurações de quantização", "Paramètres clés"). */
 typedef struct {
   int32_t bits;          /* code width: 3 or 4                                              */
-  int32_t group_size;    /* weights per scale/zero group along a row: 128                    */
+  int32_t group_size;    /* weights per scale/zero group along a row: 128, 64, 32, or -1 for  */
+                         /* one group per row ("Paramètres clés", group_size)                */
   int32_t sym;           /* 0: asymmetric grid (zero point in [0, 2^bits-1]);               */
                          /* 1: symmetric grid, levels -(2^(b-1)-1)..2^(b-1)-1, zero exact    */
+                         /*    (the grid "Paramètres clés" describes);                       */
+                         /* 2: symmetric range [-a, a] over all 2^bits codes, zero point     */
+                         /*    2^(b-1) (a variant outside the pages' text)                   */
   int32_t desc_act;      /* 1: act-order, columns visited by decreasing diag(H)              */
   float damp_percent;    /* lambda = damp_percent * mean(diag H) is added to the diagonal    */
   int32_t block_size;    /* lazy-batch width in columns: 128                                 */
@@ -131,14 +135,18 @@ gptq_status gptq_prepare_hinv(const double* H, int64_t n, const gptq_config* cfg
  *            a little-endian bit stream, column i at bits [bits*i, bits*i+bits);
  *            qweight[k, r] is word k of that stream (4-bit: 8 codes per word;
  *            3-bit: 32 codes per 3 words).
- *   scales   fp16 bits [n/group_size, rows]: group g = sweep columns
- *            [g*gs, (g+1)*gs).
- *   zeros    fp16 bits [n/group_size, rows]: integer-valued zero points.
- *   g_idx    int32 [n]: g_idx[perm[j]] = j / group_size.
+ *   scales   fp16 bits [G, rows], G = n/group_size (1 for group_size -1):
+ *            group g = sweep columns [g*gs, (g+1)*gs).  A group's grid is
+ *            taken at its first column from the current (compensated) weights
+ *            of its columns; for group_size -1 from the whole row before the
+ *            sweep.
+ *   zeros    fp16 bits [G, rows]: integer-valued zero points.
+ *   g_idx    int32 [n]: g_idx[perm[j]] = j / group_size (0 for group_size -1).
  *   loss_out HOST double, may be NULL: sum over rows and columns of e^2 / 2 with
  *            e = (w - w_hat) / U[j, j] (equals tr(D H_d D^T) / 2, D = W - W_hat).
  * Dequantization: W_hat[r, i] = scales[g_idx[i], r] * (code[r, i] - zeros[g_idx[i], r]).
- * Supported: bits in {3, 4}; group_size == block_size == 128; n % 128 == 0.
+ * Supported: bits in {3, 4}; group_size in {32, 64, 128, -1}; block_size == 128;
+ * n % 128 == 0 (GPTQ_ERR_UNSUPPORTED otherwise).
  * rows == 0 is a no-op.  Synchronizes `stream` once when loss_out != NULL.
  * ------------------------------------------------------------------------- */
 size_t gptq_quantize_workspace_bytes(int64_t rows, int64_t n, const gptq_config* cfg);

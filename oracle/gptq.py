@@ -33,8 +33,8 @@ class QuantConfig:
     """The knobs of the pages' quantize config (skillmd "Configurações de quantização";
     polydesk "Paramètres clés de GPTQ"): bits, group_size, desc_act, damp_percent, sym."""
     bits: int = 4
-    group_size: int = 128
-    sym: bool = False
+    group_size: int = 128   # -1 (or 0): one group per row
+    sym: int = 0            # 0 asymmetric, 1 the pages' symmetric grid, 2 full-range symmetric
     desc_act: bool = False
     damp: float = 0.01
 
@@ -147,10 +147,14 @@ def grid_params(wg, bits, sym, qdtype=np.float64):
 
     Readings (the pages give no formulas): the range is [min(0, min w),
     max(0, max w)]; a group whose range is {0} uses [-1, 1].
-      asym: s = (xmax - xmin) / maxq,  z = rint(-xmin / s)          (z in [0, maxq])
-      sym:  s = max(-xmin, xmax) / (2^(b-1) - 1),  z = 2^(b-1)       (codes 1..maxq)
-    All arithmetic in ``qdtype``; rint is round-half-to-even.
-    Returns (s, z) arrays of length rows, dtype ``qdtype``.
+      sym = 0, asym: s = (xmax - xmin) / maxq,  z = rint(-xmin / s)   (z in [0, maxq])
+      sym = 1:  s = max(-xmin, xmax) / (2^(b-1) - 1),  z = 2^(b-1)    (codes 1..maxq)
+      sym = 2:  the symmetric range [-a, a], a = max(-xmin, xmax), spread
+                over all 2^b codes: s = (a - (-a)) / maxq,  z = 2^(b-1)  (codes 0..maxq)
+    sym = 1 is the grid the pages describe; sym = 2 is a reading outside
+    their text (a symmetric grid that keeps every code; zero is still exact
+    because z is an integer).  All arithmetic in ``qdtype``; rint is
+    round-half-to-even.  Returns (s, z) arrays of length rows, dtype ``qdtype``.
     """
     dt = np.dtype(qdtype).type
     wg = np.asarray(wg).astype(dt)
@@ -160,7 +164,11 @@ def grid_params(wg, bits, sym, qdtype=np.float64):
     degenerate = (xmin == 0) & (xmax == 0)
     xmin = np.where(degenerate, dt(-1), xmin).astype(dt)
     xmax = np.where(degenerate, dt(1), xmax).astype(dt)
-    if sym:
+    if int(sym) == 2:
+        a = np.maximum(-xmin, xmax)
+        s = ((a - (-a)) / dt((1 << bits) - 1)).astype(dt)
+        z = np.full_like(s, dt(1 << (bits - 1)))
+    elif sym:
         a = np.maximum(-xmin, xmax)
         s = (a / dt((1 << (bits - 1)) - 1)).astype(dt)
         z = np.full_like(s, dt(1 << (bits - 1)))
@@ -172,14 +180,15 @@ def grid_params(wg, bits, sym, qdtype=np.float64):
 
 def quantize_column(w, s, z, bits, sym, qdtype=np.float64):
     """Nearest grid point of each weight: c = clamp(rint(w / s) + z, lo, maxq),
-    w_hat = s * (c - z), with lo = 1 for the symmetric grid and 0 otherwise.
+    w_hat = s * (c - z), with lo = 1 for the pages' symmetric grid (sym = 1)
+    and 0 otherwise.
 
     [polydesk] "Étape 2": a column is quantized by rounding with a scale factor.
     Returns (codes int64, w_hat float64); the decision is taken in ``qdtype``.
     """
     dt = np.dtype(qdtype).type
     w = np.asarray(w).astype(dt)
-    lo = dt(1 if sym else 0)
+    lo = dt(1 if int(sym) == 1 else 0)
     hi = dt((1 << bits) - 1)
     c = np.clip(np.rint(w / s) + z, lo, hi).astype(dt)
     q = (s * (c - z)).astype(dt)

@@ -59,14 +59,14 @@ class gptq_config(ctypes.Structure):
 class Config:
     """The pages' quantize config: bits, group_size, sym, desc_act, damp_percent, block_size."""
     bits: int = 4
-    group_size: int = 128
-    sym: bool = False
+    group_size: int = 128       # 128, 64, 32, or -1 (one group per row)
+    sym: int = 0                # 0 asymmetric, 1 the pages' symmetric grid, 2 full-range symmetric
     desc_act: bool = False
     damp_percent: float = 0.01
     block_size: int = 128
 
     def c(self) -> gptq_config:
-        return gptq_config(int(self.bits), int(self.group_size), int(bool(self.sym)), int(bool(self.desc_act)),
+        return gptq_config(int(self.bits), int(self.group_size), int(self.sym), int(bool(self.desc_act)),
                            float(self.damp_percent), int(self.block_size))
 
 
@@ -254,8 +254,9 @@ def alloc_outputs(rows: int, n: int, cfg, device):
     import torch
     c = cfg if isinstance(cfg, Config) else Config(**cfg)
     qweight = torch.empty((n * c.bits // 32, rows), dtype=torch.int32, device=device)
-    scales = torch.empty((n // c.group_size, rows), dtype=torch.float16, device=device)
-    zeros = torch.empty((n // c.group_size, rows), dtype=torch.float16, device=device)
+    groups = n // c.group_size if c.group_size > 0 else 1
+    scales = torch.empty((groups, rows), dtype=torch.float16, device=device)
+    zeros = torch.empty((groups, rows), dtype=torch.float16, device=device)
     g_idx = torch.empty(n, dtype=torch.int32, device=device)
     return qweight, scales, zeros, g_idx
 

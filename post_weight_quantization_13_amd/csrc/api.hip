@@ -20,8 +20,9 @@ hipError_t launch_prepare(const double* H, int64_t n, double damp, int desc_act,
                           uint8_t* dead, void* ws, hipStream_t s, int* info_host);
 size_t quantize_workspace(int64_t rows, int64_t n);
 hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* dead, int64_t n, int bits, int sym,
-                           const void* W, int wdt, int64_t rows, int64_t ldw, int32_t* qweight, uint16_t* scales,
-                           uint16_t* zeros, int32_t* g_idx, double* loss_host, void* ws, hipStream_t s);
+                           int group_size, const void* W, int wdt, int64_t rows, int64_t ldw, int32_t* qweight,
+                           uint16_t* scales, uint16_t* zeros, int32_t* g_idx, double* loss_host, void* ws,
+                           hipStream_t s);
 size_t loss_workspace(int64_t rows, int64_t n);
 hipError_t launch_layer_loss(const double* H, int64_t n, const void* W, int wdt, int64_t rows, int64_t ldw,
                              const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
@@ -62,10 +63,10 @@ gptq_status check_config(const gptq_config* cfg, bool for_quantize) {
     return fail(GPTQ_ERR_INVALID_ARG, "damp_percent must be finite and >= 0 (got %g)", cfg->damp_percent);
   if (cfg->desc_act != 0 && cfg->desc_act != 1) return fail(GPTQ_ERR_INVALID_ARG, "desc_act must be 0 or 1");
   if (!for_quantize) return GPTQ_OK;
-  if (cfg->sym != 0 && cfg->sym != 1) return fail(GPTQ_ERR_INVALID_ARG, "sym must be 0 or 1");
+  if (cfg->sym < 0 || cfg->sym > 2) return fail(GPTQ_ERR_INVALID_ARG, "sym must be 0, 1 or 2");
   if (cfg->bits != 3 && cfg->bits != 4) return fail(GPTQ_ERR_UNSUPPORTED, "bits=%d (supported: 3, 4)", cfg->bits);
-  if (cfg->group_size != 128)
-    return fail(GPTQ_ERR_UNSUPPORTED, "group_size=%d (supported: 128)", cfg->group_size);
+  if (cfg->group_size != 32 && cfg->group_size != 64 && cfg->group_size != 128 && cfg->group_size != -1)
+    return fail(GPTQ_ERR_UNSUPPORTED, "group_size=%d (supported: 32, 64, 128, -1)", cfg->group_size);
   if (cfg->block_size != 128)
     return fail(GPTQ_ERR_UNSUPPORTED, "block_size=%d (supported: 128)", cfg->block_size);
   return GPTQ_OK;
@@ -151,8 +152,8 @@ gptq_status gptq_quantize_layer(const float* U, const int32_t* perm, const uint8
   gptq_status st = check_config(cfg, true);
   if (st != GPTQ_OK) return st;
   if (n < 1 || n > kMaxDim) return fail(GPTQ_ERR_INVALID_ARG, "n=%lld out of range", (long long)n);
-  if (n % cfg->group_size != 0)
-    return fail(GPTQ_ERR_UNSUPPORTED, "n=%lld is not a multiple of group_size=%d", (long long)n, cfg->group_size);
+  if (n % cfg->block_size != 0)
+    return fail(GPTQ_ERR_UNSUPPORTED, "n=%lld is not a multiple of block_size=%d", (long long)n, cfg->block_size);
   if (rows < 0 || rows > (int64_t)1 << 30) return fail(GPTQ_ERR_INVALID_ARG, "rows=%lld out of range", (long long)rows);
   if (!valid_dtype(wdt)) return fail(GPTQ_ERR_INVALID_ARG, "unknown dtype %d", (int)wdt);
   if (rows == 0) {
@@ -165,9 +166,9 @@ gptq_status gptq_quantize_layer(const float* U, const int32_t* perm, const uint8
   const size_t need = gptq::quantize_workspace(rows, n);
   if (!workspace || ws_bytes < need)
     return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace ? ws_bytes : 0, need);
-  hipError_t e = gptq::launch_quantize(U, perm, dead, n, cfg->bits, cfg->sym, W, static_cast<int>(wdt), rows, ldw,
-                                       qweight, scales, zeros, g_idx, loss_out, workspace,
-                                       static_cast<hipStream_t>(stream));
+  hipError_t e = gptq::launch_quantize(U, perm, dead, n, cfg->bits, cfg->sym, cfg->group_size, W,
+                                       static_cast<int>(wdt), rows, ldw, qweight, scales, zeros, g_idx, loss_out,
+                                       workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("gptq_quantize_layer", e);
   return ok();
 }
@@ -186,7 +187,7 @@ gptq_status gptq_layer_loss(const double* H, int64_t n, const void* W, gptq_dtyp
   if (st != GPTQ_OK) return st;
   if (!H || !W || !qweight || !scales || !zeros || !g_idx || !rel_loss)
     return fail(GPTQ_ERR_INVALID_ARG, "NULL pointer argument");
-  if (n < 1 || n > kMaxDim || n % cfg->group_size != 0)
+  if (n < 1 || n > kMaxDim || (cfg->group_size > 0 && n % cfg->group_size != 0))
     return fail(GPTQ_ERR_INVALID_ARG, "n=%lld invalid", (long long)n);
   if (rows < 1 || rows > (int64_t)1 << 30) return fail(GPTQ_ERR_INVALID_ARG, "rows=%lld invalid", (long long)rows);
   if (!valid_dtype(wdt)) return fail(GPTQ_ERR_INVALID_ARG, "unknown dtype %d", (int)wdt);

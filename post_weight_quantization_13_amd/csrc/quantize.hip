@@ -224,6 +224,69 @@ __device__ __forceinline__ void pending_update(float (*Ws)[kRowsSweep], const ui
       Ws[32 * wave + (lane & 31)][32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)] -= acc[i][q];
 }
 
+// ---------------------------------------------------------------- quantization grid
+// Scale and zero point of a group whose values span [xmin, xmax] with
+// xmin <= 0 <= xmax (the range always includes 0); a range of {0} takes
+// [-1, 1].  polydesk.ai "GPTQ" glossary, "Paramètres clés" (sym): the
+// asymmetric grid has a non-zero zero point; the symmetric grid spans
+// -(2^(b-1)-1) .. 2^(b-1)-1 steps with zero exact (SYM = 1).  SYM = 2 spreads
+// the symmetric range [-a, a] over all 2^b codes (zero still exact, the zero
+// point being the integer 2^(b-1)).
+//   SYM 0: s = (xmax - xmin) / maxq,           z = rint(-xmin / s)
+//   SYM 1: s = max(-xmin, xmax) / (2^(b-1)-1), z = 2^(b-1)
+//   SYM 2: s = (a - (-a)) / maxq,              z = 2^(b-1),  a = max(-xmin, xmax)
+template <int BITS, int SYM>
+__device__ __forceinline__ void grid_from_range(float xmin, float xmax, float& s, float& z) {
+  constexpr float maxq = static_cast<float>((1 << BITS) - 1);
+  if (xmin == 0.0f && xmax == 0.0f) {
+    xmin = -1.0f;
+    xmax = 1.0f;
+  }
+  if constexpr (SYM == 1) {
+    const float a = fmaxf(-xmin, xmax);
+    s = a / static_cast<float>((1 << (BITS - 1)) - 1);
+    z = static_cast<float>(1 << (BITS - 1));
+  } else if constexpr (SYM == 2) {
+    const float a = fmaxf(-xmin, xmax);
+    s = (a - (-a)) / maxq;
+    z = static_cast<float>(1 << (BITS - 1));
+  } else {
+    s = (xmax - xmin) / maxq;
+    z = rintf(-xmin / s);
+  }
+}
+
+// One group per row (group_size -1): the grid of each row from all n of its
+// columns as gathered, before any of them is updated.  grid.x = rows.
+template <int BITS, int SYM>
+__global__ void __launch_bounds__(256) row_params_kernel(const float* __restrict__ Wk, int n, int rows,
+                                                          float* __restrict__ rowsz) {
+  __shared__ float smin[256], smax[256];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  float xmin = 0.0f, xmax = 0.0f;
+  for (int k = tid; k < n; k += 256) {
+    const float v = Wk[static_cast<int64_t>(r) * n + k];
+    xmin = fminf(xmin, v);
+    xmax = fmaxf(xmax, v);
+  }
+  smin[tid] = xmin;
+  smax[tid] = xmax;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) {
+      smin[tid] = fminf(smin[tid], smin[tid + w]);
+      smax[tid] = fmaxf(smax[tid], smax[tid + w]);
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    float sv, zv;
+    grid_from_range<BITS, SYM>(smin[0], smax[0], sv, zv);
+    rowsz[2 * r] = sv;
+    rowsz[2 * r + 1] = zv;
+  }
+}
+
 // ---------------------------------------------------------------- sweep
 // One workgroup (4 waves) per strip of 64 rows and one block of 128 columns;
 // lane = row in every wave.  LDS: UT[k][j] = U[i1+j][i1+k] (the block of U,
@@ -246,12 +309,13 @@ __device__ __forceinline__ void pending_update(float (*Ws)[kRowsSweep], const ui
 // correctly rounded w / s.  The fast path has no branch inside the chain.
 constexpr int kSubs = kBlk / kSub;  // 8
 
-template <int BITS, bool SYM>
+template <int BITS, int SYM>
 __global__ void __launch_bounds__(256) sweep_block_kernel(
     const float* __restrict__ Wk, const float* __restrict__ U, const uint16_t* __restrict__ UTh,
     const uint16_t* __restrict__ UTl, int n, int rows, int i1, uint8_t* __restrict__ codes,
     uint16_t* __restrict__ Eh, uint16_t* __restrict__ El, int ldE, PendSeg sa, PendSeg sb,
-    uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, double* __restrict__ rowloss) {
+    uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, double* __restrict__ rowloss, int gs,
+    const float* __restrict__ rowsz) {
   __shared__ __attribute__((aligned(16))) float UT[kBlk][kBlk + 4];
   __shared__ float Ws[kBlk][kRowsSweep];
   __shared__ __attribute__((aligned(16))) PendSmem psm;
@@ -302,37 +366,96 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
   __syncthreads();
 
   constexpr float maxq = static_cast<float>((1 << BITS) - 1);
-  const float lo = SYM ? 1.0f : 0.0f;
+  const float lo = (SYM == 1) ? 1.0f : 0.0f;
   float sv = 1.0f, zv = 0.0f, rs = 1.0f;
   double loss = 0.0;
-  if (wave == 0) {
-    // group parameters from the block-entry values (group = block)
+  // Wave 0: scale and zero point of the group of columns c0 .. c0 + cnt - 1
+  // of the block, from their current (compensated) values, written out as
+  // group (i1 + c0) / gs.  The range includes 0; a group whose range is {0}
+  // takes [-1, 1].
+  auto group_params = [&](int c0, int cnt) {
     float xmin = 0.0f, xmax = 0.0f;
-    for (int k = 0; k < kBlk; ++k) {
+    for (int k = c0; k < c0 + cnt; ++k) {
       const float v = Ws[k][lane];
       xmin = fminf(xmin, v);
       xmax = fmaxf(xmax, v);
     }
-    if (xmin == 0.0f && xmax == 0.0f) {
-      xmin = -1.0f;
-      xmax = 1.0f;
-    }
-    if constexpr (SYM) {
-      const float a = fmaxf(-xmin, xmax);
-      sv = a / static_cast<float>((1 << (BITS - 1)) - 1);
-      zv = static_cast<float>(1 << (BITS - 1));
-    } else {
-      sv = (xmax - xmin) / maxq;
-      zv = rintf(-xmin / sv);
-    }
+    grid_from_range<BITS, SYM>(xmin, xmax, sv, zv);
     rs = 1.0f / sv;
+    if (valid) {
+      const int g = (i1 + c0) / gs;
+      scales[static_cast<int64_t>(g) * rows + r] = float_to_half_bits(sv);
+      zeros[static_cast<int64_t>(g) * rows + r] = float_to_half_bits(zv);
+    }
+  };
+  if (wave == 0) {
+    if (gs > 0) {
+      group_params(0, gs < kBlk ? gs : kBlk);
+    } else {  // one group per row, its parameters taken before the sweep
+      sv = valid ? rowsz[2 * r] : 1.0f;
+      zv = valid ? rowsz[2 * r + 1] : 0.0f;
+      rs = 1.0f / sv;
+      if (valid && i1 == 0) {
+        scales[r] = float_to_half_bits(sv);
+        zeros[r] = float_to_half_bits(zv);
+      }
+    }
   }
+  // groups narrower than a block start at sub-blocks sb % (gs / 16) == 0
+  const int gsub = (gs > 0 && gs < kBlk) ? gs / kSub : kSubs;
 
   uint16_t* ehrow = Eh + static_cast<int64_t>(valid ? r : 0) * ldE;
   uint16_t* elrow = El + static_cast<int64_t>(valid ? r : 0) * ldE;
   uint8_t* crow = codes + static_cast<int64_t>(valid ? r : 0) * n + i1;
+  // Waves 1-3: errors of sub-block sb-1 onto the columns from sub-block sb+1 on.
+  auto far_update = [&](int sb) {
+    const int j0 = sb * kSub;
+    // fp32 MFMA: Ws[c][r] -= sum_t E[r][t] U[jp + t][c] over 32x32 tiles
+    // (v_mfma_f32_32x32x2_f32: lane l supplies A[l%32][l/32] and
+    // B[l/32][l%32]; accumulator q of lane l is row 8(q/4) + 4(l/32) + q%4,
+    // column l%32).  Column tiles are aligned to 32; columns of the first
+    // tile below j0 + 16 (the chain's own sub-block) read U as 0 and are not
+    // written.  Tiles (row tile, column tile) are dealt to waves 1-3.
+    const int jp = j0 - kSub;
+    const int cfirst = j0 + kSub, ct0 = cfirst >> 5;
+    const int ntl = 2 * (kBlk / 32 - ct0);
+    const float(*Ep)[kRowsSweep] = Es[(sb - 1) & 1];
+    for (int x = wave - 1; x < ntl; x += 3) {
+      const int rt = x & 1, ct = ct0 + (x >> 1);
+      const int col = 32 * ct + (lane & 31);
+      const bool on = col >= cfirst;
+      // every LDS read of the tile first (operands and the old weights),
+      // then the MFMAs, then the writes
+      float a[kSub / 2], b[kSub / 2], w[16];
+#pragma unroll
+      for (int ks = 0; ks < kSub / 2; ++ks) {
+        const int t = 2 * ks + (lane >> 5);
+        a[ks] = Ep[t][32 * rt + (lane & 31)];
+        b[ks] = on ? UT[col][jp + t] : 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) w[q] = Ws[col][32 * rt + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)];
+      f32x16 acc;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < kSub / 2; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ks], b[ks], acc, 0, 0, 0);
+      if (on) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) Ws[col][32 * rt + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)] = w[q] - acc[q];
+      }
+    }
+  };
   for (int sb = 0; sb < kSubs; ++sb) {
     const int j0 = sb * kSub;
+    // A group starting inside the block: the errors of sub-block sb-1 reach
+    // all of its columns first, then its parameters are taken.
+    const bool gstart = sb > 0 && sb % gsub == 0;
+    if (gstart) {
+      if (wave > 0) far_update(sb);
+      __syncthreads();
+      if (wave == 0) group_params(j0, gs);
+    }
     if (wave == 0) {
       float w0[kSub];
 #pragma unroll
@@ -406,43 +529,8 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
           *reinterpret_cast<uint2*>(elrow + j0 + 4 * t4) = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
         }
       }
-    } else if (sb >= 1) {
-      // far update: errors of sub-block sb-1 onto columns >= j0 + 16, on the
-      // fp32 MFMA: Ws[c][r] -= sum_t E[r][t] U[jp + t][c] over 32x32 tiles
-      // (v_mfma_f32_32x32x2_f32: lane l supplies A[l%32][l/32] and
-      // B[l/32][l%32]; accumulator q of lane l is row 8(q/4) + 4(l/32) + q%4,
-      // column l%32).  Column tiles are aligned to 32; columns of the first
-      // tile below j0 + 16 (the chain's own sub-block) read U as 0 and are not
-      // written.  Tiles (row tile, column tile) are dealt to waves 1-3.
-      const int jp = j0 - kSub;
-      const int cfirst = j0 + kSub, ct0 = cfirst >> 5;
-      const int ntl = 2 * (kBlk / 32 - ct0);
-      const float(*Ep)[kRowsSweep] = Es[(sb - 1) & 1];
-      for (int x = wave - 1; x < ntl; x += 3) {
-        const int rt = x & 1, ct = ct0 + (x >> 1);
-        const int col = 32 * ct + (lane & 31);
-        const bool on = col >= cfirst;
-        // every LDS read of the tile first (operands and the old weights),
-        // then the MFMAs, then the writes
-        float a[kSub / 2], b[kSub / 2], w[16];
-#pragma unroll
-        for (int ks = 0; ks < kSub / 2; ++ks) {
-          const int t = 2 * ks + (lane >> 5);
-          a[ks] = Ep[t][32 * rt + (lane & 31)];
-          b[ks] = on ? UT[col][jp + t] : 0.0f;
-        }
-#pragma unroll
-        for (int q = 0; q < 16; ++q) w[q] = Ws[col][32 * rt + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)];
-        f32x16 acc;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < kSub / 2; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[ks], b[ks], acc, 0, 0, 0);
-        if (on) {
-#pragma unroll
-          for (int q = 0; q < 16; ++q) Ws[col][32 * rt + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)] = w[q] - acc[q];
-        }
-      }
+    } else if (sb >= 1 && !gstart) {
+      far_update(sb);
     }
     __syncthreads();
     if (sb + 1 < kSubs) {
@@ -471,12 +559,7 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
       __syncthreads();
     }
   }
-  if (wave == 0 && valid) {
-    const int g = i1 / kBlk;
-    scales[static_cast<int64_t>(g) * rows + r] = float_to_half_bits(sv);
-    zeros[static_cast<int64_t>(g) * rows + r] = float_to_half_bits(zv);
-    rowloss[r] += 0.5 * loss;
-  }
+  if (wave == 0 && valid) rowloss[r] += 0.5 * loss;
 }
 
 // ---------------------------------------------------------------- trailing update
@@ -647,21 +730,28 @@ size_t quantize_workspace(int64_t rows, int64_t n) {
          + al256(static_cast<size_t>(rows) * n)             // codes
          + al256(static_cast<size_t>(rows) * 8)             // rowloss
          + al256(static_cast<size_t>(n) * 4)                // invperm
+         + al256(static_cast<size_t>(rows) * 8)             // per-row scale, zero (group_size -1)
          + 256;                                             // loss scalar
 }
 
-template <int BITS, bool SYM>
+template <int BITS, int SYM>
 static void launch_sweep(dim3 g, hipStream_t s, const float* Wk, const float* U, const uint16_t* UTh,
                          const uint16_t* UTl, int n, int rows, int i1, uint8_t* codes, uint16_t* Eh, uint16_t* El,
-                         const PendSeg& sa, const PendSeg& sb, uint16_t* scales, uint16_t* zeros, double* rowloss) {
+                         const PendSeg& sa, const PendSeg& sb, uint16_t* scales, uint16_t* zeros, double* rowloss,
+                         int gs, const float* rowsz) {
   hipLaunchKernelGGL((sweep_block_kernel<BITS, SYM>), g, dim3(256), 0, s, Wk, U, UTh, UTl, n, rows, i1, codes, Eh, El,
-                     kSuper, sa, sb, scales, zeros, rowloss);
+                     kSuper, sa, sb, scales, zeros, rowloss, gs, rowsz);
+}
+
+template <int BITS, int SYM>
+static void launch_row_params(hipStream_t s, const float* Wk, int n, int rows, float* rowsz) {
+  hipLaunchKernelGGL((row_params_kernel<BITS, SYM>), dim3(rows), dim3(256), 0, s, Wk, n, rows, rowsz);
 }
 
 hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* dead, int64_t n64, int bits,
-                           int sym, const void* W, int wdt, int64_t rows64, int64_t ldw, int32_t* qweight,
-                           uint16_t* scales, uint16_t* zeros, int32_t* g_idx, double* loss_host, void* ws,
-                           hipStream_t s) {
+                           int sym, int group_size, const void* W, int wdt, int64_t rows64, int64_t ldw,
+                           int32_t* qweight, uint16_t* scales, uint16_t* zeros, int32_t* g_idx, double* loss_host,
+                           void* ws, hipStream_t s) {
   const int n = static_cast<int>(n64), rows = static_cast<int>(rows64);
   uint8_t* p = static_cast<uint8_t*>(ws);
   float* Wk = reinterpret_cast<float*>(p);
@@ -681,7 +771,11 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
   p += al256(static_cast<size_t>(rows) * 8);
   int32_t* invperm = reinterpret_cast<int32_t*>(p);
   p += al256(static_cast<size_t>(n) * 4);
+  float* rowsz = reinterpret_cast<float*>(p);
+  p += al256(static_cast<size_t>(rows) * 8);
   double* loss_dev = reinterpret_cast<double*>(p);
+  // group width in the sweep: 32, 64 or 128 columns; 0 = one group per row
+  const int gs = (group_size > 0) ? group_size : 0;
 
   hipError_t e;
 #define GPTQ_CHECK_LAUNCH()        \
@@ -696,8 +790,17 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
   else if (wdt == DT_FP16) hipLaunchKernelGGL(gather_w_kernel<DT_FP16>, gg, dim3(256), 0, s, W, ldw, perm, dead, rows, n, Wk);
   else hipLaunchKernelGGL(gather_w_kernel<DT_FP32>, gg, dim3(256), 0, s, W, ldw, perm, dead, rows, n, Wk);
   GPTQ_CHECK_LAUNCH();
-  hipLaunchKernelGGL(gidx_kernel, dim3((n + 255) / 256), dim3(256), 0, s, perm, n, kBlk, g_idx, invperm);
+  hipLaunchKernelGGL(gidx_kernel, dim3((n + 255) / 256), dim3(256), 0, s, perm, n, gs > 0 ? gs : n, g_idx, invperm);
   GPTQ_CHECK_LAUNCH();
+  if (gs == 0) {
+    if (bits == 4 && sym == 0) launch_row_params<4, 0>(s, Wk, n, rows, rowsz);
+    else if (bits == 4 && sym == 1) launch_row_params<4, 1>(s, Wk, n, rows, rowsz);
+    else if (bits == 4) launch_row_params<4, 2>(s, Wk, n, rows, rowsz);
+    else if (sym == 0) launch_row_params<3, 0>(s, Wk, n, rows, rowsz);
+    else if (sym == 1) launch_row_params<3, 1>(s, Wk, n, rows, rowsz);
+    else launch_row_params<3, 2>(s, Wk, n, rows, rowsz);
+    GPTQ_CHECK_LAUNCH();
+  }
   hipLaunchKernelGGL(split_ut_kernel, dim3(n / 64, n / 64), dim3(256), 0, s, U, n, UTh, UTl);
   GPTQ_CHECK_LAUNCH();
 
@@ -708,7 +811,7 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
   // wide update (K = kSuper) on a second stream, overlapping the sweeps of
   // super-block j+1.  Super-block j+2 waits for that update before it starts.
   // E holds the errors of two super-blocks (alternating), [rows, kSuper] each.
-  const dim3 gs((rows + kRowsSweep - 1) / kRowsSweep);
+  const dim3 grid((rows + kRowsSweep - 1) / kRowsSweep);
   const int rt = (rows + 127) / 128;
   const int nsb = (n + kSuper - 1) / kSuper;
   hipStream_t side = nullptr;
@@ -745,14 +848,15 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
       const PendSeg sb{Ejh, Ejl, i1 - s1, s1};
       uint16_t* Ebh = Ejh + (i1 - s1);
       uint16_t* Ebl = Ejl + (i1 - s1);
-      if (bits == 4 && !sym)
-        launch_sweep<4, false>(gs, s, Wk, U, UTh, UTl, n, rows, i1, codes, Ebh, Ebl, sa, sb, scales, zeros, rowloss);
-      else if (bits == 4 && sym)
-        launch_sweep<4, true>(gs, s, Wk, U, UTh, UTl, n, rows, i1, codes, Ebh, Ebl, sa, sb, scales, zeros, rowloss);
-      else if (bits == 3 && !sym)
-        launch_sweep<3, false>(gs, s, Wk, U, UTh, UTl, n, rows, i1, codes, Ebh, Ebl, sa, sb, scales, zeros, rowloss);
-      else
-        launch_sweep<3, true>(gs, s, Wk, U, UTh, UTl, n, rows, i1, codes, Ebh, Ebl, sa, sb, scales, zeros, rowloss);
+#define GPTQ_SWEEP(B, S) \
+  launch_sweep<B, S>(grid, s, Wk, U, UTh, UTl, n, rows, i1, codes, Ebh, Ebl, sa, sb, scales, zeros, rowloss, gs, rowsz)
+      if (bits == 4 && sym == 0) GPTQ_SWEEP(4, 0);
+      else if (bits == 4 && sym == 1) GPTQ_SWEEP(4, 1);
+      else if (bits == 4) GPTQ_SWEEP(4, 2);
+      else if (sym == 0) GPTQ_SWEEP(3, 0);
+      else if (sym == 1) GPTQ_SWEEP(3, 1);
+      else GPTQ_SWEEP(3, 2);
+#undef GPTQ_SWEEP
       GPTQ_CHECK_LAUNCH();
     }
     const int wide = s2 + kSuper;  // first column of super-block j+2

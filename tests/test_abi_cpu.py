@@ -79,7 +79,12 @@ def test_argument_validation(g):
         FAKE, FAKE, FAKE, n, cfg or _cfg(), FAKE, wdt, rows, ldw, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, None)
     assert L.gptq_quantize_layer(*args(cfg=_cfg(bits=5))) == g.GPTQ_ERR_UNSUPPORTED
     assert L.gptq_quantize_layer(*args(cfg=_cfg(bits=8))) == g.GPTQ_ERR_UNSUPPORTED
-    assert L.gptq_quantize_layer(*args(cfg=_cfg(group_size=64))) == g.GPTQ_ERR_UNSUPPORTED
+    assert L.gptq_quantize_layer(*args(cfg=_cfg(group_size=16))) == g.GPTQ_ERR_UNSUPPORTED
+    assert L.gptq_quantize_layer(*args(cfg=_cfg(group_size=256))) == g.GPTQ_ERR_UNSUPPORTED
+    assert L.gptq_quantize_layer(*args(cfg=_cfg(group_size=0))) == g.GPTQ_ERR_UNSUPPORTED
+    assert L.gptq_quantize_layer(*args(cfg=_cfg(sym=3))) == g.GPTQ_ERR_INVALID_ARG
+    # group_size 32 or 64 still needs n to be a multiple of the 128-column block
+    assert L.gptq_quantize_layer(*args(n=192, ldw=192, cfg=_cfg(group_size=64))) == g.GPTQ_ERR_UNSUPPORTED
     assert L.gptq_quantize_layer(*args(cfg=_cfg(block_size=64))) == g.GPTQ_ERR_UNSUPPORTED
     assert L.gptq_quantize_layer(*args(n=200, ldw=200)) == g.GPTQ_ERR_UNSUPPORTED
     assert L.gptq_quantize_layer(*args(ldw=128)) == g.GPTQ_ERR_INVALID_ARG

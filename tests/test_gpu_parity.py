@@ -127,24 +127,26 @@ def test_prepare_not_positive_definite(g):
 
 
 # --------------------------------------------------------------------------- quantize
-@pytest.mark.parametrize("bits,sym", [(4, False), (3, False), (4, True), (3, True)])
-def test_identity_hessian_is_rtn_bit_exact(g, bits, sym):
+@pytest.mark.parametrize("bits,sym,gs", [(4, 0, 128), (3, 0, 128), (4, 1, 128), (3, 1, 128), (4, 2, 128),
+                                         (3, 2, 128), (4, 0, 32), (3, 1, 64), (4, 2, 32), (4, 0, -1), (3, 2, -1)])
+def test_identity_hessian_is_rtn_bit_exact(g, bits, sym, gs):
     import torch
     rows, n = 200, 384
-    rng = np.random.default_rng(bits + 10 * sym)
+    rng = np.random.default_rng(bits + 10 * sym + gs)
     W = synth.bf16_round((rng.standard_normal((rows, n)) * 0.02).astype(np.float32))
-    W[5, :128] = 0.0                                   # a degenerate group
+    W[5, :128] = 0.0                                   # a degenerate group (for gs <= 128)
+    W[6, :] = 0.0                                      # a degenerate row
     wd = to_device(synth.bf16_bits(W), "bf16")
-    cfg = g.Config(bits=bits, sym=sym, desc_act=True)
+    cfg = g.Config(bits=bits, sym=sym, group_size=gs, desc_act=True)
     U, perm, dead = g.prepare(torch.eye(n, dtype=torch.float64, device="cuda"), cfg)
     out = g.quantize_layer(U, perm, dead, cfg, wd)
-    ocfg = oracle.QuantConfig(bits=bits, group_size=128, sym=sym)
+    ocfg = oracle.QuantConfig(bits=bits, group_size=gs, sym=sym)
     r = oracle.rtn(W.astype(np.float64), ocfg, qdtype=np.float32)
     codes = oracle.unpack(out["qweight"].cpu().numpy(), bits, n)
     assert np.array_equal(codes, r["codes"])
     assert np.array_equal(out["scales"].cpu().numpy(), oracle.to_fp16(r["S"]))
     assert np.array_equal(out["zeros"].cpu().numpy(), oracle.to_fp16(r["Z"]))
-    assert np.array_equal(out["g_idx"].cpu().numpy(), np.arange(n) // 128)
+    assert np.array_equal(out["g_idx"].cpu().numpy(), np.arange(n) // gs if gs > 0 else np.zeros(n, np.int32))
 
 
 CASES = [
@@ -184,6 +186,49 @@ def test_layer_end_to_end(g, name, size):
     assert abs(out["loss"] - ref["L"]) <= 0.01 * ref["L"]
     rtn = oracle.rtn(wv.astype(np.float64), _ocfg(wl))
     assert rel < oracle.rel_loss(wv, rtn["What"], Href)
+
+
+# Group sizes and grids beyond 128 / the pages' sym grid, on the same layers:
+# skillmd "Configurações de quantização" ("Máxima precisão": 4-bit, groups of
+# 32, act-order, damp 0.005) and polydesk "Paramètres clés" (group_size 64, 32
+# and -1 for one group per row).  Groups of 32 and 64 start inside a 128-column
+# block, where the kernel takes their grid after the errors of the previous
+# sub-block have reached all of the group's columns.
+VARIANTS = [
+    ("attn4096", dict(rows=200, n=512, tokens=4096), dict(bits=4, group_size=32, sym=0, desc_act=True, damp=0.005)),
+    ("attn4096", dict(rows=200, n=1536, tokens=4096), dict(bits=4, group_size=64, sym=0, desc_act=False, damp=0.01)),
+    ("mlpdown11008", dict(rows=136, n=640, tokens=4096), dict(bits=3, group_size=32, sym=1, desc_act=True, damp=0.01)),
+    ("attn4096", dict(rows=200, n=512, tokens=4096), dict(bits=4, group_size=-1, sym=0, desc_act=True, damp=0.01)),
+    ("down28672", dict(rows=72, n=768, tokens=8192), dict(bits=4, group_size=128, sym=2, desc_act=True, damp=0.01)),
+    ("attn4096", dict(rows=200, n=512, tokens=4096), dict(bits=3, group_size=64, sym=2, desc_act=False, damp=0.005)),
+]
+
+
+@pytest.mark.parametrize("name,size,qc", VARIANTS)
+def test_layer_group_and_grid_variants(g, name, size, qc):
+    import torch
+    wl = synth.get(name).resized(**size)
+    wv, wd, xv, xd = layer_inputs(wl)
+    cfg = g.Config(bits=qc["bits"], group_size=qc["group_size"], sym=qc["sym"], desc_act=qc["desc_act"],
+                   damp_percent=qc["damp"])
+    H = torch.empty((wl.n, wl.n), dtype=torch.float64, device="cuda")
+    g.gptq_hessian_accumulate(H, 0, xd)
+    U, perm, dead = g.prepare(H, cfg)
+    out = g.quantize_layer(U, perm, dead, cfg, wd)
+    rel = g.layer_loss(H, wd, out, cfg)
+    Href, _ = oracle.hessian(xv)
+    ocfg = oracle.QuantConfig(bits=qc["bits"], group_size=qc["group_size"], sym=qc["sym"],
+                              desc_act=qc["desc_act"], damp=qc["damp"])
+    ref = oracle.gptq_layer(wv.astype(np.float64), Href, ocfg, qdtype=np.float32, block=128)
+    m = compare_layer(out, ref, qc["bits"], wl.n, wv, Href, rel)
+    print(f"{wl.name} {qc}: {m}")
+    ngroups = wl.n // qc["group_size"] if qc["group_size"] > 0 else 1
+    assert tuple(out["scales"].shape) == (ngroups, wl.rows)
+    assert m["agree"] >= 0.999
+    assert m["s_frac"] >= 0.999 and m["z_frac"] >= 0.999
+    assert m["gidx_ok"] and m["pack_ok"]
+    assert m["loss_rel"] <= 0.01
+    assert abs(out["loss"] - ref["L"]) <= 0.01 * ref["L"]
 
 
 def test_shared_hessian_several_layers(g):

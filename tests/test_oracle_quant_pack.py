@@ -16,7 +16,7 @@ def _pages():
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
-@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("sym", [0, 1, 2])
 @pytest.mark.parametrize("qdtype", [np.float64, np.float32])
 def test_code_is_nearest_grid_point_bruteforce(bits, sym, qdtype):
     rng = np.random.default_rng(bits * 10 + sym)
@@ -25,7 +25,7 @@ def test_code_is_nearest_grid_point_bruteforce(bits, sym, qdtype):
     w[4] = -np.abs(w[4])          # all-negative group
     w[5] = 0.0                    # degenerate group
     s, z = oracle.grid_params(w, bits, sym, qdtype)
-    lo = 1 if sym else 0
+    lo = 1 if sym == 1 else 0
     hi = (1 << bits) - 1
     for r in range(w.shape[0]):
         c, q = oracle.quantize_column(w[r], np.full(64, s[r]), np.full(64, z[r]), bits, sym, qdtype)
@@ -34,7 +34,10 @@ def test_code_is_nearest_grid_point_bruteforce(bits, sym, qdtype):
         best = dist.min(axis=1)
         mine = np.abs(w[r] - float(s[r]) * (c - float(z[r])))
         # chosen point is a nearest one (ties: either neighbour), up to rounding of w/s
-        assert np.all(mine <= best + 1e-6 * float(s[r])), r
+        # and, when the decision is taken in binary32, of w itself (|w/s| reaches
+        # 2^(b-1), so that rounding matters at 8 bits)
+        eps = 1e-6 * float(s[r]) + (2.0 ** -22 * np.abs(w[r]) if qdtype == np.float32 else 0.0)
+        assert np.all(mine <= best + eps), r
         assert np.all((c >= lo) & (c <= hi))
         np.testing.assert_allclose(q, float(s[r]) * (c - float(z[r])), rtol=1e-6)
 
@@ -159,3 +162,24 @@ def test_dequantize_roundtrip():
         for i in (0, 127, 128, 255):
             g = g_idx[i]
             assert What[r, i] == float(S[g, r]) * (codes[r, i] - float(Z[g, r]))
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_full_range_symmetric_grid(bits):
+    """sym = 2 keeps the symmetric range [-a, a] but spends all 2^b codes on it:
+    a dense ramp over the range lands on every code, zero is exact, and no
+    weight of the range is more than half a step from its grid point.  The
+    pages' grid (sym = 1) uses 2^b - 1 codes on the same ramp."""
+    a = 0.037
+    ramp = np.linspace(-a, a, 4001)[None, :]
+    s2, z2 = oracle.grid_params(ramp, bits, 2)
+    c2, q2 = oracle.quantize_column(ramp[0], s2[0], z2[0], bits, 2)
+    assert s2[0] == pytest.approx(2 * a / ((1 << bits) - 1), rel=1e-15)
+    assert z2[0] == 1 << (bits - 1)
+    assert set(np.unique(c2)) == set(range(1 << bits))
+    assert np.max(np.abs(ramp[0] - q2)) <= s2[0] / 2 * (1 + 1e-12)
+    c0, q0 = oracle.quantize_column(np.zeros(3), s2[0], z2[0], bits, 2)
+    assert np.all(q0 == 0.0)
+    s1, z1 = oracle.grid_params(ramp, bits, 1)
+    c1, _ = oracle.quantize_column(ramp[0], s1[0], z1[0], bits, 1)
+    assert len(np.unique(c1)) == (1 << bits) - 1

@@ -18,12 +18,13 @@ def _layer(rows=16, n=64, tokens=512, seed=0, outliers=2):
     return W, H
 
 
-@pytest.mark.parametrize("bits,sym", [(4, False), (3, False), (4, True), (3, True)])
+@pytest.mark.parametrize("bits,sym,gs", [(4, 0, 128), (3, 0, 128), (4, 1, 128), (3, 1, 128), (4, 2, 128),
+                                         (4, 0, 32), (3, 1, 64), (4, 0, -1), (4, 2, -1)])
 @pytest.mark.parametrize("qdtype", [np.float64, np.float32])
-def test_identity_hessian_equals_rtn_exactly(bits, sym, qdtype):
+def test_identity_hessian_equals_rtn_exactly(bits, sym, gs, qdtype):
     rng = np.random.default_rng(bits + 2 * sym)
     W = (rng.standard_normal((20, 256)) * 0.02).astype(np.float32).astype(np.float64)
-    cfg = oracle.QuantConfig(bits=bits, group_size=128, sym=sym, desc_act=True, damp=0.01)
+    cfg = oracle.QuantConfig(bits=bits, group_size=gs, sym=sym, desc_act=True, damp=0.01)
     g = oracle.gptq_layer(W, np.eye(256), cfg, qdtype=qdtype)
     r = oracle.rtn(W, cfg, qdtype=qdtype)
     assert np.array_equal(g["perm"], np.arange(256))
@@ -50,7 +51,7 @@ def test_single_column_matches_closed_forms():
     assert np.allclose(st["W"][:, 0], W[:, 0])   # quantized column itself untouched until output
 
 
-@pytest.mark.parametrize("gs", [8, 32])
+@pytest.mark.parametrize("gs", [8, 32, -1])
 def test_bruteforce_obs_tiny(gs):
     W, H = _layer(rows=8, n=32, seed=2)
     cfg = oracle.QuantConfig(bits=3, group_size=gs)
