@@ -123,6 +123,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     # quantize-config overrides (default: the workload's own); e.g. the pages'
     # "maximum precision" recipe: --group-size 32 --desc-act 1 --damp 0.005
+    ap.add_argument("--bits", type=int, default=None, choices=[2, 3, 4, 8])
     ap.add_argument("--group-size", type=int, default=None, choices=[32, 64, 128, -1])
     ap.add_argument("--sym", type=int, default=None, choices=[0, 1, 2])
     ap.add_argument("--desc-act", type=int, default=None, choices=[0, 1])
@@ -142,7 +143,7 @@ def main() -> int:
     import synth
 
     wl = synth.get(args.workload)
-    over = {k: v for k, v in (("group_size", args.group_size), ("sym", args.sym),
+    over = {k: v for k, v in (("bits", args.bits), ("group_size", args.group_size), ("sym", args.sym),
                               ("desc_act", None if args.desc_act is None else bool(args.desc_act)),
                               ("damp", args.damp)) if v is not None}
     if over:

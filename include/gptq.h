@@ -57,7 +57,7 @@ typedef enum { GPTQ_BF16 = 0, GPTQ_FP16 = 1, GPTQ_FP32 = 2 } gptq_dtype;
 
 /* The quantize config of the pages ("Configurações de quantização", "Paramètres clés"). */
 typedef struct {
-  int32_t bits;          /* code width: 3 or 4                                              */
+  int32_t bits;          /* code width: 2, 3, 4 or 8 ("Paramètres clés", bits)             */
   int32_t group_size;    /* weights per scale/zero group along a row: 128, 64, 32, or -1 for  */
                          /* one group per row ("Paramètres clés", group_size)                */
   int32_t sym;           /* 0: asymmetric grid (zero point in [0, 2^bits-1]);               */
@@ -133,8 +133,8 @@ gptq_status gptq_prepare_hinv(const double* H, int64_t n, const gptq_config* cfg
  * Outputs (caller-allocated device buffers):
  *   qweight  int32 [n*bits/32, rows]: row r's codes in ORIGINAL column order form
  *            a little-endian bit stream, column i at bits [bits*i, bits*i+bits);
- *            qweight[k, r] is word k of that stream (4-bit: 8 codes per word;
- *            3-bit: 32 codes per 3 words).
+ *            qweight[k, r] is word k of that stream (2-bit: 16 codes per word;
+ *            3-bit: 32 codes per 3 words; 4-bit: 8; 8-bit: 4).
  *   scales   fp16 bits [G, rows], G = n/group_size (1 for group_size -1):
  *            group g = sweep columns [g*gs, (g+1)*gs).  A group's grid is
  *            taken at its first column from the current (compensated) weights
@@ -145,7 +145,7 @@ gptq_status gptq_prepare_hinv(const double* H, int64_t n, const gptq_config* cfg
  *   loss_out HOST double, may be NULL: sum over rows and columns of e^2 / 2 with
  *            e = (w - w_hat) / U[j, j] (equals tr(D H_d D^T) / 2, D = W - W_hat).
  * Dequantization: W_hat[r, i] = scales[g_idx[i], r] * (code[r, i] - zeros[g_idx[i], r]).
- * Supported: bits in {3, 4}; group_size in {32, 64, 128, -1}; block_size == 128;
+ * Supported: bits in {2, 3, 4, 8}; group_size in {32, 64, 128, -1}; block_size == 128;
  * n % 128 == 0 (GPTQ_ERR_UNSUPPORTED otherwise).
  * rows == 0 is a no-op.  Synchronizes `stream` once when loss_out != NULL.
  * ------------------------------------------------------------------------- */

@@ -64,7 +64,8 @@ gptq_status check_config(const gptq_config* cfg, bool for_quantize) {
   if (cfg->desc_act != 0 && cfg->desc_act != 1) return fail(GPTQ_ERR_INVALID_ARG, "desc_act must be 0 or 1");
   if (!for_quantize) return GPTQ_OK;
   if (cfg->sym < 0 || cfg->sym > 2) return fail(GPTQ_ERR_INVALID_ARG, "sym must be 0, 1 or 2");
-  if (cfg->bits != 3 && cfg->bits != 4) return fail(GPTQ_ERR_UNSUPPORTED, "bits=%d (supported: 3, 4)", cfg->bits);
+  if (cfg->bits != 2 && cfg->bits != 3 && cfg->bits != 4 && cfg->bits != 8)
+    return fail(GPTQ_ERR_UNSUPPORTED, "bits=%d (supported: 2, 3, 4, 8)", cfg->bits);
   if (cfg->group_size != 32 && cfg->group_size != 64 && cfg->group_size != 128 && cfg->group_size != -1)
     return fail(GPTQ_ERR_UNSUPPORTED, "group_size=%d (supported: 32, 64, 128, -1)", cfg->group_size);
   if (cfg->block_size != 128)

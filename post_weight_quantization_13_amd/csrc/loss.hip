@@ -156,15 +156,17 @@ hipError_t launch_layer_loss(const double* H, int64_t n64, const void* W, int wd
 #define GPTQ_DQ(DTV, B)                                                                                       \
   hipLaunchKernelGGL((dequant_diff_kernel<DTV, B>), g, dim3(256), 0, s, W, ldw, rows, n, qweight, scales, zeros, \
                      g_idx, D, Wf)
-  if (bits == 4) {
-    if (wdt == DT_BF16) GPTQ_DQ(DT_BF16, 4);
-    else if (wdt == DT_FP16) GPTQ_DQ(DT_FP16, 4);
-    else GPTQ_DQ(DT_FP32, 4);
-  } else {
-    if (wdt == DT_BF16) GPTQ_DQ(DT_BF16, 3);
-    else if (wdt == DT_FP16) GPTQ_DQ(DT_FP16, 3);
-    else GPTQ_DQ(DT_FP32, 3);
-  }
+#define GPTQ_DQ_BITS(B)                         \
+  do {                                          \
+    if (wdt == DT_BF16) GPTQ_DQ(DT_BF16, B);    \
+    else if (wdt == DT_FP16) GPTQ_DQ(DT_FP16, B); \
+    else GPTQ_DQ(DT_FP32, B);                   \
+  } while (0)
+  if (bits == 2) GPTQ_DQ_BITS(2);
+  else if (bits == 3) GPTQ_DQ_BITS(3);
+  else if (bits == 4) GPTQ_DQ_BITS(4);
+  else GPTQ_DQ_BITS(8);
+#undef GPTQ_DQ_BITS
 #undef GPTQ_DQ
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -302,12 +302,17 @@ __global__ void __launch_bounds__(256) row_params_kernel(const float* __restrict
 //   barrier; all waves apply the errors of sub-block s to the columns of
 //   sub-block s+1 ("near" update, which the next chain step needs); barrier.
 // Codes: c = clamp(rint(w / s) + z).  Each sub-block's chain first runs with
-// the quotient formed as w * (1/s).  If any quotient lay within 2^-18 of a
-// rounding midpoint (that form errs by at most ~2 ulp = 2^-18 for |w/s| < 16,
-// the only range where rint decides a code), the sub-block is replayed from
-// its saved inputs with IEEE division, so the codes equal those of a
+// the quotient formed as w * (1/s).  rint decides a code only while
+// |w / s| <= maxq + 1/2 < 2^b (beyond that the clamp does); there w * (1/s)
+// errs by at most ~2 ulp, under 2^(b-22) (2^-18 for b <= 4).  If any quotient
+// lay within that distance of a rounding midpoint, the sub-block is replayed
+// from its saved inputs with IEEE division, so the codes equal those of a
 // correctly rounded w / s.  The fast path has no branch inside the chain.
 constexpr int kSubs = kBlk / kSub;  // 8
+template <int BITS>
+constexpr float near_midpoint() {
+  return (BITS <= 4) ? 3.814697265625e-06f : 3.814697265625e-06f * static_cast<float>(1 << (BITS - 4));
+}
 
 template <int BITS, int SYM>
 __global__ void __launch_bounds__(256) sweep_block_kernel(
@@ -476,8 +481,8 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
         }
       }
       // The chain of one sub-block.  EXACT = false forms w / s as w * (1/s)
-      // and reports whether any quotient came within 2^-18 of a rounding
-      // midpoint; EXACT = true uses IEEE division throughout.
+      // and reports whether any quotient came within near_midpoint<BITS>() of
+      // a rounding midpoint; EXACT = true uses IEEE division throughout.
       auto chain = [&](auto exact_tag, uint32_t (&cw)[kSub / 4], float& lsum) -> bool {
         constexpr bool EXACT = decltype(exact_tag)::value;
         float w[kSub];
@@ -491,7 +496,7 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
             qt = w[t] / sv;
           } else {
             qt = w[t] * rs;
-            near |= fabsf(fabsf(qt - rintf(qt)) - 0.5f) < 3.814697265625e-06f;
+            near |= fabsf(fabsf(qt - rintf(qt)) - 0.5f) < near_midpoint<BITS>();
           }
           const float c = fminf(fmaxf(rintf(qt) + zv, lo), maxq);
           const float q = sv * (c - zv);
@@ -748,6 +753,22 @@ static void launch_row_params(hipStream_t s, const float* Wk, int n, int rows, f
   hipLaunchKernelGGL((row_params_kernel<BITS, SYM>), dim3(rows), dim3(256), 0, s, Wk, n, rows, rowsz);
 }
 
+// Calls M(bits, sym) with compile-time constants for the runtime bits (2, 3,
+// 4, 8) and sym (0, 1, 2).
+#define GPTQ_BY_SYM(M, B) \
+  do {                    \
+    if (sym == 0) M(B, 0); \
+    else if (sym == 1) M(B, 1); \
+    else M(B, 2);         \
+  } while (0)
+#define GPTQ_BY_BITS_SYM(M)                 \
+  do {                                      \
+    if (bits == 2) GPTQ_BY_SYM(M, 2);       \
+    else if (bits == 3) GPTQ_BY_SYM(M, 3);  \
+    else if (bits == 4) GPTQ_BY_SYM(M, 4);  \
+    else GPTQ_BY_SYM(M, 8);                 \
+  } while (0)
+
 hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* dead, int64_t n64, int bits,
                            int sym, int group_size, const void* W, int wdt, int64_t rows64, int64_t ldw,
                            int32_t* qweight, uint16_t* scales, uint16_t* zeros, int32_t* g_idx, double* loss_host,
@@ -793,12 +814,9 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
   hipLaunchKernelGGL(gidx_kernel, dim3((n + 255) / 256), dim3(256), 0, s, perm, n, gs > 0 ? gs : n, g_idx, invperm);
   GPTQ_CHECK_LAUNCH();
   if (gs == 0) {
-    if (bits == 4 && sym == 0) launch_row_params<4, 0>(s, Wk, n, rows, rowsz);
-    else if (bits == 4 && sym == 1) launch_row_params<4, 1>(s, Wk, n, rows, rowsz);
-    else if (bits == 4) launch_row_params<4, 2>(s, Wk, n, rows, rowsz);
-    else if (sym == 0) launch_row_params<3, 0>(s, Wk, n, rows, rowsz);
-    else if (sym == 1) launch_row_params<3, 1>(s, Wk, n, rows, rowsz);
-    else launch_row_params<3, 2>(s, Wk, n, rows, rowsz);
+#define GPTQ_ROWP(B, S) launch_row_params<B, S>(s, Wk, n, rows, rowsz)
+    GPTQ_BY_BITS_SYM(GPTQ_ROWP);
+#undef GPTQ_ROWP
     GPTQ_CHECK_LAUNCH();
   }
   hipLaunchKernelGGL(split_ut_kernel, dim3(n / 64, n / 64), dim3(256), 0, s, U, n, UTh, UTl);
@@ -850,12 +868,7 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
       uint16_t* Ebl = Ejl + (i1 - s1);
 #define GPTQ_SWEEP(B, S) \
   launch_sweep<B, S>(grid, s, Wk, U, UTh, UTl, n, rows, i1, codes, Ebh, Ebl, sa, sb, scales, zeros, rowloss, gs, rowsz)
-      if (bits == 4 && sym == 0) GPTQ_SWEEP(4, 0);
-      else if (bits == 4 && sym == 1) GPTQ_SWEEP(4, 1);
-      else if (bits == 4) GPTQ_SWEEP(4, 2);
-      else if (sym == 0) GPTQ_SWEEP(3, 0);
-      else if (sym == 1) GPTQ_SWEEP(3, 1);
-      else GPTQ_SWEEP(3, 2);
+      GPTQ_BY_BITS_SYM(GPTQ_SWEEP);
 #undef GPTQ_SWEEP
       GPTQ_CHECK_LAUNCH();
     }
@@ -884,8 +897,10 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
     }
   }
   dim3 gp((rows + 255) / 256, n / 32);  // n <= 65535 * 32 is checked by the caller
-  if (bits == 4) hipLaunchKernelGGL(pack_kernel<4>, gp, dim3(256), 0, s, codes, invperm, n, rows, qweight);
-  else hipLaunchKernelGGL(pack_kernel<3>, gp, dim3(256), 0, s, codes, invperm, n, rows, qweight);
+  if (bits == 2) hipLaunchKernelGGL(pack_kernel<2>, gp, dim3(256), 0, s, codes, invperm, n, rows, qweight);
+  else if (bits == 3) hipLaunchKernelGGL(pack_kernel<3>, gp, dim3(256), 0, s, codes, invperm, n, rows, qweight);
+  else if (bits == 4) hipLaunchKernelGGL(pack_kernel<4>, gp, dim3(256), 0, s, codes, invperm, n, rows, qweight);
+  else hipLaunchKernelGGL(pack_kernel<8>, gp, dim3(256), 0, s, codes, invperm, n, rows, qweight);
   GPTQ_CHECK_LAUNCH();
   if (loss_host) {
     hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, s, rowloss, rows, loss_dev);

@@ -78,7 +78,8 @@ def test_argument_validation(g):
     args = lambda n=256, rows=8, ldw=256, ws=1 << 30, cfg=None, wdt=0: (
         FAKE, FAKE, FAKE, n, cfg or _cfg(), FAKE, wdt, rows, ldw, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, None)
     assert L.gptq_quantize_layer(*args(cfg=_cfg(bits=5))) == g.GPTQ_ERR_UNSUPPORTED
-    assert L.gptq_quantize_layer(*args(cfg=_cfg(bits=8))) == g.GPTQ_ERR_UNSUPPORTED
+    assert L.gptq_quantize_layer(*args(cfg=_cfg(bits=1))) == g.GPTQ_ERR_UNSUPPORTED
+    assert L.gptq_quantize_layer(*args(cfg=_cfg(bits=6))) == g.GPTQ_ERR_UNSUPPORTED
     assert L.gptq_quantize_layer(*args(cfg=_cfg(group_size=16))) == g.GPTQ_ERR_UNSUPPORTED
     assert L.gptq_quantize_layer(*args(cfg=_cfg(group_size=256))) == g.GPTQ_ERR_UNSUPPORTED
     assert L.gptq_quantize_layer(*args(cfg=_cfg(group_size=0))) == g.GPTQ_ERR_UNSUPPORTED

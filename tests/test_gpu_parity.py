@@ -128,7 +128,8 @@ def test_prepare_not_positive_definite(g):
 
 # --------------------------------------------------------------------------- quantize
 @pytest.mark.parametrize("bits,sym,gs", [(4, 0, 128), (3, 0, 128), (4, 1, 128), (3, 1, 128), (4, 2, 128),
-                                         (3, 2, 128), (4, 0, 32), (3, 1, 64), (4, 2, 32), (4, 0, -1), (3, 2, -1)])
+                                         (3, 2, 128), (4, 0, 32), (3, 1, 64), (4, 2, 32), (4, 0, -1), (3, 2, -1),
+                                         (2, 0, 128), (2, 1, 64), (8, 0, 128), (8, 1, 32), (8, 2, -1)])
 def test_identity_hessian_is_rtn_bit_exact(g, bits, sym, gs):
     import torch
     rows, n = 200, 384
@@ -201,6 +202,11 @@ VARIANTS = [
     ("attn4096", dict(rows=200, n=512, tokens=4096), dict(bits=4, group_size=-1, sym=0, desc_act=True, damp=0.01)),
     ("down28672", dict(rows=72, n=768, tokens=8192), dict(bits=4, group_size=128, sym=2, desc_act=True, damp=0.01)),
     ("attn4096", dict(rows=200, n=512, tokens=4096), dict(bits=3, group_size=64, sym=2, desc_act=False, damp=0.005)),
+    # the other widths "Paramètres clés" lists (bits 3, 4 or 8) and 2 bits
+    ("attn4096", dict(rows=200, n=512, tokens=4096), dict(bits=8, group_size=128, sym=0, desc_act=True, damp=0.01)),
+    ("mlpdown11008", dict(rows=136, n=640, tokens=4096), dict(bits=8, group_size=64, sym=1, desc_act=False, damp=0.01)),
+    ("attn4096", dict(rows=200, n=512, tokens=4096), dict(bits=2, group_size=128, sym=0, desc_act=True, damp=0.01)),
+    ("down28672", dict(rows=72, n=768, tokens=8192), dict(bits=2, group_size=32, sym=2, desc_act=True, damp=0.01)),
 ]
 
 
@@ -307,7 +313,7 @@ def test_abi_edge_cases(g):
         g.gptq_quantize_layer(U, perm, dead, cfg, W, q, s, z, gi, g.workspace(16, "cuda"))
     assert ei.value.status == g.GPTQ_ERR_WORKSPACE
     with pytest.raises(g.GptqError) as ei:
-        g.quantize_layer(U, perm, dead, g.Config(bits=2), W)
+        g.quantize_layer(U, perm, dead, g.Config(bits=5), W)
     assert ei.value.status == g.GPTQ_ERR_UNSUPPORTED
 
 
