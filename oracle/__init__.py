@@ -20,5 +20,5 @@ from .gptq import (  # noqa: F401
     QuantConfig, NotPositiveDefinite,
     hessian, hessian_entries, prepare, grid_params, quantize_column, sweep,
     quantize_layer, gptq_layer, rtn, obs_bruteforce, pack, unpack,
-    dequantize, rel_loss, to_fp16,
+    dequantize, dequant_matmul, grouped_order, rel_loss, to_fp16,
 )

@@ -416,6 +416,30 @@ def dequantize(qweight, scales, zeros, g_idx, bits, rows, n):
     return s * (codes - z)
 
 
+def dequant_matmul(A, qweight, scales, zeros, g_idx, bits, rows, n):
+    """Y = A W_hat^T in float64: the product an inference kernel forms with the
+    packed layer.
+
+    [ayinedjimi] "Calibration et dataset" and "Kernels d'inférence": the GPU
+    kernels that serve a GPTQ model unpack and dequantize the low-bit weights on
+    the fly and multiply them with the (fp16) activations, so their result is
+    the product of the activations with the dequantized matrix.  A is
+    [tokens, n] (fp16 values; any real array is accepted), Y is [tokens, rows].
+    """
+    What = dequantize(qweight, scales, zeros, g_idx, bits, rows, n)
+    return np.asarray(A, dtype=np.float64) @ What.T
+
+
+def grouped_order(g_idx):
+    """Columns listed group by group, ascending column index inside a group.
+
+    The order in which a kernel that keeps one scale/zero pair per run of
+    consecutive columns has to visit the input features when act-order has
+    scattered the groups ([polydesk] "Paramètres clés de GPTQ", desc_act).
+    """
+    return np.argsort(np.asarray(g_idx), kind="stable").astype(np.int32)
+
+
 def rel_loss(W, What, H):
     """||W X - What X||^2 / ||W X||^2 = tr(D H D^T) / tr(W H W^T), D = W - What.
 
