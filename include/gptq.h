@@ -172,6 +172,59 @@ gptq_status gptq_layer_loss(const double* H, int64_t n, const void* W, gptq_dtyp
                             const gptq_config* cfg, double* rel_loss,
                             void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------- *
+ * Dequantizing matmul for inference with a quantized layer (ayinedjimi-
+ * consultants "Quantization : GPTQ, GGUF, AWQ", "Calibration et dataset" and
+ * "Kernels d'inférence": the serving kernels unpack and dequantize the packed
+ * low-bit weights on the fly and multiply them with fp16 activations).
+ *
+ * gptq_matmul_pack: once per layer, converts the outputs of
+ * gptq_quantize_layer into the tiled layout gptq_matmul reads.
+ *   qweight, scales, zeros, g_idx  as gptq_quantize_layer writes them for
+ *            (rows, n, bits, group_size); not modified.
+ *   packed   device buffer of at least gptq_matmul_packed_bytes(rows, n, bits,
+ *            group_size) bytes (packed_bytes gives its size), 16-byte aligned.
+ *   col_order device int32 [n], 16-byte aligned: the input columns listed group
+ *            by group (ascending column index inside a group).  It is the
+ *            identity unless act-order scattered the groups.
+ *   identity HOST int32 out, may be NULL: 1 if col_order is the identity.
+ * Synchronizes `stream` (to read the validation flag).  Returns
+ * GPTQ_ERR_INVALID_ARG if g_idx does not split the n columns into n/group_size
+ * groups (one for group_size -1) of group_size columns each; the codes are not
+ * retiled then, and packed and col_order hold no usable layout.
+ *
+ * gptq_matmul: Y[m, o] = sum_i A[m, i] * W_hat[o, i] for m < M, o < rows, with
+ * W_hat[o, i] = scales[g_idx[i], o] * (code[o, i] - zeros[g_idx[i], o]).
+ *   A        device fp16 [M, lda], lda >= n (adt must be GPTQ_FP16).  With
+ *            col_order NULL, A must be 16-byte aligned and lda a multiple of 8.
+ *   packed   as written by gptq_matmul_pack for the same rows, n, bits, group_size.
+ *   col_order NULL when the pack reported identity (the activations are then
+ *            read in place), else the col_order the pack wrote: the
+ *            activations are first copied in that order into the workspace.
+ *   workspace, ws_bytes: device scratch of gptq_matmul_workspace_bytes(M, n,
+ *            col_order != NULL) bytes, 16-byte aligned (0 bytes, NULL accepted,
+ *            without col_order).
+ *   Y        device [M, ldy] of ydt (GPTQ_FP16 or GPTQ_FP32), ldy >= rows; only
+ *            columns 0..rows-1 of rows 0..M-1 are written.
+ * Products of the fp16 activations with the exact integers code - zero are
+ * summed in fp32, each group's sum is scaled by its fp16 scale in fp32, and the
+ * result is rounded once to ydt.  Tokens are processed 16 at a time: beyond 16
+ * tokens the weights are read once per 16 (the kernel targets decoding).
+ * Does not synchronize, allocate or clear memory, so it can be captured in a
+ * graph; calls that share a workspace must not overlap.  M == 0 is a no-op.  Deterministic.
+ * Supported: bits 2, 3, 4, 8; group_size 32, 64, 128, -1; n a multiple of 128.
+ * ------------------------------------------------------------------------- */
+size_t gptq_matmul_packed_bytes(int64_t rows, int64_t n, int32_t bits, int32_t group_size);
+gptq_status gptq_matmul_pack(const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                             const int32_t* g_idx, int64_t rows, int64_t n, int32_t bits, int32_t group_size,
+                             void* packed, size_t packed_bytes, int32_t* col_order, int32_t* identity,
+                             void* stream);
+size_t gptq_matmul_workspace_bytes(int64_t M, int64_t n, int32_t has_col_order);
+gptq_status gptq_matmul(const void* A, gptq_dtype adt, int64_t M, int64_t lda, const void* packed,
+                        const int32_t* col_order, int64_t rows, int64_t n, int32_t bits, int32_t group_size,
+                        void* Y, gptq_dtype ydt, int64_t ldy, void* workspace, size_t ws_bytes,
+                        void* stream);
+
 /* Message for the last failing call on this thread (empty string if none). */
 const char* gptq_last_error(void);
 /* Library version string. */

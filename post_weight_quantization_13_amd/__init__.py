@@ -11,6 +11,8 @@ Functions keep the C names:
     gptq_prepare_hinv(H, cfg, U, perm, dead, ws)
     gptq_quantize_layer(U, perm, dead, cfg, W, qweight, scales, zeros, g_idx, ws) -> loss
     gptq_layer_loss(H, W, qweight, scales, zeros, g_idx, cfg, ws) -> relative loss
+    gptq_matmul_pack(qweight, scales, zeros, g_idx, bits, group_size, packed, col_order) -> identity
+    gptq_matmul(A, packed, col_order, rows, n, bits, group_size, Y, ws)
 plus the workspace queries and small allocating helpers (``quantize_layer``,
 ``hessian``, ``prepare``) that create the output tensors with torch.
 """
@@ -39,6 +41,7 @@ EXPORTS = (
     "gptq_prepare_workspace_bytes", "gptq_prepare_hinv",
     "gptq_quantize_workspace_bytes", "gptq_quantize_layer",
     "gptq_layer_loss_workspace_bytes", "gptq_layer_loss",
+    "gptq_matmul_packed_bytes", "gptq_matmul_pack", "gptq_matmul_workspace_bytes", "gptq_matmul",
     "gptq_last_error", "gptq_version",
 )
 
@@ -104,6 +107,16 @@ def lib() -> ctypes.CDLL:
     L.gptq_layer_loss.argtypes = [vp, i64, vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, cfgp,
                                   ctypes.POINTER(ctypes.c_double), vp, sz, vp]
     L.gptq_layer_loss.restype = ctypes.c_int
+    i32 = ctypes.c_int32
+    L.gptq_matmul_packed_bytes.argtypes = [i64, i64, i32, i32]
+    L.gptq_matmul_packed_bytes.restype = sz
+    L.gptq_matmul_pack.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, vp, sz, vp, ctypes.POINTER(i32), vp]
+    L.gptq_matmul_pack.restype = ctypes.c_int
+    L.gptq_matmul_workspace_bytes.argtypes = [i64, i64, i32]
+    L.gptq_matmul_workspace_bytes.restype = sz
+    L.gptq_matmul.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, i64, vp,
+                              sz, vp]
+    L.gptq_matmul.restype = ctypes.c_int
     L.gptq_last_error.argtypes = []
     L.gptq_last_error.restype = ctypes.c_char_p
     L.gptq_version.argtypes = []
@@ -212,6 +225,37 @@ def gptq_layer_loss(H, W, qweight, scales, zeros, g_idx, cfg, workspace, stream=
     return out.value
 
 
+def gptq_matmul_packed_bytes(rows: int, n: int, bits: int, group_size: int) -> int:
+    return lib().gptq_matmul_packed_bytes(rows, n, bits, group_size)
+
+
+def gptq_matmul_pack(qweight, scales, zeros, g_idx, bits: int, group_size: int, packed, col_order,
+                     stream=None) -> bool:
+    """Tiled copy of a quantized layer for gptq_matmul; returns True if col_order is the identity."""
+    rows = qweight.shape[1]
+    n = g_idx.shape[0]
+    ident = ctypes.c_int32(0)
+    _check(lib().gptq_matmul_pack(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(g_idx), rows, n, bits, group_size,
+                                  _ptr(packed), packed.numel() * packed.element_size(), _ptr(col_order),
+                                  ctypes.byref(ident), _stream(stream, qweight.device)))
+    return bool(ident.value)
+
+
+def gptq_matmul_workspace_bytes(M: int, n: int, has_col_order: bool) -> int:
+    return lib().gptq_matmul_workspace_bytes(M, n, int(bool(has_col_order)))
+
+
+def gptq_matmul(A, packed, col_order, rows: int, n: int, bits: int, group_size: int, Y, workspace=None,
+                stream=None) -> None:
+    """Y[:M, :rows] = A W_hat^T for fp16 activations A [M, >= n]."""
+    lda = _row_major_2d(A, "A")
+    ldy = _row_major_2d(Y, "Y")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gptq_matmul(_ptr(A), _dtype_code(A), A.shape[0], lda, _ptr(packed), _ptr(col_order), rows, n, bits,
+                             group_size, _ptr(Y), _dtype_code(Y), ldy, _ptr(workspace), ws_bytes,
+                             _stream(stream, A.device)))
+
+
 def gptq_version() -> str:
     return lib().gptq_version().decode()
 
@@ -274,3 +318,34 @@ def layer_loss(H, W, out, cfg) -> float:
     rows, n = W.shape
     ws = workspace(gptq_layer_loss_workspace_bytes(rows, n), W.device)
     return gptq_layer_loss(H, W, out["qweight"], out["scales"], out["zeros"], out["g_idx"], cfg, ws)
+
+
+class PackedLayer:
+    """A quantized layer in the matmul's tiled layout (see gptq_matmul_pack)."""
+
+    def __init__(self, qweight, scales, zeros, g_idx, bits: int, group_size: int):
+        import torch
+        self.rows = qweight.shape[1]
+        self.n = g_idx.shape[0]
+        self.bits, self.group_size = int(bits), int(group_size)
+        dev = qweight.device
+        self.packed = torch.empty(gptq_matmul_packed_bytes(self.rows, self.n, self.bits, self.group_size),
+                                  dtype=torch.uint8, device=dev)
+        order = torch.empty(self.n, dtype=torch.int32, device=dev)
+        ident = gptq_matmul_pack(qweight, scales, zeros, g_idx, self.bits, self.group_size, self.packed, order)
+        self.col_order = None if ident else order
+
+    def workspace(self, M: int):
+        nb = gptq_matmul_workspace_bytes(M, self.n, self.col_order is not None)
+        return workspace(nb, self.packed.device) if nb else None
+
+    def matmul(self, A, out_dtype=None, Y=None, ws=None):
+        """Y = A W_hat^T (fp16 A [M, n]); out_dtype float16 (default) or float32."""
+        import torch
+        M = A.shape[0]
+        if Y is None:
+            Y = torch.empty((M, self.rows), dtype=out_dtype or torch.float16, device=A.device)
+        if ws is None and self.col_order is not None:
+            ws = self.workspace(M)
+        gptq_matmul(A, self.packed, self.col_order, self.rows, self.n, self.bits, self.group_size, Y, ws)
+        return Y

@@ -27,6 +27,14 @@ size_t loss_workspace(int64_t rows, int64_t n);
 hipError_t launch_layer_loss(const double* H, int64_t n, const void* W, int wdt, int64_t rows, int64_t ldw,
                              const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                              const int32_t* g_idx, int bits, double* rel_host, void* ws, hipStream_t s);
+size_t matmul_packed_bytes(int64_t rows, int64_t n, int bits, int group_size);
+hipError_t launch_matmul_pack(const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                              const int32_t* g_idx, int64_t rows, int64_t n, int bits, int group_size,
+                              void* packed, int32_t* col_order, uint32_t* flags_host, hipStream_t s);
+size_t matmul_workspace_bytes(int64_t M, int64_t n);
+hipError_t launch_matmul(const void* A, int64_t M, int64_t lda, const void* packed, const int32_t* col_order,
+                         int64_t rows, int64_t n, int bits, int group_size, void* Y, int ydt, int64_t ldy,
+                         void* ws, hipStream_t s);
 }  // namespace gptq
 
 namespace {
@@ -72,6 +80,21 @@ gptq_status check_config(const gptq_config* cfg, bool for_quantize) {
     return fail(GPTQ_ERR_UNSUPPORTED, "block_size=%d (supported: 128)", cfg->block_size);
   return GPTQ_OK;
 }
+
+// Shape and format checks shared by the matmul pack and the matmul.
+gptq_status check_matmul_format(int64_t rows, int64_t n, int32_t bits, int32_t group_size) {
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8)
+    return fail(GPTQ_ERR_UNSUPPORTED, "bits=%d (supported: 2, 3, 4, 8)", bits);
+  if (group_size != 32 && group_size != 64 && group_size != 128 && group_size != -1)
+    return fail(GPTQ_ERR_UNSUPPORTED, "group_size=%d (supported: 32, 64, 128, -1)", group_size);
+  if (n < 128 || n > kMaxDim || n % 128 != 0)
+    return fail(GPTQ_ERR_UNSUPPORTED, "n=%lld must be a positive multiple of 128 up to %lld", (long long)n,
+                (long long)kMaxDim);
+  if (rows < 1 || rows > (int64_t)1 << 30) return fail(GPTQ_ERR_INVALID_ARG, "rows=%lld out of range", (long long)rows);
+  return GPTQ_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 }  // namespace
 
@@ -199,6 +222,69 @@ gptq_status gptq_layer_loss(const double* H, int64_t n, const void* W, gptq_dtyp
   hipError_t e = gptq::launch_layer_loss(H, n, W, static_cast<int>(wdt), rows, ldw, qweight, scales, zeros, g_idx,
                                          cfg->bits, rel_loss, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("gptq_layer_loss", e);
+  return ok();
+}
+
+// ----------------------------------------------------------------------------- dequantizing matmul
+size_t gptq_matmul_packed_bytes(int64_t rows, int64_t n, int32_t bits, int32_t group_size) {
+  if (check_matmul_format(rows, n, bits, group_size) != GPTQ_OK) return 0;
+  return gptq::matmul_packed_bytes(rows, n, bits, group_size);
+}
+
+gptq_status gptq_matmul_pack(const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                             const int32_t* g_idx, int64_t rows, int64_t n, int32_t bits, int32_t group_size,
+                             void* packed, size_t packed_bytes, int32_t* col_order, int32_t* identity,
+                             void* stream) {
+  gptq_status st = check_matmul_format(rows, n, bits, group_size);
+  if (st != GPTQ_OK) return st;
+  if (!qweight || !scales || !zeros || !g_idx || !packed || !col_order)
+    return fail(GPTQ_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned16(packed) || !aligned16(col_order))
+    return fail(GPTQ_ERR_INVALID_ARG, "packed and col_order must be 16-byte aligned");
+  const size_t need = gptq::matmul_packed_bytes(rows, n, bits, group_size);
+  if (packed_bytes < need)
+    return fail(GPTQ_ERR_WORKSPACE, "packed buffer %zu bytes < required %zu", packed_bytes, need);
+  uint32_t flags = 0;
+  hipError_t e = gptq::launch_matmul_pack(qweight, scales, zeros, g_idx, rows, n, bits, group_size, packed,
+                                          col_order, &flags, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("gptq_matmul_pack", e);
+  if (flags & 1u)
+    return fail(GPTQ_ERR_INVALID_ARG, "g_idx does not split the %lld columns into groups of %d", (long long)n,
+                group_size > 0 ? group_size : (int)n);
+  if (identity) *identity = (flags & 2u) ? 0 : 1;
+  return ok();
+}
+
+size_t gptq_matmul_workspace_bytes(int64_t M, int64_t n, int32_t has_col_order) {
+  if (M < 1 || n < 1 || !has_col_order) return 0;
+  return gptq::matmul_workspace_bytes(M, n);
+}
+
+gptq_status gptq_matmul(const void* A, gptq_dtype adt, int64_t M, int64_t lda, const void* packed,
+                        const int32_t* col_order, int64_t rows, int64_t n, int32_t bits, int32_t group_size,
+                        void* Y, gptq_dtype ydt, int64_t ldy, void* workspace, size_t ws_bytes, void* stream) {
+  gptq_status st = check_matmul_format(rows, n, bits, group_size);
+  if (st != GPTQ_OK) return st;
+  if (adt != GPTQ_FP16) return fail(GPTQ_ERR_UNSUPPORTED, "activations must be fp16 (got dtype %d)", (int)adt);
+  if (ydt != GPTQ_FP16 && ydt != GPTQ_FP32)
+    return fail(GPTQ_ERR_UNSUPPORTED, "output must be fp16 or fp32 (got dtype %d)", (int)ydt);
+  if (M < 0 || M > (int64_t)65535 * 16) return fail(GPTQ_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
+  if (M == 0) return ok();
+  if (!A || !packed || !Y) return fail(GPTQ_ERR_INVALID_ARG, "NULL pointer argument");
+  if (lda < n || ldy < rows)
+    return fail(GPTQ_ERR_INVALID_ARG, "lda=%lld < n or ldy=%lld < rows", (long long)lda, (long long)ldy);
+  if (!aligned16(packed)) return fail(GPTQ_ERR_INVALID_ARG, "packed must be 16-byte aligned");
+  if (col_order) {
+    const size_t need = gptq::matmul_workspace_bytes(M, n);
+    if (!workspace || ws_bytes < need || !aligned16(workspace))
+      return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes < required %zu (or not 16-byte aligned)",
+                  workspace ? ws_bytes : 0, need);
+  } else if (!aligned16(A) || lda % 8 != 0) {
+    return fail(GPTQ_ERR_INVALID_ARG, "A must be 16-byte aligned with lda a multiple of 8");
+  }
+  hipError_t e = gptq::launch_matmul(A, M, lda, packed, col_order, rows, n, bits, group_size, Y,
+                                     static_cast<int>(ydt), ldy, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("gptq_matmul", e);
   return ok();
 }
 

@@ -49,6 +49,14 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float x) {
   return b;
 }
 
+// Barrier for exchanges through LDS only: waits for this wave's LDS accesses,
+// not for its global loads, which may stay in flight across it (operands
+// prefetched into registers several steps ahead).  The memory clobber keeps
+// the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Zero `words` 8-byte words at p.  A kernel rather than hipMemsetAsync, so the

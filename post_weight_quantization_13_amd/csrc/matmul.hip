@@ -1,0 +1,626 @@
+// Dequantizing matmul for inference with the packed layer: Y = A W_hat^T with
+// fp16 activations A [M, n] and W_hat[o, i] = s[g(i), o] * (code[o, i] - z[g(i), o]).
+//
+// ayinedjimi-consultants "Quantization : GPTQ, GGUF, AWQ", "Calibration et
+// dataset" and "Kernels d'inférence": a GPTQ layer is served by a kernel that
+// unpacks and dequantizes the low-bit weights on the fly and multiplies them
+// with fp16 activations; such kernels are judged by the fraction of memory
+// bandwidth they reach.  This is a gfx950 design of that role, not of the
+// NVIDIA kernels the page names.
+//
+// Two calls:
+//   pack (once per layer): orders the columns group by group (identity unless
+//     act-order scattered the groups), retiles the codes so that one lane's
+//     16-byte load is exactly its B operand of four 16x16x32 f16 MFMAs, and
+//     interleaves scale and zero per 16-output tile.
+//   matmul (per token batch): one workgroup of 8 waves per 16 outputs; wave w
+//     takes 128-column chunks w, w+8, ...; its chunk loads run 4 chunks ahead
+//     in registers.  The activations of each 1024-column window are staged in
+//     LDS (double buffered).  Codes are turned into the exact integers c - z
+//     in fp16 with the 0x6400 exponent trick (0x6400 | c is 1024 + c), so the
+//     MFMA products are exact and only fp32 accumulation rounds; each group's
+//     partial sum is scaled by its fp32 scale when the group ends.
+//
+// Packed layout (bytes):
+//   [0, 256)           header: flags word written by pack (bit 0: g_idx is not a
+//                      grouping into groups of group_size; bit 1: order not identity)
+//   Q   at 256         [T][C][64 lanes][bits words]: T = ceil(rows/16) output
+//                      tiles, C = n/128 chunks.  Lane l = 16q + j holds, for
+//                      the four 32-column steps t of the chunk, the eight codes
+//                      of output 16T + j at grouped columns 128c + 32t + 8q + s,
+//                      s = 0..7, as an 8*bits-bit field per step (step t at bit
+//                      8*bits*t of the lane's stream); inside a field the code
+//                      of slot s sits at field position field_pos(bits, s), so the
+//                      unpacking below yields the slots in order.
+//   SZ  after Q        [T][Cs][16][spc] u32: low half the fp16 scale, high half
+//                      the fp16 zero (0 for padding outputs).  spc = 128/gs
+//                      words per chunk (groups c*spc .. c*spc+spc-1) and
+//                      Cs = C; for one group per row Cs = spc = 1.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace gptq {
+namespace {
+
+constexpr int kMmWaves = 8;          // waves per workgroup
+constexpr int kMmThreads = kMmWaves * 64;
+constexpr int kChunk = 128;          // columns per chunk (four 32-column MFMA steps)
+constexpr int kWin = kMmWaves * kChunk;  // columns per LDS window (one chunk per wave)
+constexpr int kWinStride = kWin + 8;     // halves per staged row (16-byte pad against bank conflicts)
+constexpr int kMTile = 16;           // tokens per MFMA tile
+constexpr int kAhead = 4;            // chunks of codes each wave keeps in flight (even)
+constexpr size_t kFullLds = 80 * 1024;  // largest slice of activations staged whole
+constexpr size_t kHeader = 256;
+// s_waitcnt immediate for vmcnt(0) with the other counters left alone (gfx9
+// layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kVmcntZero = 0x0F70;
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Position of slot s inside a step's field, per code width: the unpacking
+// makes half-pairs of fields (0,4), (1,5), (2,6), (3,7) (2-, 3-, 4-bit) or
+// (0,2), (1,3), (4,6), (5,7) (8-bit), and the MFMA operand wants slots
+// (0,1), (2,3), (4,5), (6,7) in that order.
+__host__ __device__ constexpr int field_pos(int bits, int s) {
+  return bits == 8 ? ((s >> 2) << 2) + ((s & 1) << 1) + ((s >> 1) & 1)
+                   : ((s & 1) << 2) + (s >> 1);
+}
+
+// ------------------------------------------------------------------ pack side
+// Column order: workgroup g lists the columns with g_idx == g in ascending
+// order into col_order[g*gs ...].  Flags bit 0 when a group does not hold
+// exactly gs columns (which also catches g_idx values outside [0, G)), bit 1
+// when some column moves.
+__global__ __launch_bounds__(256) void group_order_kernel(const int32_t* __restrict__ g_idx, int n, int gs,
+                                                         int32_t* __restrict__ col_order,
+                                                         uint32_t* __restrict__ flags) {
+  __shared__ int wave_cnt[4];
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int base = g * gs;
+  int count = 0;
+  uint32_t moved = 0, bad = 0;
+  for (int i0 = 0; i0 < n; i0 += 256) {
+    const int i = i0 + tid;
+    const bool mine = i < n && g_idx[i] == g;
+    const uint64_t mask = __ballot(mine);
+    const int rank = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                               __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
+    if (lane == 0) wave_cnt[wave] = __popcll(mask);
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int v = 0; v < 4; ++v) {
+      before += v < wave ? wave_cnt[v] : 0;
+      total += wave_cnt[v];
+    }
+    if (mine) {
+      const int pos = count + before + rank;
+      if (pos < gs) {
+        col_order[base + pos] = i;
+        moved |= (base + pos != i) ? 2u : 0u;
+      } else {
+        bad = 1u;
+      }
+    }
+    count += total;
+    __syncthreads();
+  }
+  if (tid == 0 && count != gs) bad = 1u;
+  const uint32_t f = bad | moved;
+  if (f) atomicOr(flags, f);
+}
+
+// Codes: thread per (tile, chunk, lane) writes the lane's bits words.
+template <int BITS>
+__global__ __launch_bounds__(256) void pack_codes_kernel(const uint32_t* __restrict__ qweight,
+                                                        const int32_t* __restrict__ col_order, int rows, int n,
+                                                        int T, uint32_t* __restrict__ Q) {
+  const int C = n / kChunk;
+  const int64_t id = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (id >= static_cast<int64_t>(T) * C * 64) return;
+  const int lane = static_cast<int>(id & 63);
+  const int64_t tc = id >> 6;
+  const int c = static_cast<int>(tc % C);
+  const int tile = static_cast<int>(tc / C);
+  const int q = lane >> 4, j = lane & 15;
+  const int o = tile * 16 + j;
+  uint32_t out[BITS];
+  for (int v = 0; v < BITS; ++v) out[v] = 0;
+  if (o < rows) {
+    for (int t = 0; t < 4; ++t) {
+      for (int s = 0; s < 8; ++s) {
+        const int kp = c * kChunk + 32 * t + 8 * q + s;
+        // col_order holds a permutation by the time this runs (the host
+        // checks it first); the clamp keeps any other value inside qweight
+        const int col = col_order ? min(max(col_order[kp], 0), n - 1) : kp;
+        const int64_t bit = static_cast<int64_t>(BITS) * col;
+        const int64_t wi = bit >> 5;
+        const int off = static_cast<int>(bit & 31);
+        uint64_t v = qweight[wi * rows + o];
+        if (off + BITS > 32) v |= static_cast<uint64_t>(qweight[(wi + 1) * rows + o]) << 32;
+        const uint32_t code = static_cast<uint32_t>(v >> off) & ((1u << BITS) - 1u);
+        const int dst = 8 * BITS * t + BITS * field_pos(BITS, s);
+        out[dst >> 5] |= code << (dst & 31);
+        if ((dst & 31) + BITS > 32) out[(dst >> 5) + 1] |= code >> (32 - (dst & 31));
+      }
+    }
+  }
+  uint32_t* dst = Q + id * BITS;
+  for (int v = 0; v < BITS; ++v) dst[v] = out[v];
+}
+
+// Scale/zero words in [T][Cs][16][spc] order: spc = 128/gs words (one per
+// group a 128-column chunk touches) for each chunk, or a single word per
+// output (Cs = spc = 1) for one group per row.
+__global__ __launch_bounds__(256) void pack_sz_kernel(const uint16_t* __restrict__ scales,
+                                                     const uint16_t* __restrict__ zeros, int rows, int G, int gs,
+                                                     int T, int Cs, uint32_t* __restrict__ SZ) {
+  const int spc = gs > 0 ? kChunk / gs : 1;
+  const int64_t id = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (id >= static_cast<int64_t>(T) * Cs * 16 * spc) return;
+  const int i = static_cast<int>(id % spc);
+  const int j = static_cast<int>((id / spc) & 15);
+  const int64_t tc = id / (16 * spc);
+  const int c = static_cast<int>(tc % Cs);
+  const int tile = static_cast<int>(tc / Cs);
+  const int g = gs > 0 ? c * spc + i : 0;
+  const int o = tile * 16 + j;
+  uint32_t v = 0;
+  if (o < rows && g < G) {
+    const int64_t src = static_cast<int64_t>(g) * rows + o;
+    v = static_cast<uint32_t>(scales[src]) | (static_cast<uint32_t>(zeros[src]) << 16);
+  }
+  SZ[id] = v;
+}
+
+// Activations in the packed column order (act-order layers): At[m, k] =
+// A[m, col_order[k]], row stride n.
+__global__ __launch_bounds__(256) void gather_cols_kernel(const uint16_t* __restrict__ A, int64_t lda,
+                                                         const int32_t* __restrict__ col_order, int M, int n,
+                                                         uint16_t* __restrict__ At) {
+  for (int m = blockIdx.y; m < M; m += gridDim.y) {
+    const uint16_t* row = A + static_cast<int64_t>(m) * lda;
+    uint16_t* out = At + static_cast<int64_t>(m) * n;
+    for (int k = blockIdx.x * 256 + threadIdx.x; k < n; k += gridDim.x * 256) out[k] = row[col_order[k]];
+  }
+}
+
+// ------------------------------------------------------------------ matmul side
+__device__ __forceinline__ h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
+
+// (x & mask) | 0x64006400 in one v_and_or_b32.  The compiler splits it into
+// two instructions, since gfx9 three-operand encodings take no literal: here
+// the mask is passed in a vector register and the exponent pattern in a
+// scalar one.  ALU only.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "s"(0x64006400u));
+  return r;
+}
+
+__device__ __forceinline__ h2 pk_fma(uint32_t x, h2 m, h2 c) { return __builtin_elementwise_fma(as_h2(x), m, c); }
+
+// The 8-bit-per-field step values of one lane: the lane's codes for step t as
+// the MFMA B operand, each half the exact integer code - z.  `zc[v]` holds
+// -(base_v + z) for the exponent bias base_v of half-pair v.
+template <int BITS>
+struct Unpack;
+
+template <>
+struct Unpack<4> {
+  static constexpr int kWords = 4;   // per lane per chunk
+  // pairs (0,4), (1,5) from bits 0..7 of each half; (2,6), (3,7) after >> 8
+  static constexpr float kBase[4] = {1024.f, 64.f, 1024.f, 64.f};
+  __device__ static __forceinline__ h8 step(const uint32_t* w, int t, const h2* zc) {
+    const uint32_t x = w[t];
+    const uint32_t y = x >> 8;
+    const h2 m1 = {(_Float16)1.0f, (_Float16)1.0f};
+    const h2 m16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 p0 = pk_fma(and_or(x, 0x000F000Fu), m1, zc[0]);
+    const h2 p1 = pk_fma(and_or(x, 0x00F000F0u), m16, zc[1]);
+    const h2 p2 = pk_fma(and_or(y, 0x000F000Fu), m1, zc[2]);
+    const h2 p3 = pk_fma(and_or(y, 0x00F000F0u), m16, zc[3]);
+    return h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  }
+};
+
+template <>
+struct Unpack<8> {
+  static constexpr int kWords = 8;
+  static constexpr float kBase[4] = {1024.f, 1024.f, 1024.f, 1024.f};
+  __device__ static __forceinline__ h8 step(const uint32_t* w, int t, const h2* zc) {
+    const uint32_t x0 = w[2 * t], x1 = w[2 * t + 1];
+    const h2 m1 = {(_Float16)1.0f, (_Float16)1.0f};
+    const h2 p0 = pk_fma(and_or(x0, 0x00FF00FFu), m1, zc[0]);
+    const h2 p1 = pk_fma(and_or((x0 >> 8), 0x00FF00FFu), m1, zc[0]);
+    const h2 p2 = pk_fma(and_or(x1, 0x00FF00FFu), m1, zc[0]);
+    const h2 p3 = pk_fma(and_or((x1 >> 8), 0x00FF00FFu), m1, zc[0]);
+    return h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  }
+};
+
+template <>
+struct Unpack<2> {
+  static constexpr int kWords = 2;
+  static constexpr float kBase[4] = {1024.f, 256.f, 64.f, 16.f};
+  __device__ static __forceinline__ h8 step(const uint32_t* w, int t, const h2* zc) {
+    // field t = half (t & 1) of word t >> 1; bytes 0/1 of that half go to
+    // bytes 0 and 2 of x, so each half of x holds four codes
+    const uint32_t word = w[t >> 1];
+    const uint32_t sel = (t & 1) ? 0x0C030C02u : 0x0C010C00u;
+    const uint32_t x = __builtin_amdgcn_perm(0u, word, sel);
+    const h2 m1 = {(_Float16)1.0f, (_Float16)1.0f};
+    const h2 m4 = {(_Float16)0.25f, (_Float16)0.25f};
+    const h2 m16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 m64 = {(_Float16)0.015625f, (_Float16)0.015625f};
+    const h2 p0 = pk_fma(and_or(x, 0x00030003u), m1, zc[0]);
+    const h2 p1 = pk_fma(and_or(x, 0x000C000Cu), m4, zc[1]);
+    const h2 p2 = pk_fma(and_or(x, 0x00300030u), m16, zc[2]);
+    const h2 p3 = pk_fma(and_or(x, 0x00C000C0u), m64, zc[3]);
+    return h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  }
+};
+
+template <>
+struct Unpack<3> {
+  static constexpr int kWords = 3;
+  static constexpr float kBase[4] = {1024.f, 128.f, 16.f, 1024.f};
+  __device__ static __forceinline__ h8 step(const uint32_t* w, int t, const h2* zc) {
+    // the 24-bit field of step t starts at bit 24t of the lane's 96-bit stream
+    uint32_t v;
+    if (t == 0) v = w[0];
+    else if (t == 1) v = __builtin_amdgcn_alignbit(w[1], w[0], 24);
+    else if (t == 2) v = __builtin_amdgcn_alignbit(w[2], w[1], 16);
+    else v = w[2] >> 8;
+    // fields 0..3 stay in bits 0..11, fields 4..7 move to bits 16..27
+    const uint32_t x = __builtin_amdgcn_ubfe(v, 0, 12) | ((v << 4) & 0x0FFF0000u);
+    const uint32_t y = x >> 9;
+    const h2 m1 = {(_Float16)1.0f, (_Float16)1.0f};
+    const h2 m8 = {(_Float16)0.125f, (_Float16)0.125f};
+    const h2 m64 = {(_Float16)0.015625f, (_Float16)0.015625f};
+    const h2 p0 = pk_fma(and_or(x, 0x00070007u), m1, zc[0]);
+    const h2 p1 = pk_fma(and_or(x, 0x00380038u), m8, zc[1]);
+    const h2 p2 = pk_fma(and_or(x, 0x01C001C0u), m64, zc[2]);
+    const h2 p3 = pk_fma(and_or(y, 0x00070007u), m1, zc[3]);
+    return h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  }
+};
+
+template <int BITS>
+__device__ __forceinline__ void load_chunk(const uint32_t* __restrict__ p, uint32_t* w) {
+  if constexpr (BITS == 4) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+  } else if constexpr (BITS == 8) {
+    const u32x4 a = reinterpret_cast<const u32x4*>(p)[0];
+    const u32x4 b = reinterpret_cast<const u32x4*>(p)[1];
+    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
+    w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
+  } else if constexpr (BITS == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    w[0] = p[0]; w[1] = p[1]; w[2] = p[2];
+  }
+}
+
+// Accumulator layout of the 16x16 f32 MFMA tiles: lane l, register r holds
+// row 4*(l/16) + r (token), column l%16 (output).
+__device__ __forceinline__ int acc_row(int lane, int r) { return 4 * (lane >> 4) + r; }
+
+// SPC: scale/zero words per chunk (128 / group size; 1 also for one group per
+// row, gs == 0).  A holds the activations in the packed (grouped) column order.
+// FULL: the slice's activations are staged in LDS once, before the loop
+// (decode sizes); else 1024-column windows are staged round by round.
+template <int BITS, int SPC, bool FULL>
+__global__ __launch_bounds__(kMmThreads) void dequant_matmul_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, int M, const uint32_t* __restrict__ Q,
+    const uint32_t* __restrict__ SZ, int rows, int n, int gs, void* __restrict__ Y, int ydt, int64_t ldy) {
+  using U = Unpack<BITS>;
+  extern __shared__ __align__(16) unsigned char mm_smem[];
+  _Float16* abuf = reinterpret_cast<_Float16*>(mm_smem);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = blockIdx.x;
+  const int m0 = blockIdx.y * kMTile;
+  const int ms = min(kMTile, M - m0);           // tokens of this slice
+  const int C = n / kChunk;
+  const int R = (C + kMmWaves - 1) / kMmWaves;  // rounds: one chunk per wave each
+  const int j = lane & 15, q = lane >> 4;
+  const int arow = min(j, ms - 1);              // rows >= ms repeat the last one; their outputs are dropped
+  const uint32_t* qbase = Q + (static_cast<int64_t>(tile) * C * 64 + lane) * U::kWords;
+  // scale/zero words per chunk and lane: one per group the chunk touches
+  const int Cs = gs > 0 ? C : 1;
+  const uint32_t* szbase = SZ + (static_cast<int64_t>(tile) * Cs * 16 + j) * SPC;
+  const int astride = FULL ? n + 8 : kWinStride;   // halves per staged row (16-byte pad)
+
+  // ---- codes and their scale/zero words: kAhead chunks in flight per wave.
+  // Chunk indexes past the last are clamped (loaded, never used), so the
+  // loads are unconditional and the compiler can count those in flight.
+  uint32_t breg[kAhead][U::kWords];
+  uint32_t sreg[kAhead][SPC];
+  auto b_load = [&](int c, int d) {
+    const int cl = min(c, C - 1);
+    load_chunk<BITS>(qbase + static_cast<int64_t>(cl) * 64 * U::kWords, breg[d]);
+    const uint32_t* sp = szbase + static_cast<int64_t>(gs > 0 ? cl : 0) * 16 * SPC;
+    if constexpr (SPC == 4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sp);
+      sreg[d][0] = v[0]; sreg[d][1] = v[1]; sreg[d][2] = v[2]; sreg[d][3] = v[3];
+    } else if constexpr (SPC == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(sp);
+      sreg[d][0] = v.x; sreg[d][1] = v.y;
+    } else {
+      sreg[d][0] = *sp;
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < kAhead; ++d) b_load(wave + kMmWaves * d, d);
+
+  // ---- windowed staging: window r (columns 1024 r ...) in pieces of 8 halves;
+  // piece p = tid + 512 v is token p / 128, columns 8 (p % 128).  Whether a
+  // piece exists is uniform per wave (pieces is a multiple of 64); columns
+  // past n are clamped (those LDS columns belong to chunks no wave visits).
+  // Two register sets, so a window's loads never wait for the previous one.
+  const int pieces = ms * (kWin / 8);
+  uint32_t areg[2][4][4];
+  auto a_load = [&](int r, int set) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if (wave * 64 + v * kMmThreads < pieces) {
+        const int p = tid + v * kMmThreads;
+        const int m = p / (kWin / 8), kp = p % (kWin / 8);
+        const int k = min(r * kWin + 8 * kp, n - 8);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(m0 + m) * lda + k);
+        areg[set][v][0] = x[0]; areg[set][v][1] = x[1]; areg[set][v][2] = x[2]; areg[set][v][3] = x[3];
+      }
+    }
+  };
+  auto a_store = [&](int buf, int set) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if (wave * 64 + v * kMmThreads < pieces) {
+        const int p = tid + v * kMmThreads;
+        const int m = p / (kWin / 8), kp = p % (kWin / 8);
+        u32x4 x = {areg[set][v][0], areg[set][v][1], areg[set][v][2], areg[set][v][3]};
+        *reinterpret_cast<u32x4*>(abuf + (buf * ms + m) * kWinStride + 8 * kp) = x;
+      }
+    }
+  };
+
+  if constexpr (FULL) {
+    // every column of the slice's tokens, four pieces per thread at a time
+    const int per_row = n / 8;
+    const int total = ms * per_row;
+    for (int p0 = 0; p0 < total; p0 += 4 * kMmThreads) {
+      u32x4 x[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int p = min(p0 + v * kMmThreads + tid, total - 1);
+        const int m = p / per_row, kp = p % per_row;
+        x[v] = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(m0 + m) * lda + 8 * kp);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int p = p0 + v * kMmThreads + tid;
+        if (p < total) {
+          const int m = p / per_row, kp = p % per_row;
+          *reinterpret_cast<u32x4*>(abuf + m * astride + 8 * kp) = x[v];
+        }
+      }
+    }
+  } else {
+    a_load(0, 0);
+    a_store(0, 0);
+  }
+  // Everything issued so far has landed (the staging stores needed their
+  // loads, which were issued after the code prefetches).  Saying so tells the
+  // compiler that no load is in flight at the top of the loop, so inside it
+  // it waits only for the chunk it is about to use.
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  lds_barrier();
+
+  f4 yacc = {0.f, 0.f, 0.f, 0.f};
+  f4 gacc = {0.f, 0.f, 0.f, 0.f};
+  // group boundaries: gs is 32, 64 or 128 (a power of two), or one group per row
+  const int gmask = gs > 0 ? gs - 1 : 0x7fffffff;
+
+  // One chunk: four MFMA steps over the prefetched codes of slot d.  Rounds
+  // past the last chunk of a wave run on the clamped chunk with their result
+  // dropped (live false), so that every round is the same straight-line code.
+  auto chunk = [&](int d, int c, bool live, const _Float16* ap) {
+    h2 zc[4];
+    float s = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int k = c * kChunk + 32 * t;
+      if (t == 0 || (k & gmask) == 0) {
+        const uint32_t sz = sreg[d][(t * SPC) >> 2];
+        s = live ? half_bits_to_float(static_cast<uint16_t>(sz & 0xFFFFu)) : 0.f;
+        const _Float16 z = __builtin_bit_cast(_Float16, static_cast<uint16_t>(sz >> 16));
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const _Float16 c0 = -(static_cast<_Float16>(U::kBase[v]) + z);
+          zc[v] = h2{c0, c0};
+        }
+      }
+      const h8 b = U::step(breg[d], t, zc);
+      const h8 a = *reinterpret_cast<const h8*>(ap + 32 * t);
+      gacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, gacc, 0, 0, 0);
+      // a group ends here, or continues in another wave's chunk: scale this
+      // wave's partial sum of it now (exact scaling, one fp32 rounding)
+      if (t == 3 || ((k + 32) & gmask) == 0) {
+        yacc += s * gacc;
+        gacc = f4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+
+  const int Rp = (R + kAhead - 1) / kAhead * kAhead;
+  for (int r0 = 0; r0 < Rp; r0 += kAhead) {
+#pragma unroll
+    for (int d = 0; d < kAhead; ++d) {
+      const int r = r0 + d;
+      const int c = wave + kMmWaves * r;
+      const bool live = c < C;
+      const int cc = live ? c : C - 1;
+      if constexpr (FULL) {
+        chunk(d, cc, live, abuf + arow * astride + cc * kChunk + 8 * q);
+        b_load(c + kMmWaves * kAhead, d);
+      } else {
+        // window r + 1 goes to buffer and register set (r + 1) & 1 = (d + 1) & 1
+        if (r + 1 < R) a_load(r + 1, (d + 1) & 1);
+        const int rc = cc / kMmWaves;   // window holding chunk cc (r when live)
+        chunk(d, cc, live, abuf + ((rc & 1) * ms + arow) * kWinStride + (cc - kMmWaves * rc) * kChunk + 8 * q);
+        b_load(c + kMmWaves * kAhead, d);
+        if (r + 1 < R) a_store((d + 1) & 1, (d + 1) & 1);
+        lds_barrier();
+      }
+    }
+  }
+
+  // ---- sum the 8 waves' partial tiles and store
+  float* red = reinterpret_cast<float*>(mm_smem);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[(wave * 64 + lane) * 4 + r] = yacc[r];
+  __syncthreads();
+  if (tid < kMTile * 16) {
+    const int mm = tid >> 4, o_in = tid & 15;
+    const int l = 16 * (mm >> 2) + o_in, r = mm & 3;   // inverse of acc_row
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < kMmWaves; ++v) sum += red[(v * 64 + l) * 4 + r];
+    const int o = tile * 16 + o_in;
+    if (mm < ms && o < rows) {
+      const int64_t idx = static_cast<int64_t>(m0 + mm) * ldy + o;
+      if (ydt == DT_FP32) static_cast<float*>(Y)[idx] = sum;
+      else static_cast<uint16_t*>(Y)[idx] = float_to_half_bits(sum);
+    }
+  }
+}
+
+template <int BITS, int SPC, bool FULL>
+hipError_t launch_mm_v(const uint16_t* A, int64_t lda, int M, const uint32_t* Q, const uint32_t* SZ, int rows,
+                       int n, int gs, void* Y, int ydt, int64_t ldy, size_t lds, hipStream_t s) {
+  auto kern = dequant_matmul_kernel<BITS, SPC, FULL>;
+  static bool attr_set = false;   // per instantiation; idempotent if raced
+  if (!attr_set) {
+    const size_t most = FULL ? kFullLds : static_cast<size_t>(2) * kMTile * kWinStride * sizeof(_Float16);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(most));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int T = (rows + 15) / 16;
+  dim3 grid(T, (M + kMTile - 1) / kMTile);
+  hipLaunchKernelGGL(kern, grid, dim3(kMmThreads), lds, s, A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy);
+  return hipGetLastError();
+}
+
+template <int BITS, int SPC>
+hipError_t launch_mm(const uint16_t* A, int64_t lda, int M, const uint32_t* Q, const uint32_t* SZ, int rows, int n,
+                     int gs, void* Y, int ydt, int64_t ldy, hipStream_t s) {
+  const int ms = M < kMTile ? M : kMTile;
+  const size_t red = static_cast<size_t>(kMmWaves) * 64 * 4 * sizeof(float);   // final sum of the waves
+  const size_t full = static_cast<size_t>(ms) * (n + 8) * sizeof(_Float16);
+  if (full <= kFullLds)
+    return launch_mm_v<BITS, SPC, true>(A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy, full < red ? red : full, s);
+  size_t win = static_cast<size_t>(2) * ms * kWinStride * sizeof(_Float16);
+  return launch_mm_v<BITS, SPC, false>(A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy, win < red ? red : win, s);
+}
+
+}  // namespace
+
+size_t matmul_packed_bytes(int64_t rows, int64_t n, int bits, int group_size) {
+  const int64_t T = (rows + 15) / 16;
+  const int64_t C = n / kChunk;
+  const int64_t G = group_size > 0 ? n / group_size : 1;
+  return kHeader + align256(static_cast<size_t>(T * C * 64 * bits) * 4) + static_cast<size_t>(T * G * 16) * 4;
+}
+
+hipError_t launch_matmul_pack(const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                              const int32_t* g_idx, int64_t rows, int64_t n, int bits, int group_size,
+                              void* packed, int32_t* col_order, uint32_t* flags_host, hipStream_t s) {
+  const int gs = group_size > 0 ? group_size : static_cast<int>(n);
+  const int G = static_cast<int>(n / gs);
+  const int T = static_cast<int>((rows + 15) / 16);
+  const int C = static_cast<int>(n / kChunk);
+  unsigned char* base = static_cast<unsigned char*>(packed);
+  uint32_t* flags = reinterpret_cast<uint32_t*>(base);
+  uint32_t* Q = reinterpret_cast<uint32_t*>(base + kHeader);
+  uint32_t* SZ = reinterpret_cast<uint32_t*>(base + kHeader + align256(static_cast<size_t>(T) * C * 64 * bits * 4));
+  hipError_t e = zero_words(flags, 1, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(group_order_kernel, dim3(G), dim3(256), 0, s, g_idx, static_cast<int>(n), gs, col_order, flags);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // the order must be a valid grouping before the codes are gathered through it
+  if ((e = hipMemcpyAsync(flags_host, flags, sizeof(uint32_t), hipMemcpyDeviceToHost, s)) != hipSuccess) return e;
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+  if (*flags_host & 1u) return hipSuccess;
+  const int64_t qthreads = static_cast<int64_t>(T) * C * 64;
+  const unsigned qblocks = static_cast<unsigned>((qthreads + 255) / 256);
+  const uint32_t* qw = reinterpret_cast<const uint32_t*>(qweight);
+  const int r32 = static_cast<int>(rows), n32 = static_cast<int>(n);
+  switch (bits) {
+    case 2: hipLaunchKernelGGL(pack_codes_kernel<2>, dim3(qblocks), dim3(256), 0, s, qw, col_order, r32, n32, T, Q); break;
+    case 3: hipLaunchKernelGGL(pack_codes_kernel<3>, dim3(qblocks), dim3(256), 0, s, qw, col_order, r32, n32, T, Q); break;
+    case 4: hipLaunchKernelGGL(pack_codes_kernel<4>, dim3(qblocks), dim3(256), 0, s, qw, col_order, r32, n32, T, Q); break;
+    case 8: hipLaunchKernelGGL(pack_codes_kernel<8>, dim3(qblocks), dim3(256), 0, s, qw, col_order, r32, n32, T, Q); break;
+    default: return hipErrorInvalidValue;
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int gsk = group_size > 0 ? group_size : 0;
+  const int Cs = group_size > 0 ? C : 1;
+  const int64_t zthreads = static_cast<int64_t>(T) * G * 16;   // = T * Cs * 16 * spc
+  hipLaunchKernelGGL(pack_sz_kernel, dim3(static_cast<unsigned>((zthreads + 255) / 256)), dim3(256), 0, s, scales,
+                     zeros, r32, G, gsk, T, Cs, SZ);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return hipStreamSynchronize(s);
+}
+
+size_t matmul_workspace_bytes(int64_t M, int64_t n) { return align256(static_cast<size_t>(M * n) * 2); }
+
+hipError_t launch_matmul(const void* A, int64_t M, int64_t lda, const void* packed, const int32_t* col_order,
+                         int64_t rows, int64_t n, int bits, int group_size, void* Y, int ydt, int64_t ldy,
+                         void* ws, hipStream_t s) {
+  const int gs = group_size > 0 ? group_size : 0;
+  const int T = static_cast<int>((rows + 15) / 16);
+  const int C = static_cast<int>(n / kChunk);
+  const unsigned char* base = static_cast<const unsigned char*>(packed);
+  const uint32_t* Q = reinterpret_cast<const uint32_t*>(base + kHeader);
+  const uint32_t* SZ =
+      reinterpret_cast<const uint32_t*>(base + kHeader + align256(static_cast<size_t>(T) * C * 64 * bits * 4));
+  const uint16_t* a = static_cast<const uint16_t*>(A);
+  if (col_order) {
+    uint16_t* at = static_cast<uint16_t*>(ws);
+    unsigned gx = static_cast<unsigned>((n + 255) / 256);
+    if (gx > 64) gx = 64;
+    const unsigned gy = static_cast<unsigned>(M < 1024 ? M : 1024);
+    hipLaunchKernelGGL(gather_cols_kernel, dim3(gx, gy), dim3(256), 0, s, a, lda, col_order, static_cast<int>(M),
+                       static_cast<int>(n), at);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a = at;
+    lda = n;
+  }
+  const int m = static_cast<int>(M), r = static_cast<int>(rows), nn = static_cast<int>(n);
+#define GPTQ_MM(B)                                                                                    \
+  if (bits == B) {                                                                                    \
+    if (gs == 32) return launch_mm<B, 4>(a, lda, m, Q, SZ, r, nn, gs, Y, ydt, ldy, s);     \
+    if (gs == 64) return launch_mm<B, 2>(a, lda, m, Q, SZ, r, nn, gs, Y, ydt, ldy, s);     \
+    return launch_mm<B, 1>(a, lda, m, Q, SZ, r, nn, gs, Y, ydt, ldy, s);                   \
+  }
+  GPTQ_MM(2)
+  GPTQ_MM(3)
+  GPTQ_MM(4)
+  GPTQ_MM(8)
+#undef GPTQ_MM
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gptq

@@ -125,14 +125,6 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
   return __longlong_as_double((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// Barrier for exchanges through LDS only: waits for this wave's LDS accesses,
-// not for its global loads, which may stay in flight across it (the
-// column-update operands are prefetched across the whole factorization).
-// The memory clobber keeps the compiler from moving memory accesses across.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 __device__ __forceinline__ double rsqrt_refined(double x) {
   double r = __builtin_amdgcn_rsq(x);
   const double h = 0.5 * x;

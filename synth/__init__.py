@@ -256,3 +256,47 @@ def activations(wl: Workload, xset: int = 0) -> np.ndarray:
 
 def get(name: str) -> Workload:
     return WORKLOADS[name]
+
+
+# ----------------------------------------------------------------------------
+# Inputs of the dequantizing matmul: a quantized layer in the quantizer's
+# output shapes and fp16 decode-time activations
+# ----------------------------------------------------------------------------
+def quantized_layer(seed: int, rows: int, n: int, bits: int, group_size: int, act_order: bool = False):
+    """Random codes int64 [rows, n], fp16 scales and integer-valued fp16 zero
+    points [G, rows] (G = n / group_size, 1 for group_size -1) and the group
+    index int32 [n] of each column.
+
+    Scales are drawn around what a 4-bit grid over N(0, 0.02^2) weights in
+    groups of 128 gives (range about 6 sigma over 2^bits - 1 steps).  Without
+    act_order the groups are runs of consecutive columns; with it they are
+    spread over the columns by a random permutation, as a column order that
+    visits columns by decreasing activation leaves them."""
+    g = _ss(seed, 300, rows, n, bits, max(group_size, 0))
+    gs = n if group_size <= 0 else group_size
+    G = n // gs
+    maxq = (1 << bits) - 1
+    codes = g.integers(0, maxq + 1, size=(rows, n), dtype=np.int64)
+    scales = (g.uniform(0.5, 1.5, size=(G, rows)) * 0.02 * 6.0 / maxq).astype(np.float16)
+    zeros = g.integers(0, maxq + 1, size=(G, rows)).astype(np.float16)
+    pos = np.arange(n)
+    if act_order:
+        order = g.permutation(n)                     # column visited at position j
+        g_idx = np.empty(n, dtype=np.int32)
+        g_idx[order] = (pos // gs).astype(np.int32)
+    else:
+        g_idx = (pos // gs).astype(np.int32)
+    return codes, scales, zeros, g_idx
+
+
+def decode_activations_raw(seed: int, tokens: int, n: int, outlier_frac: float = 0.01,
+                           outlier_scale: float = 20.0) -> np.ndarray:
+    """fp16 bits uint16 [tokens, n]: N(0, 1) entries with a fixed set of outlier
+    channels (outlier_frac of them) scaled by outlier_scale, the input of a
+    linear layer at decode time."""
+    g = _ss(seed, 400, tokens, n)
+    x = g.standard_normal((tokens, n))
+    k = int(round(outlier_frac * n))
+    if k:
+        x[:, g.choice(n, size=k, replace=False)] *= outlier_scale
+    return x.astype(np.float16).view(np.uint16)

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(g):
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 15, names
     assert set(names) == set(g.EXPORTS)
     L = g.lib()
     for n in names:
@@ -104,6 +104,38 @@ def test_argument_validation(g):
                              FAKE, 1 << 30, None) == g.GPTQ_ERR_INVALID_ARG
     assert L.gptq_layer_loss(FAKE, 256, FAKE, 0, 8, 256, FAKE, FAKE, FAKE, FAKE, _cfg(), ctypes.byref(rel),
                              FAKE, 8, None) == g.GPTQ_ERR_WORKSPACE
+
+
+def test_matmul_queries_and_validation(g):
+    L = g.lib()
+    # header + codes ([tiles][chunks][64 lanes][bits words]) + scale/zero words
+    assert g.gptq_matmul_packed_bytes(4096, 4096, 4, 128) == 256 + 256 * 32 * 64 * 4 * 4 + 256 * 32 * 16 * 4
+    assert g.gptq_matmul_packed_bytes(50, 384, 3, 32) == 256 + 4 * 3 * 64 * 3 * 4 + 4 * 12 * 16 * 4
+    assert g.gptq_matmul_packed_bytes(16, 128, 8, -1) == 256 + 1 * 1 * 64 * 8 * 4 + 16 * 4
+    assert g.gptq_matmul_packed_bytes(16, 200, 4, 128) == 0      # n not a multiple of 128
+    assert g.gptq_matmul_packed_bytes(16, 256, 5, 128) == 0
+    assert g.gptq_matmul_workspace_bytes(1, 4096, False) == 0
+    assert g.gptq_matmul_workspace_bytes(3, 4096, True) == 3 * 4096 * 2
+    i32 = ctypes.c_int32(0)
+    pk = lambda rows=16, n=256, bits=4, gs=128, nbytes=1 << 30, order=FAKE: L.gptq_matmul_pack(
+        FAKE, FAKE, FAKE, FAKE, rows, n, bits, gs, FAKE, nbytes, order, ctypes.byref(i32), None)
+    assert pk(bits=5) == g.GPTQ_ERR_UNSUPPORTED
+    assert pk(gs=16) == g.GPTQ_ERR_UNSUPPORTED
+    assert pk(n=192, gs=64) == g.GPTQ_ERR_UNSUPPORTED
+    assert pk(rows=0) == g.GPTQ_ERR_INVALID_ARG
+    assert pk(order=None) == g.GPTQ_ERR_INVALID_ARG
+    assert pk(nbytes=100) == g.GPTQ_ERR_WORKSPACE
+    mm = lambda adt=g.GPTQ_FP16, M=1, lda=256, ydt=g.GPTQ_FP16, ldy=16, order=None, ws=None, wsb=0, A=FAKE: \
+        L.gptq_matmul(A, adt, M, lda, FAKE, order, 16, 256, 4, 128, FAKE, ydt, ldy, ws, wsb, None)
+    assert mm(adt=g.GPTQ_BF16) == g.GPTQ_ERR_UNSUPPORTED
+    assert mm(ydt=g.GPTQ_BF16) == g.GPTQ_ERR_UNSUPPORTED
+    assert mm(M=-1) == g.GPTQ_ERR_INVALID_ARG
+    assert mm(lda=128) == g.GPTQ_ERR_INVALID_ARG
+    assert mm(ldy=8) == g.GPTQ_ERR_INVALID_ARG
+    assert mm(lda=260) == g.GPTQ_ERR_INVALID_ARG                  # rows of A must stay 16-byte aligned
+    assert mm(A=ctypes.c_void_p(0x1002)) == g.GPTQ_ERR_INVALID_ARG
+    assert mm(order=FAKE) == g.GPTQ_ERR_WORKSPACE                  # act-order needs the gather workspace
+    assert mm(M=0, A=None) == g.GPTQ_OK                            # no tokens: nothing to do
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, g):

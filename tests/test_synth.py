@@ -39,3 +39,22 @@ def test_toy_is_fp32_and_shaped():
     x = synth.activations(wl)
     assert x.dtype == np.float32 and x.shape == (2048, 256)
     assert synth.weights(wl).shape == (256, 256)
+
+
+def test_matmul_inputs_are_deterministic_and_well_formed():
+    for act in (False, True):
+        codes, s, z, g_idx = synth.quantized_layer(3, 20, 256, 4, 64, act_order=act)
+        codes2, s2, z2, g2 = synth.quantized_layer(3, 20, 256, 4, 64, act_order=act)
+        assert np.array_equal(codes, codes2) and np.array_equal(s, s2) and np.array_equal(g_idx, g2)
+        assert codes.shape == (20, 256) and codes.min() >= 0 and codes.max() <= 15
+        assert s.shape == z.shape == (4, 20) and s.dtype == z.dtype == np.float16
+        assert np.all(s > 0) and np.array_equal(z, np.round(z))
+        assert np.array_equal(np.bincount(g_idx, minlength=4), [64] * 4)
+        assert act == (not np.array_equal(g_idx, np.arange(256) // 64))
+    _, s, _, g_idx = synth.quantized_layer(1, 4, 256, 3, -1)
+    assert s.shape == (1, 4) and not g_idx.any()
+    a = synth.decode_activations_raw(5, 3, 1000)
+    assert a.dtype == np.uint16 and a.shape == (3, 1000)
+    assert np.array_equal(a, synth.decode_activations_raw(5, 3, 1000))
+    v = a.view(np.float16).astype(np.float64)
+    assert np.all(np.isfinite(v)) and (np.abs(v) > 10).any(axis=0).sum() >= 5
