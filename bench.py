@@ -14,8 +14,14 @@ solve-only rate (prepare + quantize, H given), per-stage times, the roofline of
 the Hessian kernel measured live with HIP events on its stream, and the
 float64 CPU oracle timed on a bounded sample of the same workload.
 
+The line also carries "dequant_matmul": the decode-time product with the
+packed layers (one token, and a batch of 16) through every linear of a
+32-block Llama-2-7B-shaped stack at 4-bit g128, replayed as a graph, with its
+HBM roofline.
+
 Usage: python bench.py [--steps K] [--warmup W] [--workload attn4096]
-       python bench.py --pmc-probe   (short run for rocprofv3 --pmc counter passes)
+       python bench.py --matmul-only  (only the dequant_matmul part, for profiling)
+       python bench.py --pmc-probe    (short run for rocprofv3 --pmc counter passes)
 """
 from __future__ import annotations
 
@@ -114,6 +120,81 @@ def cpu_baseline(wl, w_raw, x_raw):
     }
 
 
+# Llama-2-7B block linears with q/k/v and gate/up fused, as a decoder serves them
+MM_SHAPES = (("qkv_proj", 12288, 4096), ("o_proj", 4096, 4096), ("gate_up_proj", 22016, 4096),
+             ("down_proj", 4096, 11008))
+MM_BLOCKS = 32
+MM_BITS, MM_GS = 4, 128
+
+
+def dequant_matmul_bench(g, torch, replays: int = 20, token_counts=(1, 16)):
+    """Decode through all linears of MM_BLOCKS blocks (each block its own copy
+    of the packed weights, 3.4 GB in all, so nothing is served from cache),
+    captured once as a graph of 4 * MM_BLOCKS launches and replayed."""
+    import numpy as np
+    import synth
+    dev = torch.device("cuda")
+    base = []
+    for li, (name, rows, n) in enumerate(MM_SHAPES):
+        qw = torch.from_numpy(synth.random_qweight(31 + li, rows, n, MM_BITS).view(np.int32)).to(dev)
+        sc, ze, gi = synth.group_params(31 + li, rows, n, MM_BITS, MM_GS)
+        layer = g.PackedLayer(qw, torch.from_numpy(sc).to(dev), torch.from_numpy(ze).to(dev),
+                              torch.from_numpy(gi).to(dev), MM_BITS, MM_GS)
+        assert layer.col_order is None
+        base.append(layer)
+        del qw
+    packed = [[base[li].packed if b == 0 else base[li].packed.clone() for li in range(len(MM_SHAPES))]
+              for b in range(MM_BLOCKS)]
+    torch.cuda.synchronize()
+    weight_bytes = sum(int(p.numel()) - 256 for blk in packed for p in blk)
+    out = {"workload": (f"decode through the q/k/v (fused), o, gate/up (fused) and down projections of "
+                        f"{MM_BLOCKS} Llama-2-7B-shaped blocks, {MM_BITS}-bit asym g{MM_GS}, desc_act off, "
+                        f"fp16 activations and outputs; one graph replay = {4 * MM_BLOCKS} launches"),
+           "packed_weight_bytes": weight_bytes, "by_tokens": {}}
+    for M in token_counts:
+        A = [torch.from_numpy(synth.decode_activations_raw(41 + li, M, n).view(np.float16)).to(dev)
+             for li, (_, rows, n) in enumerate(MM_SHAPES)]
+        Y = [torch.empty((M, rows), dtype=torch.float16, device=dev) for (_, rows, n) in MM_SHAPES]
+
+        def run():
+            for b in range(MM_BLOCKS):
+                for li, (_, rows, n) in enumerate(MM_SHAPES):
+                    g.gptq_matmul(A[li], packed[b][li], None, rows, n, MM_BITS, MM_GS, Y[li])
+
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            run()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / replays
+        act_bytes = MM_BLOCKS * sum(M * n * 2 + M * rows * 2 for (_, rows, n) in MM_SHAPES)
+        gbs = (weight_bytes + act_bytes) / (ms * 1e-3) / 1e9
+        out["by_tokens"][str(M)] = {"ms_per_step": ms, "tokens_per_s": M / (ms * 1e-3), "GB_per_s": gbs,
+                                    "algorithmic_bytes_per_step": weight_bytes + act_bytes}
+        _log(f"dequant matmul, {M} token(s): {ms:.4f} ms per pass, {gbs:.0f} GB/s")
+        del graph
+    one = out["by_tokens"][str(token_counts[0])]
+    out["roofline"] = {"kernel": "dequant_matmul_kernel<4,1,full> (one token)", "bound": "hbm",
+                       "achieved": one["GB_per_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                       "frac": one["GB_per_s"] / PEAK_HBM_GBS, "traffic": None,
+                       "note": "algorithmic bytes (packed codes, scale/zero words, activations, outputs) "
+                               "over the graph replay time, inter-kernel gaps included"}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +209,8 @@ def main() -> int:
     ap.add_argument("--sym", type=int, default=None, choices=[0, 1, 2])
     ap.add_argument("--desc-act", type=int, default=None, choices=[0, 1])
     ap.add_argument("--damp", type=float, default=None)
+    ap.add_argument("--matmul-only", action="store_true", help="only the dequant_matmul measurement")
+    ap.add_argument("--no-matmul", action="store_true", help="skip the dequant_matmul measurement")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="copy 1 GiB (counter calibration) then 3 Hessian launches; no timing output")
     args = ap.parse_args()
@@ -141,6 +224,11 @@ def main() -> int:
     import torch
     import post_weight_quantization_13_amd as g
     import synth
+
+    if args.matmul_only:
+        torch.cuda.set_device(0)
+        print(json.dumps({"dequant_matmul": dequant_matmul_bench(g, torch)}), flush=True)
+        return 0
 
     wl = synth.get(args.workload)
     over = {k: v for k, v in (("bits", args.bits), ("group_size", args.group_size), ("sym", args.sym),
@@ -236,6 +324,10 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if not args.no_matmul:
+        del X, W, H, U, ws_h, ws_p, ws_q
+        torch.cuda.empty_cache()
+        out["dequant_matmul"] = dequant_matmul_bench(g, torch)
     if not args.no_cpu_baseline:
         _log("timing the float64 oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(wl, w_raw, x_raw)

@@ -212,7 +212,8 @@ gptq_status gptq_layer_loss(const double* H, int64_t n, const void* W, gptq_dtyp
  * tokens the weights are read once per 16 (the kernel targets decoding).
  * Does not synchronize, allocate or clear memory, so it can be captured in a
  * graph; calls that share a workspace must not overlap.  M == 0 is a no-op.  Deterministic.
- * Supported: bits 2, 3, 4, 8; group_size 32, 64, 128, -1; n a multiple of 128.
+ * Supported: bits 2, 3, 4, 8; group_size 32, 64, 128, -1; n a multiple of 128
+ * with at most 1528 groups per row (n <= 48896 at group_size 32, 195584 at 128).
  * ------------------------------------------------------------------------- */
 size_t gptq_matmul_packed_bytes(int64_t rows, int64_t n, int32_t bits, int32_t group_size);
 gptq_status gptq_matmul_pack(const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,

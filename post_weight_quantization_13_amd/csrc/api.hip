@@ -28,6 +28,7 @@ hipError_t launch_layer_loss(const double* H, int64_t n, const void* W, int wdt,
                              const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                              const int32_t* g_idx, int bits, double* rel_host, void* ws, hipStream_t s);
 size_t matmul_packed_bytes(int64_t rows, int64_t n, int bits, int group_size);
+bool matmul_fits(int64_t n, int group_size);
 hipError_t launch_matmul_pack(const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                               const int32_t* g_idx, int64_t rows, int64_t n, int bits, int group_size,
                               void* packed, int32_t* col_order, uint32_t* flags_host, hipStream_t s);
@@ -91,6 +92,9 @@ gptq_status check_matmul_format(int64_t rows, int64_t n, int32_t bits, int32_t g
     return fail(GPTQ_ERR_UNSUPPORTED, "n=%lld must be a positive multiple of 128 up to %lld", (long long)n,
                 (long long)kMaxDim);
   if (rows < 1 || rows > (int64_t)1 << 30) return fail(GPTQ_ERR_INVALID_ARG, "rows=%lld out of range", (long long)rows);
+  if (!gptq::matmul_fits(n, group_size))
+    return fail(GPTQ_ERR_UNSUPPORTED, "n=%lld has too many groups of %d for the matmul (at most 1528)", (long long)n,
+                group_size);
   return GPTQ_OK;
 }
 

@@ -38,23 +38,27 @@
 //                      Cs = C; for one group per row Cs = spc = 1.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace gptq {
 namespace {
 
-constexpr int kMmWaves = 8;          // waves per workgroup
-constexpr int kMmThreads = kMmWaves * 64;
+constexpr int kWinWaves = 8;         // waves per workgroup of the windowed variant
 constexpr int kChunk = 128;          // columns per chunk (four 32-column MFMA steps)
-constexpr int kWin = kMmWaves * kChunk;  // columns per LDS window (one chunk per wave)
+constexpr int kWin = kWinWaves * kChunk;  // columns per LDS window (one chunk per wave)
 constexpr int kWinStride = kWin + 8;     // halves per staged row (16-byte pad against bank conflicts)
 constexpr int kMTile = 16;           // tokens per MFMA tile
 constexpr int kAhead = 4;            // chunks of codes each wave keeps in flight (even)
 constexpr size_t kFullLds = 80 * 1024;  // largest slice of activations staged whole
+constexpr int kFullPieces = 8;          // ... in at most this many 16-byte pieces per thread
+constexpr size_t kWinLds = 160 * 1024;  // windowed variant: two windows of 16 tokens and the scale/zero words
 constexpr size_t kHeader = 256;
 // s_waitcnt immediate for vmcnt(0) with the other counters left alone (gfx9
 // layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kVmcntZero = 0x0F70;
+constexpr int kWaveSlots = 256 * 32;   // waves the chip holds at once (256 CUs x 32)
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -291,21 +295,26 @@ struct Unpack<3> {
   }
 };
 
+// The codes are read once: non-temporal loads keep them from displacing the
+// activations and scale/zero words in the caches.
 template <int BITS>
 __device__ __forceinline__ void load_chunk(const uint32_t* __restrict__ p, uint32_t* w) {
   if constexpr (BITS == 4) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
   } else if constexpr (BITS == 8) {
-    const u32x4 a = reinterpret_cast<const u32x4*>(p)[0];
-    const u32x4 b = reinterpret_cast<const u32x4*>(p)[1];
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + 1);
     w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
     w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
   } else if constexpr (BITS == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    w[0] = v.x; w[1] = v.y;
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    w[0] = v[0]; w[1] = v[1];
   } else {
-    w[0] = p[0]; w[1] = p[1]; w[2] = p[2];
+    w[0] = __builtin_nontemporal_load(p);
+    w[1] = __builtin_nontemporal_load(p + 1);
+    w[2] = __builtin_nontemporal_load(p + 2);
   }
 }
 
@@ -316,9 +325,10 @@ __device__ __forceinline__ int acc_row(int lane, int r) { return 4 * (lane >> 4)
 // SPC: scale/zero words per chunk (128 / group size; 1 also for one group per
 // row, gs == 0).  A holds the activations in the packed (grouped) column order.
 // FULL: the slice's activations are staged in LDS once, before the loop
-// (decode sizes); else 1024-column windows are staged round by round.
-template <int BITS, int SPC, bool FULL>
-__global__ __launch_bounds__(kMmThreads) void dequant_matmul_kernel(
+// (decode sizes); else 1024-column windows are staged round by round (NW = 8).
+// NW: waves per workgroup, all on the same 16 outputs, splitting the chunks.
+template <int BITS, int SPC, bool FULL, int NW>
+__global__ __launch_bounds__(NW * 64) void dequant_matmul_kernel(
     const uint16_t* __restrict__ A, int64_t lda, int M, const uint32_t* __restrict__ Q,
     const uint32_t* __restrict__ SZ, int rows, int n, int gs, void* __restrict__ Y, int ydt, int64_t ldy) {
   using U = Unpack<BITS>;
@@ -330,37 +340,27 @@ __global__ __launch_bounds__(kMmThreads) void dequant_matmul_kernel(
   const int m0 = blockIdx.y * kMTile;
   const int ms = min(kMTile, M - m0);           // tokens of this slice
   const int C = n / kChunk;
-  const int R = (C + kMmWaves - 1) / kMmWaves;  // rounds: one chunk per wave each
+  static_assert(FULL || NW == kWinWaves, "windowed staging assumes one window chunk per wave");
+  constexpr int kThreads = NW * 64;
+  const int R = (C + NW - 1) / NW;  // rounds: one chunk per wave each
   const int j = lane & 15, q = lane >> 4;
   const int arow = min(j, ms - 1);              // rows >= ms repeat the last one; their outputs are dropped
   const uint32_t* qbase = Q + (static_cast<int64_t>(tile) * C * 64 + lane) * U::kWords;
-  // scale/zero words per chunk and lane: one per group the chunk touches
+  // The tile's scale/zero words ([Cs][16][SPC], G * 16 in all) are staged in
+  // LDS after the activations.
   const int Cs = gs > 0 ? C : 1;
-  const uint32_t* szbase = SZ + (static_cast<int64_t>(tile) * Cs * 16 + j) * SPC;
+  const int szw = Cs * 16 * SPC;
+  const uint32_t* sztile = SZ + static_cast<int64_t>(tile) * szw;
   const int astride = FULL ? n + 8 : kWinStride;   // halves per staged row (16-byte pad)
+  uint32_t* szs = reinterpret_cast<uint32_t*>(abuf + (FULL ? ms * astride : 2 * ms * kWinStride));
 
-  // ---- codes and their scale/zero words: kAhead chunks in flight per wave.
-  // Chunk indexes past the last are clamped (loaded, never used), so the
-  // loads are unconditional and the compiler can count those in flight.
+  // ---- codes: kAhead chunks in flight per wave.  Chunk indexes past the
+  // last are clamped (loaded, never used), so the loop issues exactly one
+  // unconditional load per round and the compiler can count those in flight.
   uint32_t breg[kAhead][U::kWords];
-  uint32_t sreg[kAhead][SPC];
   auto b_load = [&](int c, int d) {
-    const int cl = min(c, C - 1);
-    load_chunk<BITS>(qbase + static_cast<int64_t>(cl) * 64 * U::kWords, breg[d]);
-    const uint32_t* sp = szbase + static_cast<int64_t>(gs > 0 ? cl : 0) * 16 * SPC;
-    if constexpr (SPC == 4) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(sp);
-      sreg[d][0] = v[0]; sreg[d][1] = v[1]; sreg[d][2] = v[2]; sreg[d][3] = v[3];
-    } else if constexpr (SPC == 2) {
-      const uint2 v = *reinterpret_cast<const uint2*>(sp);
-      sreg[d][0] = v.x; sreg[d][1] = v.y;
-    } else {
-      sreg[d][0] = *sp;
-    }
+    load_chunk<BITS>(qbase + static_cast<int64_t>(min(c, C - 1)) * 64 * U::kWords, breg[d]);
   };
-#pragma unroll
-  for (int d = 0; d < kAhead; ++d) b_load(wave + kMmWaves * d, d);
-
   // ---- windowed staging: window r (columns 1024 r ...) in pieces of 8 halves;
   // piece p = tid + 512 v is token p / 128, columns 8 (p % 128).  Whether a
   // piece exists is uniform per wave (pieces is a multiple of 64); columns
@@ -371,8 +371,8 @@ __global__ __launch_bounds__(kMmThreads) void dequant_matmul_kernel(
   auto a_load = [&](int r, int set) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      if (wave * 64 + v * kMmThreads < pieces) {
-        const int p = tid + v * kMmThreads;
+      if (wave * 64 + v * kThreads < pieces) {
+        const int p = tid + v * kThreads;
         const int m = p / (kWin / 8), kp = p % (kWin / 8);
         const int k = min(r * kWin + 8 * kp, n - 8);
         const u32x4 x = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(m0 + m) * lda + k);
@@ -383,8 +383,8 @@ __global__ __launch_bounds__(kMmThreads) void dequant_matmul_kernel(
   auto a_store = [&](int buf, int set) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      if (wave * 64 + v * kMmThreads < pieces) {
-        const int p = tid + v * kMmThreads;
+      if (wave * 64 + v * kThreads < pieces) {
+        const int p = tid + v * kThreads;
         const int m = p / (kWin / 8), kp = p % (kWin / 8);
         u32x4 x = {areg[set][v][0], areg[set][v][1], areg[set][v][2], areg[set][v][3]};
         *reinterpret_cast<u32x4*>(abuf + (buf * ms + m) * kWinStride + 8 * kp) = x;
@@ -393,53 +393,67 @@ __global__ __launch_bounds__(kMmThreads) void dequant_matmul_kernel(
   };
 
   if constexpr (FULL) {
-    // every column of the slice's tokens, four pieces per thread at a time
+    // The slice's activations and the tile's scale/zero words, at most
+    // kFullPieces pieces of 16 bytes per thread, are loaded before the code
+    // prefetch is issued, so the stores below wait only for them and the first
+    // chunk is consumed as soon as it lands.  Loads are clamped, not skipped.
     const int per_row = n / 8;
-    const int total = ms * per_row;
-    for (int p0 = 0; p0 < total; p0 += 4 * kMmThreads) {
-      u32x4 x[4];
+    const int total_a = ms * per_row;
+    const int total = total_a + szw / 4;
+    u32x4 x[kFullPieces];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int p = min(p0 + v * kMmThreads + tid, total - 1);
+    for (int v = 0; v < kFullPieces; ++v) {
+      const int p = min(tid + v * kThreads, total - 1);
+      const int m = p / per_row, kp = p % per_row;
+      const u32x4* src = p < total_a
+          ? reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(m0 + m) * lda + 8 * kp)
+          : reinterpret_cast<const u32x4*>(sztile) + (p - total_a);
+      x[v] = *src;
+    }
+#pragma unroll
+    for (int d = 0; d < kAhead; ++d) b_load(wave + NW * d, d);
+#pragma unroll
+    for (int v = 0; v < kFullPieces; ++v) {
+      const int p = tid + v * kThreads;
+      if (p < total_a) {
         const int m = p / per_row, kp = p % per_row;
-        x[v] = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(m0 + m) * lda + 8 * kp);
-      }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int p = p0 + v * kMmThreads + tid;
-        if (p < total) {
-          const int m = p / per_row, kp = p % per_row;
-          *reinterpret_cast<u32x4*>(abuf + m * astride + 8 * kp) = x[v];
-        }
+        *reinterpret_cast<u32x4*>(abuf + m * astride + 8 * kp) = x[v];
+      } else if (p < total) {
+        reinterpret_cast<u32x4*>(szs)[p - total_a] = x[v];
       }
     }
   } else {
+    for (int p = tid; p < szw / 4; p += kThreads)
+      reinterpret_cast<u32x4*>(szs)[p] = reinterpret_cast<const u32x4*>(sztile)[p];
+#pragma unroll
+    for (int d = 0; d < kAhead; ++d) b_load(wave + NW * d, d);
     a_load(0, 0);
     a_store(0, 0);
+    // Everything issued so far has landed (the staging stores needed their
+    // loads, which were issued after the code prefetches).  Saying so tells
+    // the compiler that no load is in flight at the top of the loop, so inside
+    // it it waits only for the chunk it is about to use.
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
   }
-  // Everything issued so far has landed (the staging stores needed their
-  // loads, which were issued after the code prefetches).  Saying so tells the
-  // compiler that no load is in flight at the top of the loop, so inside it
-  // it waits only for the chunk it is about to use.
-  __builtin_amdgcn_s_waitcnt(kVmcntZero);
   lds_barrier();
 
   f4 yacc = {0.f, 0.f, 0.f, 0.f};
   f4 gacc = {0.f, 0.f, 0.f, 0.f};
-  // group boundaries: gs is 32, 64 or 128 (a power of two), or one group per row
-  const int gmask = gs > 0 ? gs - 1 : 0x7fffffff;
+  // A group covers 4 / SPC steps of a chunk (one group per row: the chunk's
+  // four steps, all with the row's one scale and zero).
+  constexpr int kGroupSteps = 4 / SPC;
 
-  // One chunk: four MFMA steps over the prefetched codes of slot d.  Rounds
-  // past the last chunk of a wave run on the clamped chunk with their result
-  // dropped (live false), so that every round is the same straight-line code.
-  auto chunk = [&](int d, int c, bool live, const _Float16* ap) {
+  // One chunk: four MFMA steps over the prefetched codes of slot d.  Waves
+  // past the last chunk run on the clamped chunk with their result dropped
+  // (live false), so that every round is the same straight-line code.
+  auto chunk = [&](int d, int cc, bool live, const _Float16* ap) {
+    const uint32_t* szc = szs + ((gs > 0 ? cc : 0) * 16 + j) * SPC;
     h2 zc[4];
     float s = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int k = c * kChunk + 32 * t;
-      if (t == 0 || (k & gmask) == 0) {
-        const uint32_t sz = sreg[d][(t * SPC) >> 2];
+      if (t % kGroupSteps == 0) {
+        const uint32_t sz = szc[t / kGroupSteps];
         s = live ? half_bits_to_float(static_cast<uint16_t>(sz & 0xFFFFu)) : 0.f;
         const _Float16 z = __builtin_bit_cast(_Float16, static_cast<uint16_t>(sz >> 16));
 #pragma unroll
@@ -451,32 +465,37 @@ __global__ __launch_bounds__(kMmThreads) void dequant_matmul_kernel(
       const h8 b = U::step(breg[d], t, zc);
       const h8 a = *reinterpret_cast<const h8*>(ap + 32 * t);
       gacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, gacc, 0, 0, 0);
-      // a group ends here, or continues in another wave's chunk: scale this
-      // wave's partial sum of it now (exact scaling, one fp32 rounding)
-      if (t == 3 || ((k + 32) & gmask) == 0) {
+      // the group ends here (or, one group per row, continues in another
+      // chunk): scale this wave's partial sum of it now (exact scaling, one
+      // fp32 rounding)
+      if (t % kGroupSteps == kGroupSteps - 1) {
         yacc += s * gacc;
         gacc = f4{0.f, 0.f, 0.f, 0.f};
       }
     }
   };
 
+  // Whole groups of kAhead rounds: a round past the end runs like the rest
+  // on the clamped chunk with its result dropped.  (Skipping it instead makes
+  // the compiler lose count of the loads in flight and wait for all of them
+  // in every round.)
   const int Rp = (R + kAhead - 1) / kAhead * kAhead;
   for (int r0 = 0; r0 < Rp; r0 += kAhead) {
 #pragma unroll
     for (int d = 0; d < kAhead; ++d) {
       const int r = r0 + d;
-      const int c = wave + kMmWaves * r;
+      const int c = wave + NW * r;
       const bool live = c < C;
       const int cc = live ? c : C - 1;
       if constexpr (FULL) {
         chunk(d, cc, live, abuf + arow * astride + cc * kChunk + 8 * q);
-        b_load(c + kMmWaves * kAhead, d);
+        b_load(c + NW * kAhead, d);
       } else {
         // window r + 1 goes to buffer and register set (r + 1) & 1 = (d + 1) & 1
         if (r + 1 < R) a_load(r + 1, (d + 1) & 1);
-        const int rc = cc / kMmWaves;   // window holding chunk cc (r when live)
-        chunk(d, cc, live, abuf + ((rc & 1) * ms + arow) * kWinStride + (cc - kMmWaves * rc) * kChunk + 8 * q);
-        b_load(c + kMmWaves * kAhead, d);
+        const int rc = cc / NW;   // window holding chunk cc (r when live)
+        chunk(d, cc, live, abuf + ((rc & 1) * ms + arow) * kWinStride + (cc - NW * rc) * kChunk + 8 * q);
+        b_load(c + NW * kAhead, d);
         if (r + 1 < R) a_store((d + 1) & 1, (d + 1) & 1);
         lds_barrier();
       }
@@ -494,7 +513,7 @@ __global__ __launch_bounds__(kMmThreads) void dequant_matmul_kernel(
     const int l = 16 * (mm >> 2) + o_in, r = mm & 3;   // inverse of acc_row
     float sum = 0.f;
 #pragma unroll
-    for (int v = 0; v < kMmWaves; ++v) sum += red[(v * 64 + l) * 4 + r];
+    for (int v = 0; v < NW; ++v) sum += red[(v * 64 + l) * 4 + r];
     const int o = tile * 16 + o_in;
     if (mm < ms && o < rows) {
       const int64_t idx = static_cast<int64_t>(m0 + mm) * ldy + o;
@@ -504,13 +523,13 @@ __global__ __launch_bounds__(kMmThreads) void dequant_matmul_kernel(
   }
 }
 
-template <int BITS, int SPC, bool FULL>
+template <int BITS, int SPC, bool FULL, int NW>
 hipError_t launch_mm_v(const uint16_t* A, int64_t lda, int M, const uint32_t* Q, const uint32_t* SZ, int rows,
                        int n, int gs, void* Y, int ydt, int64_t ldy, size_t lds, hipStream_t s) {
-  auto kern = dequant_matmul_kernel<BITS, SPC, FULL>;
+  auto kern = dequant_matmul_kernel<BITS, SPC, FULL, NW>;
   static bool attr_set = false;   // per instantiation; idempotent if raced
   if (!attr_set) {
-    const size_t most = FULL ? kFullLds : static_cast<size_t>(2) * kMTile * kWinStride * sizeof(_Float16);
+    const size_t most = FULL ? kFullLds : kWinLds;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(most));
     if (e != hipSuccess) return e;
@@ -518,7 +537,7 @@ hipError_t launch_mm_v(const uint16_t* A, int64_t lda, int M, const uint32_t* Q,
   }
   const int T = (rows + 15) / 16;
   dim3 grid(T, (M + kMTile - 1) / kMTile);
-  hipLaunchKernelGGL(kern, grid, dim3(kMmThreads), lds, s, A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy);
+  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy);
   return hipGetLastError();
 }
 
@@ -526,15 +545,34 @@ template <int BITS, int SPC>
 hipError_t launch_mm(const uint16_t* A, int64_t lda, int M, const uint32_t* Q, const uint32_t* SZ, int rows, int n,
                      int gs, void* Y, int ydt, int64_t ldy, hipStream_t s) {
   const int ms = M < kMTile ? M : kMTile;
-  const size_t red = static_cast<size_t>(kMmWaves) * 64 * 4 * sizeof(float);   // final sum of the waves
-  const size_t full = static_cast<size_t>(ms) * (n + 8) * sizeof(_Float16);
-  if (full <= kFullLds)
-    return launch_mm_v<BITS, SPC, true>(A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy, full < red ? red : full, s);
-  size_t win = static_cast<size_t>(2) * ms * kWinStride * sizeof(_Float16);
-  return launch_mm_v<BITS, SPC, false>(A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy, win < red ? red : win, s);
+  const int T = (rows + 15) / 16;
+  const int64_t tiles = static_cast<int64_t>(T) * ((M + kMTile - 1) / kMTile);
+  const int G = gs > 0 ? n / gs : 1;
+  const size_t sz_bytes = static_cast<size_t>(G) * 16 * 4;          // the tile's scale/zero words
+  auto red = [](int nw) { return static_cast<size_t>(nw) * 64 * 4 * sizeof(float); };   // final sum of the waves
+  const size_t full = static_cast<size_t>(ms) * (n + 8) * sizeof(_Float16) + sz_bytes;
+  const int64_t pieces = static_cast<int64_t>(ms) * (n / 8) + G * 4;
+  if (full <= kFullLds) {
+    // 8 waves per tile, or 4 when 8 would not put every tile on the chip at once
+    if (tiles * 8 <= kWaveSlots && pieces <= kFullPieces * 8 * 64)
+      return launch_mm_v<BITS, SPC, true, 8>(A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy, std::max(full, red(8)), s);
+    if (pieces <= kFullPieces * 4 * 64)
+      return launch_mm_v<BITS, SPC, true, 4>(A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy, std::max(full, red(4)), s);
+  }
+  const size_t win = static_cast<size_t>(2) * ms * kWinStride * sizeof(_Float16) + sz_bytes;
+  if (win > kWinLds) return hipErrorInvalidValue;   // the entry point bounds n so this cannot happen
+  return launch_mm_v<BITS, SPC, false, kWinWaves>(A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy,
+                                                  std::max(win, red(kWinWaves)), s);
 }
 
 }  // namespace
+
+// The windowed variant keeps a tile's scale/zero words in LDS beside two
+// windows of 16 tokens: n / group_size groups must fit.
+bool matmul_fits(int64_t n, int group_size) {
+  const int64_t G = group_size > 0 ? n / group_size : 1;
+  return static_cast<size_t>(2) * kMTile * kWinStride * sizeof(_Float16) + static_cast<size_t>(G) * 64 <= kWinLds;
+}
 
 size_t matmul_packed_bytes(int64_t rows, int64_t n, int bits, int group_size) {
   const int64_t T = (rows + 15) / 16;

@@ -262,21 +262,20 @@ def get(name: str) -> Workload:
 # Inputs of the dequantizing matmul: a quantized layer in the quantizer's
 # output shapes and fp16 decode-time activations
 # ----------------------------------------------------------------------------
-def quantized_layer(seed: int, rows: int, n: int, bits: int, group_size: int, act_order: bool = False):
-    """Random codes int64 [rows, n], fp16 scales and integer-valued fp16 zero
-    points [G, rows] (G = n / group_size, 1 for group_size -1) and the group
-    index int32 [n] of each column.
+def group_params(seed: int, rows: int, n: int, bits: int, group_size: int, act_order: bool = False):
+    """fp16 scales and integer-valued fp16 zero points [G, rows] (G = n /
+    group_size, 1 for group_size -1) and the group index int32 [n] of each
+    column, in the shapes the quantizer writes.
 
     Scales are drawn around what a 4-bit grid over N(0, 0.02^2) weights in
     groups of 128 gives (range about 6 sigma over 2^bits - 1 steps).  Without
     act_order the groups are runs of consecutive columns; with it they are
     spread over the columns by a random permutation, as a column order that
     visits columns by decreasing activation leaves them."""
-    g = _ss(seed, 300, rows, n, bits, max(group_size, 0))
+    g = _ss(seed, 310, rows, n, bits, max(group_size, 0))
     gs = n if group_size <= 0 else group_size
     G = n // gs
     maxq = (1 << bits) - 1
-    codes = g.integers(0, maxq + 1, size=(rows, n), dtype=np.int64)
     scales = (g.uniform(0.5, 1.5, size=(G, rows)) * 0.02 * 6.0 / maxq).astype(np.float16)
     zeros = g.integers(0, maxq + 1, size=(G, rows)).astype(np.float16)
     pos = np.arange(n)
@@ -286,7 +285,14 @@ def quantized_layer(seed: int, rows: int, n: int, bits: int, group_size: int, ac
         g_idx[order] = (pos // gs).astype(np.int32)
     else:
         g_idx = (pos // gs).astype(np.int32)
-    return codes, scales, zeros, g_idx
+    return scales, zeros, g_idx
+
+
+def quantized_layer(seed: int, rows: int, n: int, bits: int, group_size: int, act_order: bool = False):
+    """Random codes int64 [rows, n] in [0, 2^bits) with ``group_params``:
+    (codes, scales, zeros, g_idx)."""
+    codes = _ss(seed, 300, rows, n, bits).integers(0, 1 << bits, size=(rows, n), dtype=np.int64)
+    return (codes, *group_params(seed, rows, n, bits, group_size, act_order))
 
 
 def decode_activations_raw(seed: int, tokens: int, n: int, outlier_frac: float = 0.01,
@@ -300,3 +306,10 @@ def decode_activations_raw(seed: int, tokens: int, n: int, outlier_frac: float =
     if k:
         x[:, g.choice(n, size=k, replace=False)] *= outlier_scale
     return x.astype(np.float16).view(np.uint16)
+
+
+def random_qweight(seed: int, rows: int, n: int, bits: int) -> np.ndarray:
+    """uint32 [n * bits / 32, rows] of uniform random bits: a packed code matrix
+    in the quantizer's output shape (every bit pattern is a valid code stream)."""
+    g = _ss(seed, 500, rows, n, bits)
+    return g.integers(0, 1 << 32, size=(n * bits // 32, rows), dtype=np.uint64).astype(np.uint32)

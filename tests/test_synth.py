@@ -58,3 +58,11 @@ def test_matmul_inputs_are_deterministic_and_well_formed():
     assert np.array_equal(a, synth.decode_activations_raw(5, 3, 1000))
     v = a.view(np.float16).astype(np.float64)
     assert np.all(np.isfinite(v)) and (np.abs(v) > 10).any(axis=0).sum() >= 5
+
+
+def test_random_qweight():
+    q = synth.random_qweight(2, 24, 256, 3)
+    assert q.shape == (24, 24) and q.dtype == np.uint32
+    assert np.array_equal(q, synth.random_qweight(2, 24, 256, 3))
+    bits = np.unpackbits(q.view(np.uint8))
+    assert abs(bits.mean() - 0.5) < 0.02
