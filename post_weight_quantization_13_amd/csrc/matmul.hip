@@ -327,7 +327,9 @@ __device__ __forceinline__ int acc_row(int lane, int r) { return 4 * (lane >> 4)
 // FULL: the slice's activations are staged in LDS once, before the loop
 // (decode sizes); else 1024-column windows are staged round by round (NW = 8).
 // NW: waves per workgroup, all on the same 16 outputs, splitting the chunks.
-template <int BITS, int SPC, bool FULL, int NW>
+// PIECES: 16-byte pieces of activations and scale/zero words each thread
+// stages (FULL).
+template <int BITS, int SPC, bool FULL, int NW, int PIECES>
 __global__ __launch_bounds__(NW * 64) void dequant_matmul_kernel(
     const uint16_t* __restrict__ A, int64_t lda, int M, const uint32_t* __restrict__ Q,
     const uint32_t* __restrict__ SZ, int rows, int n, int gs, void* __restrict__ Y, int ydt, int64_t ldy) {
@@ -394,15 +396,15 @@ __global__ __launch_bounds__(NW * 64) void dequant_matmul_kernel(
 
   if constexpr (FULL) {
     // The slice's activations and the tile's scale/zero words, at most
-    // kFullPieces pieces of 16 bytes per thread, are loaded before the code
+    // PIECES pieces of 16 bytes per thread, are loaded before the code
     // prefetch is issued, so the stores below wait only for them and the first
     // chunk is consumed as soon as it lands.  Loads are clamped, not skipped.
     const int per_row = n / 8;
     const int total_a = ms * per_row;
     const int total = total_a + szw / 4;
-    u32x4 x[kFullPieces];
+    u32x4 x[PIECES];
 #pragma unroll
-    for (int v = 0; v < kFullPieces; ++v) {
+    for (int v = 0; v < PIECES; ++v) {
       const int p = min(tid + v * kThreads, total - 1);
       const int m = p / per_row, kp = p % per_row;
       const u32x4* src = p < total_a
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(NW * 64) void dequant_matmul_kernel(
 #pragma unroll
     for (int d = 0; d < kAhead; ++d) b_load(wave + NW * d, d);
 #pragma unroll
-    for (int v = 0; v < kFullPieces; ++v) {
+    for (int v = 0; v < PIECES; ++v) {
       const int p = tid + v * kThreads;
       if (p < total_a) {
         const int m = p / per_row, kp = p % per_row;
@@ -523,10 +525,10 @@ __global__ __launch_bounds__(NW * 64) void dequant_matmul_kernel(
   }
 }
 
-template <int BITS, int SPC, bool FULL, int NW>
+template <int BITS, int SPC, bool FULL, int NW, int PIECES = 1>
 hipError_t launch_mm_v(const uint16_t* A, int64_t lda, int M, const uint32_t* Q, const uint32_t* SZ, int rows,
                        int n, int gs, void* Y, int ydt, int64_t ldy, size_t lds, hipStream_t s) {
-  auto kern = dequant_matmul_kernel<BITS, SPC, FULL, NW>;
+  auto kern = dequant_matmul_kernel<BITS, SPC, FULL, NW, PIECES>;
   static bool attr_set = false;   // per instantiation; idempotent if raced
   if (!attr_set) {
     const size_t most = FULL ? kFullLds : kWinLds;
@@ -553,11 +555,23 @@ hipError_t launch_mm(const uint16_t* A, int64_t lda, int M, const uint32_t* Q, c
   const size_t full = static_cast<size_t>(ms) * (n + 8) * sizeof(_Float16) + sz_bytes;
   const int64_t pieces = static_cast<int64_t>(ms) * (n / 8) + G * 4;
   if (full <= kFullLds) {
-    // 8 waves per tile, or 4 when 8 would not put every tile on the chip at once
-    if (tiles * 8 <= kWaveSlots && pieces <= kFullPieces * 8 * 64)
-      return launch_mm_v<BITS, SPC, true, 8>(A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy, std::max(full, red(8)), s);
-    if (pieces <= kFullPieces * 4 * 64)
-      return launch_mm_v<BITS, SPC, true, 4>(A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy, std::max(full, red(4)), s);
+    // 8 waves per tile, or 4 when 8 would not put every tile on the chip at
+    // once; the fewest staging pieces per thread that cover the slice
+#define GPTQ_MM_FULL(NW)                                                                                   \
+    if (pieces <= 2 * NW * 64)                                                                             \
+      return launch_mm_v<BITS, SPC, true, NW, 2>(A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy,               \
+                                                 std::max(full, red(NW)), s);                              \
+    if (pieces <= 4 * NW * 64)                                                                             \
+      return launch_mm_v<BITS, SPC, true, NW, 4>(A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy,               \
+                                                 std::max(full, red(NW)), s);                              \
+    if (pieces <= kFullPieces * NW * 64)                                                                   \
+      return launch_mm_v<BITS, SPC, true, NW, kFullPieces>(A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy,     \
+                                                           std::max(full, red(NW)), s);
+    if (tiles * 8 <= kWaveSlots) {
+      GPTQ_MM_FULL(8)
+    }
+    GPTQ_MM_FULL(4)
+#undef GPTQ_MM_FULL
   }
   const size_t win = static_cast<size_t>(2) * ms * kWinStride * sizeof(_Float16) + sz_bytes;
   if (win > kWinLds) return hipErrorInvalidValue;   // the entry point bounds n so this cannot happen
