@@ -22,6 +22,7 @@ HBM roofline.
 Usage: python bench.py [--steps K] [--warmup W] [--workload attn4096]
        python bench.py --matmul-only  (only the dequant_matmul part, for profiling)
        python bench.py --pmc-probe    (short run for rocprofv3 --pmc counter passes)
+       python bench.py --matmul-only --pmc-probe   (the same for the dequant_matmul pass)
 """
 from __future__ import annotations
 
@@ -42,28 +43,30 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
 METRIC = "GPTQ weights quantized/sec per layer (4096×4096, g128) + Hessian TFLOP/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hessian_attn4096_traffic.json")
 HESSIAN_SRC = os.path.join(ROOT, "post_weight_quantization_13_amd", "csrc", "hessian.hip")
+MM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dequant_matmul_decode7b_traffic.json")
+MM_SRC = os.path.join(ROOT, "post_weight_quantization_13_amd", "csrc", "matmul.hip")
 
 
 def _log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def _hessian_sha() -> str:
-    with open(HESSIAN_SRC, "rb") as f:
+def _sha(path) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic():
-    """HBM bytes per Hessian launch from the committed counter summary, if it is
-    for the current kernel source; else None."""
+def _traffic(path=TRAFFIC_FILE, src=HESSIAN_SRC, key="bytes_per_launch"):
+    """HBM bytes per launch (or per pass) from a committed counter summary, if
+    it is for the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != _hessian_sha():
+    if t.get("source_sha") != _sha(src):
         return None
-    return t.get("bytes_per_launch")
+    return t.get(key)
 
 
 def _device_inputs(wl, torch):
@@ -127,10 +130,13 @@ MM_BLOCKS = 32
 MM_BITS, MM_GS = 4, 128
 
 
-def dequant_matmul_bench(g, torch, replays: int = 20, token_counts=(1, 16)):
+def dequant_matmul_bench(g, torch, replays: int = 20, token_counts=(1, 16), pmc_probe: bool = False):
     """Decode through all linears of MM_BLOCKS blocks (each block its own copy
     of the packed weights, 3.4 GB in all, so nothing is served from cache),
-    captured once as a graph of 4 * MM_BLOCKS launches and replayed."""
+    captured once as a graph of 4 * MM_BLOCKS launches and replayed.
+
+    pmc_probe: instead, a 1 GiB device copy (counter calibration) and one
+    eager one-token pass, for rocprofv3 --pmc passes."""
     import numpy as np
     import synth
     dev = torch.device("cuda")
@@ -151,6 +157,21 @@ def dequant_matmul_bench(g, torch, replays: int = 20, token_counts=(1, 16)):
                         f"{MM_BLOCKS} Llama-2-7B-shaped blocks, {MM_BITS}-bit asym g{MM_GS}, desc_act off, "
                         f"fp16 activations and outputs; one graph replay = {4 * MM_BLOCKS} launches"),
            "packed_weight_bytes": weight_bytes, "by_tokens": {}}
+    if pmc_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        A = [torch.from_numpy(synth.decode_activations_raw(41 + li, 1, n).view(np.float16)).to(dev)
+             for li, (_, rows, n) in enumerate(MM_SHAPES)]
+        Y = [torch.empty((1, rows), dtype=torch.float16, device=dev) for (_, rows, n) in MM_SHAPES]
+        for b in range(MM_BLOCKS):
+            for li, (_, rows, n) in enumerate(MM_SHAPES):
+                g.gptq_matmul(A[li], packed[b][li], None, rows, n, MM_BITS, MM_GS, Y[li])
+        torch.cuda.synchronize()
+        _log(f"pmc probe done: 1 GiB copy + {4 * MM_BLOCKS} one-token launches")
+        return None
     for M in token_counts:
         A = [torch.from_numpy(synth.decode_activations_raw(41 + li, M, n).view(np.float16)).to(dev)
              for li, (_, rows, n) in enumerate(MM_SHAPES)]
@@ -189,9 +210,11 @@ def dequant_matmul_bench(g, torch, replays: int = 20, token_counts=(1, 16)):
     one = out["by_tokens"][str(token_counts[0])]
     out["roofline"] = {"kernel": "dequant_matmul_kernel<4,1,full> (one token)", "bound": "hbm",
                        "achieved": one["GB_per_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                       "frac": one["GB_per_s"] / PEAK_HBM_GBS, "traffic": None,
-                       "note": "algorithmic bytes (packed codes, scale/zero words, activations, outputs) "
-                               "over the graph replay time, inter-kernel gaps included"}
+                       "frac": one["GB_per_s"] / PEAK_HBM_GBS,
+                       "traffic": _traffic(MM_TRAFFIC_FILE, MM_SRC, "bytes_per_pass"),
+                       "note": "achieved: algorithmic bytes (packed codes, scale/zero words, activations, outputs) "
+                               "over the graph replay time, inter-kernel gaps included; traffic: HBM bytes per "
+                               "one-token pass from FETCH_SIZE/WRITE_SIZE"}
     return out
 
 
@@ -227,7 +250,9 @@ def main() -> int:
 
     if args.matmul_only:
         torch.cuda.set_device(0)
-        print(json.dumps({"dequant_matmul": dequant_matmul_bench(g, torch)}), flush=True)
+        res = dequant_matmul_bench(g, torch, pmc_probe=args.pmc_probe)
+        if res is not None:
+            print(json.dumps({"dequant_matmul": res}), flush=True)
         return 0
 
     wl = synth.get(args.workload)
