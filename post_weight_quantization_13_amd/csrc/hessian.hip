@@ -22,7 +22,9 @@
 //     values in registers and stores 8 feature rows of 8 consecutive tokens
 //     into LDS, so each MFMA operand fragment (8 consecutive tokens of one
 //     feature) is a single 16-byte LDS read.  LDS is double buffered and one
-//     further stage is in flight into registers ahead of the MFMAs.
+//     further stage is in flight into registers ahead of the MFMAs; the
+//     per-stage barrier waits for LDS traffic only, so that stage's global
+//     loads overlap the current stage's MFMAs.
 //   * Epilogue: H <- beta*H + alpha*master; each element is written once and
 //     mirrored through LDS so H is exactly symmetric and both writes coalesce.
 //   * fp32 inputs use a VALU kernel accumulating in fp64.
@@ -242,7 +244,9 @@ __device__ __forceinline__ void tile_accumulate(const TileCtx& cx, int ti, int t
     if (s + 1 >= nstages) break;
     lds_store(ra, buf ^ 1);
     global_load(ra, t0 + (s + 2) * kKStep);
-    __syncthreads();
+    // LDS-only barrier: the loads of stage s + 2 stay in flight across it and
+    // land while stage s + 1 computes (a full barrier would wait for them).
+    lds_barrier();
     buf ^= 1;
   }
   flush();
