@@ -14,7 +14,9 @@ Functions keep the C names:
     gptq_matmul_pack(qweight, scales, zeros, g_idx, bits, group_size, packed, col_order) -> identity
     gptq_matmul(A, packed, col_order, rows, n, bits, group_size, Y, ws)
 plus the workspace queries and small allocating helpers (``quantize_layer``,
-``hessian``, ``prepare``) that create the output tensors with torch.
+``hessian``, ``prepare``, ``PackedLayer``) that create the output tensors with
+torch, and ``quantize_block``, which sequences those calls for the linears of a
+decoder block that share activation sets.
 """
 from __future__ import annotations
 
@@ -349,3 +351,27 @@ class PackedLayer:
             ws = self.workspace(M)
         gptq_matmul(A, self.packed, self.col_order, self.rows, self.n, self.bits, self.group_size, Y, ws)
         return Y
+
+
+def quantize_block(X_sets, weights, xset_of, cfg, want_loss: bool = True):
+    """Quantize the linears of a decoder block whose inputs come in a few
+    shared activation sets (q/k/v read one, gate/up another): one Hessian and
+    one prepare per set, then one quantize per linear with its set's factor.
+
+    X_sets: list of [tokens, n_s] device tensors; weights: list of [rows, n]
+    device tensors; xset_of[i]: the set linear i reads.  Returns a list of
+    dicts (qweight, scales, zeros, g_idx, loss, rel_loss) in the order of
+    ``weights``, plus the Hessians (for the caller's checks).
+    """
+    Hs, factors = [], []
+    for X in X_sets:
+        H, _ = hessian(X)
+        Hs.append(H)
+        factors.append(prepare(H, cfg))
+    outs = []
+    for W, s in zip(weights, xset_of):
+        U, perm, dead = factors[s]
+        out = quantize_layer(U, perm, dead, cfg, W)
+        out["rel_loss"] = layer_loss(Hs[s], W, out, cfg) if want_loss else None
+        outs.append(out)
+    return outs, Hs

@@ -50,3 +50,18 @@ def compare_layer(out, ref, bits, n, W, H, gpu_rel_loss):
     loss_rel = abs(gpu_rel_loss - ref["rel_loss"]) / ref["rel_loss"]
     return dict(agree=agree, s_rel=s_rel, s_frac=s_frac, z_frac=z_frac, gidx_ok=gidx_ok, pack_ok=pack_ok,
                 loss_rel=loss_rel, gpu_rel_loss=gpu_rel_loss, ref_rel_loss=ref["rel_loss"])
+
+
+def groups_before_first_flip(codes_gpu, codes_ref, g_idx, G):
+    """Mask [G, rows] of the groups whose parameters were taken before the
+    first differing code of their row (in sweep order, groups are numbered by
+    sweep position; a group's grid is taken at its first column, so a group
+    is upstream of a flip when its index is at most the flipped column's
+    group).  Rows with no differing code: every group."""
+    rows = codes_gpu.shape[0]
+    mask = np.ones((G, rows), dtype=bool)
+    g_idx = np.asarray(g_idx)
+    for r in np.nonzero((codes_gpu != codes_ref).any(axis=1))[0]:
+        first = int(g_idx[codes_gpu[r] != codes_ref[r]].min())
+        mask[first + 1:, r] = False
+    return mask
