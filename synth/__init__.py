@@ -313,3 +313,28 @@ def random_qweight(seed: int, rows: int, n: int, bits: int) -> np.ndarray:
     in the quantizer's output shape (every bit pattern is a valid code stream)."""
     g = _ss(seed, 500, rows, n, bits)
     return g.integers(0, 1 << 32, size=(n * bits // 32, rows), dtype=np.uint64).astype(np.uint32)
+
+
+def _chunk_job(args):
+    wl, xset, c = args
+    return c, activations_chunk_raw(wl, c, xset)
+
+
+def activations_raw_parallel(wl: Workload, xset: int = 0, workers: int = 16, out=None):
+    """``activations_raw`` with the chunks generated by spawned worker
+    processes (each chunk is seeded on its own, so the result is identical).
+    ``out``, if given, is called as out(t0, chunk) for each chunk instead of
+    assembling the whole array (which is then not returned)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    n = wl.xsets[xset][0]
+    full = None if out is not None else np.empty((wl.tokens, n), dtype=np.uint16 if wl.dtype == "bf16"
+                                                 else np.float32)
+    jobs = [(wl, xset, c) for c in range(n_chunks(wl))]
+    with ProcessPoolExecutor(max_workers=max(1, workers), mp_context=mp.get_context("spawn")) as ex:
+        for c, raw in ex.map(_chunk_job, jobs):
+            if out is not None:
+                out(c * CHUNK, raw)
+            else:
+                full[c * CHUNK:c * CHUNK + raw.shape[0]] = raw
+    return full

@@ -66,3 +66,13 @@ def test_random_qweight():
     assert np.array_equal(q, synth.random_qweight(2, 24, 256, 3))
     bits = np.unpackbits(q.view(np.uint8))
     assert abs(bits.mean() - 0.5) < 0.02
+
+
+def test_parallel_generation_is_identical():
+    wl = synth.get("attn4096").resized(rows=16, n=256, tokens=2 * synth.CHUNK + 17)
+    a = synth.activations_raw_parallel(wl, 0, workers=2)
+    assert np.array_equal(a, synth.activations_raw(wl, 0))
+    got = {}
+    synth.activations_raw_parallel(wl, 0, workers=2, out=lambda t0, c: got.__setitem__(t0, c))
+    assert sorted(got) == [0, synth.CHUNK, 2 * synth.CHUNK]
+    assert np.array_equal(np.concatenate([got[k] for k in sorted(got)]), a)
