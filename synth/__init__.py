@@ -206,7 +206,9 @@ _STATIC_CACHE: dict = {}
 
 
 def _static(wl: Workload, xset: int):
-    key = (wl.name, wl.seed, wl.xsets[xset])
+    # keyed by the set's index too: sets with equal descriptions (q/k/v-in,
+    # o-in, gate/up-in of a block) still have their own seeded loadings
+    key = (wl.name, wl.seed, xset, wl.xsets[xset])
     if key not in _STATIC_CACHE:
         _STATIC_CACHE[key] = _xset_static(wl, xset)
     return _STATIC_CACHE[key]

@@ -76,3 +76,21 @@ def test_parallel_generation_is_identical():
     synth.activations_raw_parallel(wl, 0, workers=2, out=lambda t0, c: got.__setitem__(t0, c))
     assert sorted(got) == [0, synth.CHUNK, 2 * synth.CHUNK]
     assert np.array_equal(np.concatenate([got[k] for k in sorted(got)]), a)
+
+
+def test_sets_with_equal_descriptions_are_independent_of_order():
+    """Activation sets with the same description (the block's q/k/v-in, o-in
+    and gate/up-in) each have their own seeded loadings, whatever set was
+    generated first in the process."""
+    import dataclasses
+    base = synth.get("llama2block")
+    wl = dataclasses.replace(base, name="order-check", tokens=64,
+                             xsets=((96, "factor", 0, 1.0), (96, "factor", 0, 1.0)))
+    synth._STATIC_CACHE.clear()
+    b_first = synth.activations_chunk_raw(wl, 0, 1)
+    a_after = synth.activations_chunk_raw(wl, 0, 0)
+    synth._STATIC_CACHE.clear()
+    a_first = synth.activations_chunk_raw(wl, 0, 0)
+    b_after = synth.activations_chunk_raw(wl, 0, 1)
+    assert np.array_equal(a_first, a_after) and np.array_equal(b_first, b_after)
+    assert not np.array_equal(a_first, b_first)
