@@ -89,22 +89,26 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
   }
 }
 
-// Schedule order of the upper-triangle tiles: super-blocks of 4 tile-rows x 8
-// tile-columns, row-major over the super-blocks that meet the triangle, tiles
-// row-major inside each.  A run of 32 consecutive indices (one XCD's share of
-// a round) then needs about 12 panels of X instead of 33, so the XCD's L2
-// serves most operand loads.  index -> (ti, tj), O(#super-blocks).
-__device__ void sched_tile(int idx, int nt, int& ti, int& tj) {
-  const int nsr = (nt + 3) / 4, nsc = (nt + 7) / 8;
+// Schedule order of the upper-triangle tiles: super-blocks of sbr tile-rows x
+// 8 tile-columns, row-major over the super-blocks that meet the triangle,
+// tiles row-major inside each.  The work-groups that one XCD receives in a
+// round take consecutive indices, so they need few panels of X between them
+// and the XCD's L2 serves most operand loads: 32 work-groups (one per
+// compute unit) on a 4 x 8 super-block need about 12 panels instead of 33;
+// 64 (two per compute unit) on an 8 x 8 one, 16 instead of 24 on two 4 x 8.
+// index -> (ti, tj), O(#super-blocks).
+__device__ void sched_tile(int idx, int nt, int sbr, int& ti, int& tj) {
+  constexpr int sbc = 8;
+  const int nsr = (nt + sbr - 1) / sbr, nsc = (nt + sbc - 1) / sbc;
   int rem = idx;
   ti = 0;
   tj = 0;
   for (int SR = 0; SR < nsr; ++SR) {
-    const int a_end = (4 * SR + 4 < nt) ? 4 * SR + 4 : nt;
-    for (int SC = SR / 2; SC < nsc; ++SC) {
-      const int c_hi = (8 * SC + 8 < nt) ? 8 * SC + 8 : nt;
-      for (int a = 4 * SR; a < a_end; ++a) {
-        const int lo = (a > 8 * SC) ? a : 8 * SC;
+    const int a_end = (sbr * SR + sbr < nt) ? sbr * SR + sbr : nt;
+    for (int SC = (sbr * SR) / sbc; SC < nsc; ++SC) {
+      const int c_hi = (sbc * SC + sbc < nt) ? sbc * SC + sbc : nt;
+      for (int a = sbr * SR; a < a_end; ++a) {
+        const int lo = (a > sbc * SC) ? a : sbc * SC;
         const int cnt = (c_hi > lo) ? c_hi - lo : 0;
         if (rem < cnt) {
           ti = a;
@@ -317,6 +321,7 @@ __device__ __forceinline__ void tile_store_partial(const double (&master)[2][16]
 // syrk_reduce_kernel sums in a fixed order (S == 1: the pieces are whole tiles).
 struct HessSched {
   int nt, T, P, R, L, S;
+  int sbr;        // super-block rows of the schedule order
   int64_t chunk;  // tokens per piece
 };
 
@@ -343,7 +348,7 @@ __global__ void __launch_bounds__(kThreads) syrk_mfma_kernel(const uint16_t* __r
     }
   }
   int ti, tj;
-  sched_tile(idx, sc.nt, ti, tj);
+  sched_tile(idx, sc.nt, sc.sbr, ti, tj);
   double master[2][16];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -354,6 +359,312 @@ __global__ void __launch_bounds__(kThreads) syrk_mfma_kernel(const uint16_t* __r
   else tile_epilogue(master, ti, tj, n, alpha, beta, H, lds);
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS path (16-byte aligned rows, n a multiple of 8).
+//
+// Four waves per work-group, each a 64x64 block of the 128x128 tile (2x2 MFMA
+// 32x32x16 tiles), so one LDS fragment feeds two MFMAs instead of 1.5, and
+// two work-groups share a compute unit (64 KB of LDS each, at most 256
+// registers per wave): their barriers are independent, so one work-group's
+// MFMAs run while the other waits.
+//   * Staging: buffer loads write X straight into LDS in its natural
+//     [token][feature] order, 32 tokens per stage, four stages resident (one
+//     computed, three in flight).  No staging registers and no transposes: a
+//     lane's MFMA operand (8 consecutive tokens of one feature) comes from
+//     two ds_read_b64_tr_b16, each handing a 16-lane group 4 tokens x 16
+//     features.  The buffer's range check returns zeros past the last token
+//     and for features >= n, so ragged tails need no branches.
+//   * LDS panel: 32 token rows of 256 bytes (16 chunks of 8 features); chunk
+//     c of row r sits at 16-byte slot c ^ 4 (r & 3), so the 32 lanes of a
+//     transposing read (4 rows x 64 bytes) touch 64 distinct banks and a
+//     load instruction still writes 1 KB contiguously.
+//   * Precision as above: fp32 chains of 256 tokens (8 stages) summed into an
+//     fp64 master in registers.
+constexpr int kDKS = 32;                       // tokens per stage
+constexpr int kDBufs = 4;                      // resident stages
+constexpr int kDThreads = 256;                 // 4 waves
+constexpr int kDPanel = kDKS * kTile * 2;      // 8 KB
+constexpr int kDStage = 2 * kDPanel;           // both panels
+constexpr int kDLds = kDBufs * kDStage;        // 64 KB
+constexpr int kDChain = 256 / kDKS;            // stages per fp32 chain
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a byte offset past any range
+static_assert(kDChain * kDKS == kFlushSteps * kKStep, "both paths keep 256-token fp32 chains");
+static_assert(kDKS % 16 == 0 && kDBufs >= 2 && kDLds <= 80 * 1024, "whole k-steps; two work-groups per compute unit");
+static_assert(kDLds >= 64 * kTile * 8, "the epilogue stages 64 columns of the fp64 tile in LDS");
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
+// One 16-byte-per-lane buffer load into LDS: lane L's 16 bytes land at
+// lds_addr + 16 L.  Written out rather than through the compiler's builtin,
+// whose wait-count tracking would make every later LDS read wait for all
+// loads in flight, including those of stages not yet needed; the waits on
+// these loads are explicit (vm_wait_barrier).  M0 is saved and restored
+// around the load, and one wait state separates its write from the load.
+__device__ __forceinline__ void lds_dma16(const u32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
+// Loads per wave and stage: DIAG tiles stage one panel, others two; each
+// load fills 4 token rows.
+template <bool DIAG>
+constexpr int dma_loads_per_wave() { return DIAG ? kDKS / 16 : kDKS / 8; }
+
+// Per-tile constants of this lane's stage loads.  Wave w fills rows of panel
+// p as whole 1 KB blocks of 4 rows; lane L of a block fills slot L % 16 of row
+// L / 16, which holds chunk (L % 16) ^ 4 (L / 16) of that row.  off[q] is the
+// byte offset of that chunk from the stage's first token (out of range for
+// features >= n); lds is the wave's first row in a stage buffer.
+template <bool DIAG>
+struct DmaLane {
+  uint32_t off[dma_loads_per_wave<DIAG>()];
+  uint32_t lds;
+};
+
+template <bool DIAG>
+__device__ __forceinline__ DmaLane<DIAG> dma_lane(int64_t ldx, int n, int fI, int fJ) {
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  const int c = (lane & 15) ^ ((lane >> 4) << 2);
+  const int p = DIAG ? 0 : (wave >> 1);
+  const int f = (p ? fJ : fI) + 8 * c;
+  const int rw = DIAG ? (kDKS / 4) * wave : (kDKS / 2) * (wave & 1);
+  DmaLane<DIAG> d;
+#pragma unroll
+  for (int q = 0; q < dma_loads_per_wave<DIAG>(); ++q) {
+    const int r = rw + 4 * q + (lane >> 4);
+    d.off[q] = (f < n) ? static_cast<uint32_t>((r * ldx + f) * 2) : kOutOfRange;
+  }
+  d.lds = static_cast<uint32_t>(p * kDPanel + rw * 256);
+  return d;
+}
+
+// Issue one stage's loads into the stage buffer at LDS address stage_lds.  The
+// buffer's range ends at token t1 (nothing at all past the end), so later rows
+// read as zeros.
+template <bool DIAG>
+__device__ __forceinline__ void dma_stage(const uint16_t* X, int64_t ldx, int64_t tstage, int64_t t1,
+                                          const DmaLane<DIAG>& d, uint32_t stage_lds) {
+  int64_t rows = t1 - tstage;
+  rows = rows < 0 ? 0 : (rows > kDKS ? kDKS : rows);
+  const uint64_t base = reinterpret_cast<uint64_t>(X + (rows > 0 ? tstage * ldx : 0));
+  u32x4 rs;
+  rs[0] = static_cast<uint32_t>(base);
+  rs[1] = static_cast<uint32_t>(base >> 32);  // stride 0
+  rs[2] = static_cast<uint32_t>(rows * ldx * 2);
+  rs[3] = kRsrcWord3;
+#pragma unroll
+  for (int q = 0; q < dma_loads_per_wave<DIAG>(); ++q) lds_dma16(rs, stage_lds + d.lds + q * 1024, d.off[q]);
+}
+
+// This lane's MFMA operand for features fb .. fb+31 and tokens 16 kk ..
+// 16 kk + 15 of a staged panel: two transposing reads of 4 tokens each.
+__device__ __forceinline__ u32x4 dma_frag(const uint8_t* panel, int fb, int kk, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int rl = 8 * (g >> 1) + (j >> 2);                    // row within the k-step (h = 0)
+  const int slot = ((fb >> 3) ^ ((j >> 2) << 2)) + 2 * (g & 1) + ((j & 3) >> 1);
+  const uint8_t* p = panel + (16 * kk + rl) * 256 + 16 * slot + 8 * (j & 1);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p + 4 * 256));
+  u32x4 v;
+  __builtin_memcpy(&v, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<uint8_t*>(&v) + 8, &hi, 8);
+  return v;
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// master (this wave's 64x64 block, fp64) += X[t0:t1, I]^T X[t0:t1, J].
+template <int DT, bool DIAG>
+__device__ __forceinline__ void tile_accumulate_dma(const uint16_t* X, int64_t ldx, int n, int ti, int tj,
+                                                    int64_t t0, int64_t t1, uint8_t* lds, double (&master)[2][2][16]) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int fI = ti * kTile, fJ = tj * kTile;
+  // the strictly lower block of a diagonal tile is never stored
+  const bool idle = DIAG && wm == 1 && wn == 0;
+  constexpr int NL = dma_loads_per_wave<DIAG>();
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  auto flush = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          master[i][j][r] += static_cast<double>(acc[i][j][r]);
+          acc[i][j][r] = 0.0f;
+        }
+  };
+  const int64_t nst = (t1 - t0 + kDKS - 1) / kDKS;
+  if (nst <= 0) return;
+  // three stages in flight before the first is computed; stages past the end
+  // load zeros without touching memory, which keeps the wait counts fixed
+  const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)lds));
+  const DmaLane<DIAG> dl = dma_lane<DIAG>(ldx, n, fI, fJ);
+#pragma unroll
+  for (int s = 0; s < kDBufs - 1; ++s) dma_stage<DIAG>(X, ldx, t0 + s * kDKS, t1, dl, lds_addr + s * kDStage);
+  int chain = 0;
+  for (int64_t s = 0; s < nst; ++s) {
+    // this wave's loads of stage s have landed (those of the later stages in
+    // flight may not); after the barrier every wave's have, and every wave is
+    // done with stage s-1, whose buffer the next loads reuse
+    vm_wait_barrier<(kDBufs - 2) * NL>();
+    const int64_t sn = s + kDBufs - 1;
+    dma_stage<DIAG>(X, ldx, t0 + sn * kDKS, t1, dl, lds_addr + static_cast<uint32_t>(sn % kDBufs) * kDStage);
+    const uint8_t* pa = lds + (s % kDBufs) * kDStage;
+    const uint8_t* pb = DIAG ? pa : pa + kDPanel;
+    if (!idle) {
+#pragma unroll
+      for (int kk = 0; kk < kDKS / 16; ++kk) {
+        u32x4 fa[2], fb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) fa[i] = dma_frag(pa, wm * 64 + 32 * i, kk, lane);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[j] = dma_frag(pb, wn * 64 + 32 * j, kk, lane);
+        // raised wave priority while MFMAs issue: the other work-group's wave
+        // on this SIMD, busy with loads and LDS reads, yields to them
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            __builtin_amdgcn_s_setprio(1);
+            acc[i][j] = mfma_32x32x16<DT>(fa[i], fb[j], acc[i][j]);
+          }
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
+    if (++chain == kDChain) {
+      flush();
+      chain = 0;
+    }
+  }
+  flush();
+  vm_wait_barrier<0>();  // the trailing zero loads have landed; LDS free for the epilogue
+}
+
+// Element (i, j, r) of a wave's 64x64 block -> row / column inside the tile.
+__device__ __forceinline__ int dma_row(int wm, int i, int r, int lane) { return wm * 64 + acc_row(i, r, lane); }
+__device__ __forceinline__ int dma_col(int wn, int j, int lane) { return wn * 64 + j * 32 + (lane & 31); }
+
+// H <- beta*H + alpha*master, each element written once; the mirror goes
+// through LDS in two halves of 64 columns (64 KB each), so both writes
+// coalesce.
+__device__ __forceinline__ void tile_epilogue_dma(const double (&master)[2][2][16], int ti, int tj, int n,
+                                                  double alpha, double beta, double* __restrict__ H, uint8_t* lds) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave & 1, wn = wave >> 1;
+  const bool diag = (ti == tj);
+  double* stage = reinterpret_cast<double*>(lds);  // [64 columns][128 rows], rows XOR-swizzled
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (wn == half) {
+      // one 32x32 MFMA block at a time, so the previous values of H take
+      // 32 registers beside the master copy instead of 128
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          double old[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int gi = ti * kTile + dma_row(wm, i, r, lane), gj = tj * kTile + dma_col(wn, j, lane);
+            const bool own = gi < n && gj < n && !(diag && gi > gj);
+            old[r] = (beta != 0.0 && own) ? H[static_cast<int64_t>(gi) * n + gj] : 0.0;
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int lr = dma_row(wm, i, r, lane), lc = j * 32 + (lane & 31);
+            const int gi = ti * kTile + lr, gj = tj * kTile + half * 64 + lc;
+            double v = alpha * master[i][j][r];
+            const bool own = gi < n && gj < n && !(diag && gi > gj);
+            if (own) {
+              if (beta != 0.0) v += beta * old[r];
+              H[static_cast<int64_t>(gi) * n + gj] = v;
+            }
+            stage[lc * kTile + (lr ^ lc)] = v;
+          }
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < 64 * kTile; e += kDThreads) {
+      const int c = e >> 7, r = e & 127;
+      const int gi = ti * kTile + r, gjj = tj * kTile + half * 64 + c;
+      if (gi < n && gjj < n && gi < gjj) H[static_cast<int64_t>(gjj) * n + gi] = stage[c * kTile + (r ^ c)];
+    }
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ void tile_store_partial_dma(const double (&master)[2][2][16], double* __restrict__ dst) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave & 1, wn = wave >> 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dst[dma_row(wm, i, r, lane) * kTile + dma_col(wn, j, lane)] = master[i][j][r];
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kDThreads) __attribute__((amdgpu_waves_per_eu(2)))
+syrk_dma_kernel(const uint16_t* __restrict__ X, int64_t ldx, int n, int64_t tokens, HessSched sc, int pieces,
+                double alpha, double beta, double* __restrict__ H, double* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kDLds];
+  const int b = blockIdx.x;
+  int idx;
+  int64_t p0 = 0, p1 = tokens;
+  bool partial_out = false;
+  if (!pieces) {
+    const int r = b / sc.P, s = b % sc.P;
+    idx = r * sc.P + ((sc.P % 8 == 0) ? (s % 8) * (sc.P / 8) + s / 8 : s);
+  } else {
+    idx = sc.R * sc.P + b / sc.S;
+    if (sc.S > 1) {
+      partial_out = true;
+      p0 = (b % sc.S) * sc.chunk;
+      p1 = (p0 + sc.chunk < tokens) ? p0 + sc.chunk : tokens;
+    }
+  }
+  int ti, tj;
+  sched_tile(idx, sc.nt, sc.sbr, ti, tj);
+  double master[2][2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) master[i][j][e] = 0.0;
+  if (ti == tj) tile_accumulate_dma<DT, true>(X, ldx, n, ti, tj, p0, p1, lds, master);
+  else tile_accumulate_dma<DT, false>(X, ldx, n, ti, tj, p0, p1, lds, master);
+  if (partial_out) tile_store_partial_dma(master, partial + static_cast<int64_t>(b) * kTile * kTile);
+  else tile_epilogue_dma(master, ti, tj, n, alpha, beta, H, lds);
+}
+
 // Leftover tiles split into S pieces: sum the pieces in piece order (fp64),
 // apply H <- beta*H + alpha*sum, write tile and mirror.  grid = (L, 4 quarters).
 __global__ void __launch_bounds__(256) syrk_reduce_kernel(const double* __restrict__ partial, HessSched sc, int n,
@@ -362,7 +673,7 @@ __global__ void __launch_bounds__(256) syrk_reduce_kernel(const double* __restri
   const int q = blockIdx.x;
   const int w = blockIdx.y;
   int ti, tj;
-  sched_tile(sc.R * sc.P + q, sc.nt, ti, tj);
+  sched_tile(sc.R * sc.P + q, sc.nt, sc.sbr, ti, tj);
   const bool diag = (ti == tj);
   const int rw = (w >> 1) * 64, cw = (w & 1) * 64;
   const int tid = threadIdx.x;
@@ -448,12 +759,15 @@ static int device_cus() {
   return cus;
 }
 
-static HessSched make_sched(int64_t n, int64_t tokens) {
+// per_cu: work-groups resident on one compute unit (1 for syrk_mfma_kernel,
+// 2 for syrk_dma_kernel).
+static HessSched make_sched(int64_t n, int64_t tokens, int per_cu) {
   HessSched sc{};
   sc.nt = static_cast<int>((n + kTile - 1) / kTile);
   sc.T = static_cast<int>(upper_tiles(sc.nt));
-  const int cus = device_cus();
-  sc.P = sc.T < cus ? sc.T : cus;
+  const int slots = device_cus() * per_cu;
+  sc.P = sc.T < slots ? sc.T : slots;
+  sc.sbr = 4 * per_cu;
   sc.R = sc.T / sc.P;
   sc.L = sc.T % sc.P;
   sc.S = sc.L > 0 ? sc.P / sc.L : 0;
@@ -467,11 +781,15 @@ static HessSched make_sched(int64_t n, int64_t tokens) {
   return sc;
 }
 
+static size_t sched_workspace(const HessSched& sc) {
+  return sc.S <= 1 ? 0 : static_cast<size_t>(sc.L) * sc.S * kTile * kTile * sizeof(double);
+}
+
+// Enough for either path: which one runs depends on X's alignment.
 size_t hessian_workspace(int64_t n, int64_t tokens, int dt) {
   if (dt == DT_FP32 || n <= 0 || tokens <= 0) return 0;
-  const HessSched sc = make_sched(n, tokens);
-  if (sc.S <= 1) return 0;
-  return static_cast<size_t>(sc.L) * sc.S * kTile * kTile * sizeof(double);
+  const size_t a = sched_workspace(make_sched(n, tokens, 1)), b = sched_workspace(make_sched(n, tokens, 2));
+  return a > b ? a : b;
 }
 
 hipError_t launch_hessian(double* H, int64_t n, const void* X, int dt, int64_t tokens, int64_t ldx, double alpha,
@@ -482,11 +800,47 @@ hipError_t launch_hessian(double* H, int64_t n, const void* X, int dt, int64_t t
                        static_cast<const float*>(X), ldx, static_cast<int>(n), tokens, nt64, alpha, beta, H);
     return hipGetLastError();
   }
-  const HessSched sc = make_sched(n, tokens);
   const int vec_ok = (ldx % 8 == 0) && (reinterpret_cast<uintptr_t>(X) % 16 == 0);
   double* partial = static_cast<double*>(ws);
-  auto kern = (dt == DT_BF16) ? syrk_mfma_kernel<DT_BF16> : syrk_mfma_kernel<DT_FP16>;
   const uint16_t* Xp = static_cast<const uint16_t*>(X);
+  // the direct-to-LDS path: whole 8-feature chunks, 32-bit byte offsets
+  // within a stage
+  if (vec_ok && n % 8 == 0 && ldx <= (int64_t{1} << 24)) {
+    // Token chunks of about 256 MB of X each (16384 to 65536 tokens), one
+    // pass over all tiles per chunk, the first applying beta and the rest
+    // adding on: a work-group then walks at most one chunk of tokens, so the
+    // work-groups sharing an XCD stay close enough in token position to find
+    // each other's operand panels in its L2.  Over long token ranges they
+    // drift apart, and the operand traffic (measured: twice the fetched bytes
+    // at 11008 features x 65536 tokens) outweighs the chunk's extra read and
+    // write of H.
+    int64_t chunk = ((int64_t{1} << 28) / n) / 256 * 256;
+    chunk = chunk < 16384 ? 16384 : (chunk > 65536 ? 65536 : chunk);
+    auto kd = (dt == DT_BF16) ? syrk_dma_kernel<DT_BF16> : syrk_dma_kernel<DT_FP16>;
+    for (int64_t c0 = 0; c0 < tokens; c0 += chunk) {
+      const int64_t tc = (tokens - c0 < chunk) ? tokens - c0 : chunk;
+      const double bc = (c0 == 0) ? beta : 1.0;
+      const uint16_t* Xc = Xp + c0 * ldx;
+      const HessSched sc = make_sched(n, tc, 2);
+      hipLaunchKernelGGL(kd, dim3(sc.R * sc.P), dim3(kDThreads), 0, s, Xc, ldx, static_cast<int>(n), tc, sc, 0, alpha,
+                         bc, H, partial);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      if (sc.L == 0) continue;
+      hipLaunchKernelGGL(kd, dim3(sc.L * sc.S), dim3(kDThreads), 0, s, Xc, ldx, static_cast<int>(n), tc, sc, 1, alpha,
+                         bc, H, partial);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      if (sc.S <= 1) continue;
+      hipLaunchKernelGGL(syrk_reduce_kernel, dim3(sc.L, 4), dim3(256), 0, s, partial, sc, static_cast<int>(n), alpha,
+                         bc, H);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const HessSched sc = make_sched(n, tokens, 1);
+  auto kern = (dt == DT_BF16) ? syrk_mfma_kernel<DT_BF16> : syrk_mfma_kernel<DT_FP16>;
   hipLaunchKernelGGL(kern, dim3(sc.R * sc.P), dim3(kThreads), 0, s, Xp, ldx, static_cast<int>(n), tokens, sc, 0, vec_ok,
                      alpha, beta, H, partial);
   hipError_t e = hipGetLastError();

@@ -38,8 +38,10 @@ def test_exports_every_declared_symbol(g):
 
 def test_workspace_queries(g):
     cfg = g.Config()
-    # 528 tiles on 256 compute units: 16 leftover tiles in 16 token pieces of 128x128 fp64
-    assert g.gptq_hessian_workspace_bytes(4096, 65536, g.GPTQ_BF16) == 16 * 16 * 128 * 128 * 8
+    # 528 tiles of 128x128 on 256 compute units: 16 tiles left over after the
+    # rounds, cut into token pieces with fp64 partials; the larger of the two
+    # kernels' needs (16 pieces each at one work-group per compute unit, 32 at two)
+    assert g.gptq_hessian_workspace_bytes(4096, 65536, g.GPTQ_BF16) == 16 * 32 * 128 * 128 * 8
     assert g.gptq_hessian_workspace_bytes(4096, 65536, g.GPTQ_FP32) == 0
     assert g.gptq_hessian_workspace_bytes(256, 65536, g.GPTQ_BF16) == 0   # 3 tiles: one round
     assert g.gptq_hessian_chain_tokens() == 256

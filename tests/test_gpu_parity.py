@@ -42,7 +42,8 @@ def _ocfg(wl):
 
 # --------------------------------------------------------------------------- Hessian
 @pytest.mark.parametrize("name,n,tokens", [("toy256", None, None), ("attn4096", 300, 1000),
-                                           ("attn4096", 640, 5000), ("mlpdown11008", 257, 333)])
+                                           ("attn4096", 640, 5000), ("mlpdown11008", 257, 333),
+                                           ("attn4096", 4104, 3001)])
 def test_hessian_matches_oracle(g, name, n, tokens):
     import torch
     wl = synth.get(name)
