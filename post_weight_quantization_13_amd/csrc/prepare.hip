@@ -732,6 +732,8 @@ constexpr int kT2 = 128;
 constexpr int kBigTiles = 512;
 // LDS requested per work-group of the overlapped top level of the inverse
 constexpr int kTopLds = 96 * 1024;
+// largest top-level split h whose first product runs on part of the chip
+constexpr int kTopSplitMax = 2048;
 static_assert(kTopLds >= static_cast<int>(sizeof(TileSmem)) && kTopLds + static_cast<int>(sizeof(TileSmem)) > 160 * 1024,
               "top-level LDS");
 template <int KC>
@@ -1046,9 +1048,10 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
   // product T = L21 X11 need only block columns < h of L, so they run on a
   // second side stream as soon as the step for block column h/64 - 1 is done,
   // beside the rest of the factorization, which writes nothing they read.
-  // The first product runs on 3/8 of the compute units, each held whole, so
-  // the strips and steps keep the rest.  The levels inside [h, n) and the top
-  // level's second product follow the factorization on the caller's stream.
+  // For h <= 2048 the first product runs on 3/8 of the compute units, each
+  // held whole, so the strips and steps keep the rest; for larger h on the
+  // whole chip.  The levels inside [h, n) and the top level's second product
+  // follow the factorization on the caller's stream.
   auto level = [&](int sz, int phase, int pair0, int npairs, hipStream_t st) -> hipError_t {
     if (npairs <= 0) return hipSuccess;
     if (sz < kT2 || npairs * (sz / kT2) * (sz / kT2) < kBigTiles) {
@@ -1087,10 +1090,18 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
           e = level(sz, 0, 0, h / (2 * sz), side2);
           if (e == hipSuccess) e = level(sz, 1, 0, h / (2 * sz), side2);
         }
-        // the top level's first product, on a few compute units held whole
-        // (enough LDS per work-group that no step, strip or trailing-pass
-        // work-group fits beside one), long before the factorization ends
-        if (e == hipSuccess) {
+        // the top level's first product, long before the factorization ends:
+        // up to h = 2048, on a few compute units held whole (enough LDS per
+        // work-group that no step, strip or trailing-pass work-group fits
+        // beside one), since the panel steps left after block column h are a
+        // long latency-bound chain beside a small product; beyond that on the
+        // whole chip, since the product (about h^3/2 flop) then outweighs the
+        // rest of the factorization, which finishes early and would wait for
+        // it (measured: 502 -> 354 ms at n = 28672, 13.4 -> 12.3 ms at 8192,
+        // but 2.95 -> 3.7 ms at 4096)
+        if (e == hipSuccess && h > kTopSplitMax) {
+          e = level(h, 0, 0, 1, side2);
+        } else if (e == hipSuccess) {
           const int tiles = (h / kB) * (h / kB);
           const int wgs = (top_wgs < tiles) ? top_wgs : tiles;
           hipLaunchKernelGGL(trtri_level_kernel, dim3(1, wgs), dim3(256), kTopLds - sizeof(TileSmem), side2, A, Linv, n,
