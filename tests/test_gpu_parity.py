@@ -62,6 +62,32 @@ def test_hessian_matches_oracle(g, name, n, tokens):
     assert np.array_equal(Hg, Hg.T)
 
 
+def test_hessian_token_chunks_pieces_and_tails(g):
+    """n = 8200 (65 tile rows: rounds of whole tiles plus leftover tiles cut
+    into token pieces, a ragged last feature tile) over 40001 tokens, which
+    the direct-to-LDS kernel splits into token chunks with a ragged last one.
+    Compared with the oracle on a sampled set of 96 features (all pairs among
+    them, including features of the ragged tile and at tile boundaries);
+    H must also be exactly symmetric."""
+    import torch
+    wl = synth.get("attn4096").resized(rows=8, n=8200, tokens=40001)
+    raw = synth.activations_raw(wl)
+    rng = np.random.default_rng(8200)
+    cols = np.unique(np.concatenate([[0, 127, 128, 8191, 8192, 8199],
+                                     rng.choice(8200, size=90, replace=False)]))
+    Href, _ = oracle.hessian(synth.bf16_value(raw[:, cols]))
+    H = torch.empty((8200, 8200), dtype=torch.float64, device="cuda")
+    assert g.gptq_hessian_accumulate(H, 0, to_device(raw, "bf16")) == 40001
+    del raw
+    torch.cuda.synchronize()
+    assert torch.equal(H, H.T)
+    idx = torch.from_numpy(cols).cuda()
+    sub = H[idx][:, idx].cpu().numpy()
+    err = rel_frobenius(sub, Href)
+    print(f"n=8200 tokens=40001: sampled H rel Frobenius {err:.3e}")
+    assert err <= 1e-5
+
+
 def test_hessian_chunked_and_fp16(g):
     import torch
     wl = synth.get("attn4096").resized(rows=8, n=384, tokens=3000)
