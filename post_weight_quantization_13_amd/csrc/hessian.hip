@@ -666,36 +666,35 @@ syrk_dma_kernel(const uint16_t* __restrict__ X, int64_t ldx, int n, int64_t toke
 }
 
 // Leftover tiles split into S pieces: sum the pieces in piece order (fp64),
-// apply H <- beta*H + alpha*sum, write tile and mirror.  grid = (L, 4 quarters).
+// apply H <- beta*H + alpha*sum, write tile and mirror.  grid = (L, 64): one
+// 16x16 block of a tile per work-group, one element per thread, so the S
+// loads of every element are in flight together across the whole chip.
 __global__ void __launch_bounds__(256) syrk_reduce_kernel(const double* __restrict__ partial, HessSched sc, int n,
                                                           double alpha, double beta, double* __restrict__ H) {
-  __shared__ double stage[64 * 64];
+  __shared__ double stage[16 * 17];  // [column][row], padded
   const int q = blockIdx.x;
   const int w = blockIdx.y;
   int ti, tj;
   sched_tile(sc.R * sc.P + q, sc.nt, sc.sbr, ti, tj);
   const bool diag = (ti == tj);
-  const int rw = (w >> 1) * 64, cw = (w & 1) * 64;
+  const int rb = (w >> 3) * 16, cb = (w & 7) * 16;
   const int tid = threadIdx.x;
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int lr = e >> 6, lc = e & 63;
-    const int gi = ti * kTile + rw + lr, gj = tj * kTile + cw + lc;
-    double s = 0.0;
-    for (int p = 0; p < sc.S; ++p)
-      s += partial[static_cast<int64_t>(q * sc.S + p) * kTile * kTile + (rw + lr) * kTile + cw + lc];
-    double v = alpha * s;
-    if (gi < n && gj < n && !(diag && gi > gj)) {
-      if (beta != 0.0) v += beta * H[static_cast<int64_t>(gi) * n + gj];
-      H[static_cast<int64_t>(gi) * n + gj] = v;
-    }
-    stage[lc * 64 + (lr ^ lc)] = v;
+  const int lr = tid >> 4, lc = tid & 15;
+  const int gi = ti * kTile + rb + lr, gj = tj * kTile + cb + lc;
+  const double* src = partial + static_cast<int64_t>(q) * sc.S * kTile * kTile + (rb + lr) * kTile + cb + lc;
+  double s = 0.0;
+  for (int p = 0; p < sc.S; ++p) s += src[static_cast<int64_t>(p) * kTile * kTile];
+  double v = alpha * s;
+  if (gi < n && gj < n && !(diag && gi > gj)) {
+    if (beta != 0.0) v += beta * H[static_cast<int64_t>(gi) * n + gj];
+    H[static_cast<int64_t>(gi) * n + gj] = v;
   }
+  stage[lc * 17 + lr] = v;
   __syncthreads();
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int lc = e >> 6, lr = e & 63;
-    const int gi = ti * kTile + rw + lr, gj = tj * kTile + cw + lc;
-    if (gi < n && gj < n && gi < gj) H[static_cast<int64_t>(gj) * n + gi] = stage[lc * 64 + (lr ^ lc)];
-  }
+  // mirror: thread (c, r) = (tid / 16, tid % 16) writes H[col][row], rows consecutive
+  const int c = tid >> 4, r = tid & 15;
+  const int mi = ti * kTile + rb + r, mj = tj * kTile + cb + c;
+  if (mi < n && mj < n && mi < mj) H[static_cast<int64_t>(mj) * n + mi] = stage[c * 17 + r];
 }
 
 // fp32 inputs: 64x64 tiles of the upper triangle, fp64 accumulation on the VALU.
@@ -832,7 +831,7 @@ hipError_t launch_hessian(double* H, int64_t n, const void* X, int dt, int64_t t
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       if (sc.S <= 1) continue;
-      hipLaunchKernelGGL(syrk_reduce_kernel, dim3(sc.L, 4), dim3(256), 0, s, partial, sc, static_cast<int>(n), alpha,
+      hipLaunchKernelGGL(syrk_reduce_kernel, dim3(sc.L, 64), dim3(256), 0, s, partial, sc, static_cast<int>(n), alpha,
                          bc, H);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -849,7 +848,7 @@ hipError_t launch_hessian(double* H, int64_t n, const void* X, int dt, int64_t t
                      alpha, beta, H, partial);
   e = hipGetLastError();
   if (e != hipSuccess || sc.S <= 1) return e;
-  hipLaunchKernelGGL(syrk_reduce_kernel, dim3(sc.L, 4), dim3(256), 0, s, partial, sc, static_cast<int>(n), alpha,
+  hipLaunchKernelGGL(syrk_reduce_kernel, dim3(sc.L, 64), dim3(256), 0, s, partial, sc, static_cast<int>(n), alpha,
                      beta, H);
   return hipGetLastError();
 }
