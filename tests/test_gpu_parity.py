@@ -88,6 +88,36 @@ def test_hessian_token_chunks_pieces_and_tails(g):
     assert err <= 1e-5
 
 
+@pytest.mark.parametrize("n", [640, 300, 4104])
+def test_hessian_graph_replay(g, n):
+    """The Hessian call captured in a graph and replayed several times with
+    eager work in between: every replay equals the eager result bitwise.
+    n = 640 and 4104 take the direct-to-LDS kernel (4104 also its leftover-tile
+    pieces and their reduction), n = 300 the register-staged one."""
+    import torch
+    wl = synth.get("attn4096").resized(rows=8, n=n, tokens=5000)
+    xd = to_device(synth.activations_raw(wl), "bf16")
+    ws = g.hessian_workspace(n, xd)
+    eager = torch.empty((n, n), dtype=torch.float64, device="cuda")
+    g.gptq_hessian_accumulate(eager, 0, xd, workspace=ws)
+    H = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g.gptq_hessian_accumulate(H, 0, xd, workspace=ws)      # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.gptq_hessian_accumulate(H, 0, xd, workspace=ws)
+    for i in range(4):
+        H.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(H, eager), i
+        _ = (xd.float() * 2).sum().item()                      # eager work between replays
+
+
 def test_hessian_chunked_and_fp16(g):
     import torch
     wl = synth.get("attn4096").resized(rows=8, n=384, tokens=3000)
