@@ -96,27 +96,44 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
 // and the XCD's L2 serves most operand loads: 32 work-groups (one per
 // compute unit) on a 4 x 8 super-block need about 12 panels instead of 33;
 // 64 (two per compute unit) on an 8 x 8 one, 16 instead of 24 on two 4 x 8.
-// index -> (ti, tj), O(#super-blocks).
+// index -> (ti, tj): whole super-block rows skipped by their tile counts in
+// closed form, then super-blocks of that row, then tile rows.
 __device__ void sched_tile(int idx, int nt, int sbr, int& ti, int& tj) {
   constexpr int sbc = 8;
   const int nsr = (nt + sbr - 1) / sbr, nsc = (nt + sbc - 1) / sbc;
   int rem = idx;
   ti = 0;
   tj = 0;
-  for (int SR = 0; SR < nsr; ++SR) {
-    const int a_end = (sbr * SR + sbr < nt) ? sbr * SR + sbr : nt;
-    for (int SC = (sbr * SR) / sbc; SC < nsc; ++SC) {
-      const int c_hi = (sbc * SC + sbc < nt) ? sbc * SC + sbc : nt;
-      for (int a = sbr * SR; a < a_end; ++a) {
-        const int lo = (a > sbc * SC) ? a : sbc * SC;
-        const int cnt = (c_hi > lo) ? c_hi - lo : 0;
-        if (rem < cnt) {
-          ti = a;
-          tj = lo + rem;
-          return;
-        }
-        rem -= cnt;
+  // super-block row: its rows a0 .. a1-1 hold sum (nt - a) tiles
+  int SR = 0, a0 = 0, a1 = 0;
+  for (; SR < nsr; ++SR) {
+    a0 = sbr * SR;
+    a1 = (a0 + sbr < nt) ? a0 + sbr : nt;
+    const int cnt = (a1 - a0) * nt - (a0 + a1 - 1) * (a1 - a0) / 2;
+    if (rem < cnt) break;
+    rem -= cnt;
+  }
+  if (SR >= nsr) return;
+  for (int SC = a0 / sbc; SC < nsc; ++SC) {
+    const int c_lo = sbc * SC, c_hi = (c_lo + sbc < nt) ? c_lo + sbc : nt;
+    int cnt = 0;
+    for (int a = a0; a < a1; ++a) {
+      const int lo = (a > c_lo) ? a : c_lo;
+      cnt += (c_hi > lo) ? c_hi - lo : 0;
+    }
+    if (rem >= cnt) {
+      rem -= cnt;
+      continue;
+    }
+    for (int a = a0; a < a1; ++a) {
+      const int lo = (a > c_lo) ? a : c_lo;
+      const int c = (c_hi > lo) ? c_hi - lo : 0;
+      if (rem < c) {
+        ti = a;
+        tj = lo + rem;
+        return;
       }
+      rem -= c;
     }
   }
 }
