@@ -37,14 +37,35 @@ constexpr int kSub = 16;      // sub-block kept in registers inside the sweep
 constexpr int kRowsSweep = 64;
 
 // ---------------------------------------------------------------- gather
+// Wk[r][j] = W[r][perm[j]] as fp32 (0 for dead columns).  Four consecutive
+// output columns per thread, written as one 16-byte store when n % 4 == 0
+// and Wk is 16-byte aligned (every row start then is), else one by one.
 template <int DT>
 __global__ void gather_w_kernel(const void* __restrict__ W, int64_t ldw, const int32_t* __restrict__ perm,
                                 const uint8_t* __restrict__ dead, int rows, int n, float* __restrict__ Wk) {
+  const int nq = (n + 3) / 4;
+  const bool vec = (n % 4) == 0 && (reinterpret_cast<uintptr_t>(Wk) & 15) == 0;
   for (int r = blockIdx.y; r < rows; r += gridDim.y) {
-    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
-      const int src = perm[j];
-      float v = dead[src] ? 0.0f : load_as_float<DT>(W, static_cast<int64_t>(r) * ldw + src);
-      Wk[static_cast<int64_t>(r) * n + j] = v;
+    for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += gridDim.x * blockDim.x) {
+      const int j0 = 4 * q;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + e;
+        v[e] = 0.0f;
+        if (j < n) {
+          const int src = perm[j];
+          if (!dead[src]) v[e] = load_as_float<DT>(W, static_cast<int64_t>(r) * ldw + src);
+        }
+      }
+      float* dst = Wk + static_cast<int64_t>(r) * n + j0;
+      if (vec) {
+        *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j0 + e < n) dst[e] = v[e];
+      }
     }
   }
 }
@@ -806,7 +827,7 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
   } while (0)
   e = zero_words(rowloss, static_cast<size_t>(rows), s);
   if (e != hipSuccess) return e;
-  dim3 gg((n + 255) / 256, rows < 65535 ? rows : 65535);
+  dim3 gg(((n + 3) / 4 + 255) / 256, rows < 65535 ? rows : 65535);
   if (wdt == DT_BF16) hipLaunchKernelGGL(gather_w_kernel<DT_BF16>, gg, dim3(256), 0, s, W, ldw, perm, dead, rows, n, Wk);
   else if (wdt == DT_FP16) hipLaunchKernelGGL(gather_w_kernel<DT_FP16>, gg, dim3(256), 0, s, W, ldw, perm, dead, rows, n, Wk);
   else hipLaunchKernelGGL(gather_w_kernel<DT_FP32>, gg, dim3(256), 0, s, W, ldw, perm, dead, rows, n, Wk);
