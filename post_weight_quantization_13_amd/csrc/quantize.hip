@@ -132,11 +132,17 @@ __global__ void __launch_bounds__(256) split_ut_kernel(const float* __restrict__
 }
 
 // Staged operand planes: rows of 64 bf16 values (128 bytes = eight 16-byte
-// units of 8 k); unit u of row r sits at slot u ^ (r & 7), so the 16-byte
-// stores (8 lanes on one row) and the fragment reads (8 lanes on 8
-// consecutive rows) each touch 8 distinct 16-byte bank groups.
+// units of 8 k); unit u of row r sits at slot u ^ ((r >> 1) & 7).  LDS has
+// 64 banks of 4 bytes and serves 16 lanes of a 16-byte access per cycle: the
+// fragment reads (16 lanes on 16 consecutive rows, one unit) then touch 16
+// distinct 16-byte bank groups (even and odd rows fall in different halves
+// of 256 bytes, and the 8 rows of one parity on 8 slots), as do the stores
+// (16 lanes on two rows, all eight units of each).  Keyed on r & 7 instead,
+// rows r and r + 8 shared a slot and every read took two cycles.
 constexpr int kTK = 64;
-__device__ __forceinline__ int tk_offset(int row, int c) { return row * (kTK * 2) + ((c ^ (row & 7)) << 4); }
+__device__ __forceinline__ int tk_offset(int row, int c) {
+  return row * (kTK * 2) + ((c ^ ((row >> 1) & 7)) << 4);
+}
 
 // ---------------------------------------------------------------- pending block update
 // Before its chain, a sweep workgroup applies to its own 64 rows x 128
