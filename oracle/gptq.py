@@ -198,7 +198,18 @@ def quantize_column(w, s, z, bits, sym, qdtype=np.float64):
 # ---------------------------------------------------------------------------
 # The column sweep
 # ---------------------------------------------------------------------------
-def sweep(Wp, U, cfg: QuantConfig, qdtype=np.float64, block=None, stop=None):
+def _tie_between(t, c, alt, tol):
+    """True where ``alt`` is the other neighbour of the rounding of ``t`` to
+    ``c`` and ``t`` lies within ``tol`` of the midpoint between them: both are
+    then nearest points within an arithmetic error of ``tol`` (the pages fix no
+    rounding precision, so either is a correct result)."""
+    t = np.asarray(t, dtype=np.float64)
+    mid = np.minimum(c, alt) + 0.5
+    return (np.abs(alt - c) == 1) & (np.abs(t - mid) <= tol)
+
+
+def sweep(Wp, U, cfg: QuantConfig, qdtype=np.float64, block=None, stop=None, follow=None, tie_tol=None,
+          record=False):
     """GPTQ column sweep over W already in sweep order.
 
     [polydesk] "Étape 1 : Ordre arbitraire": all rows visit the columns in the
@@ -219,6 +230,32 @@ def sweep(Wp, U, cfg: QuantConfig, qdtype=np.float64, block=None, stop=None):
     ``qdtype``, What [rows, n] float64 in sweep order, E [rows, n], L) where
     L = sum of e^2 / 2.  With ``stop=k`` (unblocked only) the sweep ends after
     k columns and the working matrix is returned as ``W``.
+
+    Several correct results.  A quotient w/s that lies on a rounding midpoint
+    has two nearest codes, and the same holds for a zero point -xmin/s; a
+    solver whose arithmetic differs from this float64 path by a small amount
+    may therefore take the other code where the quotient is within that
+    amount of a midpoint, and its later columns then follow from that choice.
+    ``follow`` (dict with "codes" [rows, n] in sweep order and optionally
+    "zeros" [n/gs, rows]) names such another result; at each decision where
+    it differs, the sweep takes the followed choice only if it is the other
+    neighbour and the position lies within the tolerance of the midpoint:
+      codes:  tol_j = tie_tol * (|w0_j| + sum_{k<j} |e_k| |U_kj|) / s,
+              w0 the column's weight before any compensation, e the errors
+              of the columns already quantized on this path;
+      zeros:  tol = 2 * tie_tol * (tol scale at the group's argmin column +
+              at its argmax column), from the first-order error of -xmin/s.
+    ``tie_tol`` is the relative arithmetic error allowed on the magnitudes
+    that make up the compensated weight.  Otherwise it keeps its own choice.
+    The result then carries "follow" = dict(ties, zero_ties, unexplained,
+    ratio_max): how many choices were taken from ``follow`` as verified ties,
+    how many differing choices were not ties (kept), and the largest
+    |distance to the midpoint| / tol among the ties taken.
+    ``record=True`` (unblocked only) also returns, in sweep order, the
+    position of every decision on its own path: "t" [rows, n] = w/s + z before
+    rounding, "tol_scale" [rows, n] = (|w0_j| + sum_k |e_k||U_kj|) / s, and for
+    the asymmetric grid "zq" [G, rows] = -xmin/s and "zq_scale" [G, rows] =
+    2 * (tol_scale at the group's argmin column + at its argmax column).
     """
     W = np.array(Wp, dtype=np.float64, copy=True)
     rows, n = W.shape
@@ -236,6 +273,25 @@ def sweep(Wp, U, cfg: QuantConfig, qdtype=np.float64, block=None, stop=None):
     s = z = None
     if stop is not None and block is not None:
         raise ValueError("stop is only defined for the unblocked sweep")
+    tracking = follow is not None or record
+    if tracking:
+        if block is not None:
+            raise ValueError("follow and record are only defined for the unblocked sweep")
+        w0 = np.abs(W)
+        A = np.zeros_like(W)            # sum_k |e_k| |U_kj| over the quantized columns k < j
+    if follow is not None:
+        f_codes = np.asarray(follow["codes"], dtype=np.int64)
+        f_zeros = follow.get("zeros")
+        tau = float(tie_tol)
+        fst = dict(ties=0, zero_ties=0, unexplained=0, ratio_max=0.0)
+    else:
+        f_codes = f_zeros = None
+    if record:
+        rec_t = np.zeros((rows, n))
+        rec_scale = np.zeros((rows, n))
+        rec_zq = np.zeros((ngroups, rows))
+        rec_zs = np.zeros((ngroups, rows))
+    dt = np.dtype(qdtype).type
     for i1 in range(0, n, B):
         i2 = min(i1 + B, n)
         for j in range(i1, i2):
@@ -243,21 +299,65 @@ def sweep(Wp, U, cfg: QuantConfig, qdtype=np.float64, block=None, stop=None):
                 return dict(W=W, codes=codes, E=E, L=loss)
             if j % gs == 0:
                 s, z = grid_params(W[:, j:j + gs], cfg.bits, cfg.sym, qdtype)
+                if tracking and not cfg.sym:
+                    wg = W[:, j:j + gs]
+                    scale = (w0[:, j:j + gs] + A[:, j:j + gs]) / np.abs(s)[:, None]
+                    r = np.arange(rows)
+                    zscale = 2 * (scale[r, wg.argmin(axis=1)] + scale[r, wg.argmax(axis=1)])
+                    xmin = np.minimum(wg.astype(dt).min(axis=1), dt(0))
+                    if record:
+                        rec_zq[j // gs] = -xmin / s
+                        rec_zs[j // gs] = zscale
+                if f_zeros is not None and not cfg.sym:
+                    tol = tau * zscale
+                    alt = np.asarray(f_zeros[j // gs], dtype=np.float64)
+                    ok = _tie_between(-xmin / s, z, alt, tol)
+                    differ = alt != z
+                    fst["zero_ties"] += int(np.sum(differ & ok))
+                    fst["unexplained"] += int(np.sum(differ & ~ok))
+                    if np.any(differ & ok):
+                        m = np.abs(-xmin / s - (np.minimum(z, alt) + 0.5)) / tol
+                        fst["ratio_max"] = max(fst["ratio_max"], float(m[differ & ok].max()))
+                    z = np.where(differ & ok, alt, z).astype(z.dtype)
                 S[j // gs] = s
                 Z[j // gs] = z
             c, q = quantize_column(W[:, j], s, z, cfg.bits, cfg.sym, qdtype)
+            if record:
+                rec_t[:, j] = W[:, j].astype(dt) / s + z
+                rec_scale[:, j] = (w0[:, j] + A[:, j]) / np.abs(s)
+            if f_codes is not None:
+                alt = f_codes[:, j]
+                t = W[:, j].astype(dt) / s + z
+                tol = tau * (w0[:, j] + A[:, j]) / np.abs(s)
+                ok = _tie_between(t, c, alt, tol)
+                differ = alt != c
+                fst["ties"] += int(np.sum(differ & ok))
+                fst["unexplained"] += int(np.sum(differ & ~ok))
+                if np.any(differ & ok):
+                    m = np.abs(t - (np.minimum(c, alt) + 0.5)) / tol
+                    fst["ratio_max"] = max(fst["ratio_max"], float(m[differ & ok].max()))
+                    c = np.where(differ & ok, alt, c)
+                    q = (s * (c.astype(dt) - z)).astype(dt).astype(np.float64)
             e = (W[:, j] - q) / U[j, j]
             W[:, j + 1:i2] -= np.outer(e, U[j, j + 1:i2])
+            if tracking:
+                A[:, j + 1:] += np.outer(np.abs(e), np.abs(U[j, j + 1:]))
             codes[:, j] = c
             What[:, j] = q
             E[:, j] = e
             loss += 0.5 * float(e @ e)
         if i2 < n:
             W[:, i2:] -= E[:, i1:i2] @ U[i1:i2, i2:]
-    return dict(codes=codes, S=S, Z=Z, What=What, E=E, L=loss)
+    out = dict(codes=codes, S=S, Z=Z, What=What, E=E, L=loss)
+    if follow is not None:
+        out["follow"] = fst
+    if record:
+        out.update(t=rec_t, tol_scale=rec_scale, zq=rec_zq, zq_scale=rec_zs)
+    return out
 
 
-def quantize_layer(W, U, perm, dead, cfg: QuantConfig, qdtype=np.float64, block=None):
+def quantize_layer(W, U, perm, dead, cfg: QuantConfig, qdtype=np.float64, block=None, follow=None,
+                   tie_tol=None, record=False):
     """One layer: zero dead columns, permute, sweep, and return the outputs in
     the original column order.
 
@@ -269,13 +369,17 @@ def quantize_layer(W, U, perm, dead, cfg: QuantConfig, qdtype=np.float64, block=
         original column is the sweep group that quantized it),
       codes int64 [rows, n] in original order, L (internal damped loss),
       What float64 [rows, n] (working-precision grid values, original order).
+    ``follow`` (dict with "codes" [rows, n] in ORIGINAL column order and
+    optionally "zeros" [n/gs, rows]) and ``tie_tol``: see ``sweep``.
     """
     W = np.array(W, dtype=np.float64, copy=True)
     rows, n = W.shape
     perm = np.asarray(perm)
     W[:, np.asarray(dead, dtype=bool)] = 0.0
     Wp = W[:, perm]
-    r = sweep(Wp, U, cfg, qdtype=qdtype, block=block)
+    if follow is not None:
+        follow = dict(follow, codes=np.asarray(follow["codes"])[:, perm])
+    r = sweep(Wp, U, cfg, qdtype=qdtype, block=block, follow=follow, tie_tol=tie_tol, record=record)
     gs = n if cfg.group_size in (-1, 0) else cfg.group_size
     codes = np.empty_like(r["codes"])
     codes[:, perm] = r["codes"]
@@ -283,9 +387,13 @@ def quantize_layer(W, U, perm, dead, cfg: QuantConfig, qdtype=np.float64, block=
     What[:, perm] = r["What"]
     g_idx = np.empty(n, dtype=np.int32)
     g_idx[perm] = np.arange(n) // gs
-    return dict(qweight=pack(codes, cfg.bits), scales=to_fp16(r["S"]), zeros=to_fp16(r["Z"]),
-                g_idx=g_idx, codes=codes, What=What, L=r["L"], S=r["S"], Z=r["Z"],
-                codes_sweep=r["codes"], E=r["E"])
+    out = dict(qweight=pack(codes, cfg.bits), scales=to_fp16(r["S"]), zeros=to_fp16(r["Z"]),
+               g_idx=g_idx, codes=codes, What=What, L=r["L"], S=r["S"], Z=r["Z"],
+               codes_sweep=r["codes"], E=r["E"])
+    for k in ("follow", "t", "tol_scale", "zq", "zq_scale"):
+        if k in r:
+            out[k] = r[k]
+    return out
 
 
 def gptq_layer(W, H, cfg: QuantConfig, qdtype=np.float64, block=None):

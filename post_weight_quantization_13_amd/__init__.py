@@ -159,7 +159,53 @@ def _row_major_2d(t, name):
 
 
 def _cfg(cfg):
-    return ctypes.byref((cfg if isinstance(cfg, Config) else Config(**cfg)).c())
+    return ctypes.byref(_config(cfg).c())
+
+
+def _config(cfg) -> Config:
+    return cfg if isinstance(cfg, Config) else Config(**cfg)
+
+
+def _groups(n: int, group_size: int) -> int:
+    return n // group_size if group_size > 0 else 1
+
+
+def _need(t, name: str, dtype, shape, device) -> None:
+    """Raise ValueError unless ``t`` is a contiguous tensor of exactly this dtype
+    and shape on ``device``: the C side reads and writes through the raw
+    pointer with sizes derived from n, rows and the config, so any other
+    layout would be read or written out of bounds."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor (got {type(t).__name__})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _need_matrix(t, name: str, cols: int, device) -> None:
+    """A 2-D row-major operand (unit column stride, any row stride >= cols)."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D torch tensor")
+    if t.shape[1] != cols:
+        raise ValueError(f"{name} must have {cols} columns (got {t.shape[1]})")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _need_workspace(ws, device) -> int:
+    """Byte size of a workspace tensor (None: 0 bytes)."""
+    if ws is None:
+        return 0
+    if not ws.is_contiguous() or ws.device != device:
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    return ws.numel() * ws.element_size()
 
 
 # ---------------------------------------------------------------- C entry points
@@ -175,12 +221,15 @@ def gptq_hessian_accumulate(H, n_tokens: int, X, workspace="auto", stream=None) 
     """H (float64 [n, n], device) <- running mean of 2 x x^T; returns the new token count.
 
     workspace="auto" allocates the scratch the call needs (a torch tensor)."""
-    n = H.shape[0]
+    import torch
+    n = H.shape[0] if H.dim() == 2 else -1
+    _need(H, "H", torch.float64, (n, n), H.device)
+    _need_matrix(X, "X", n, H.device)
     if isinstance(workspace, str):
         workspace = hessian_workspace(n, X) if X.shape[0] > 0 else None
     ldx = _row_major_2d(X, "X")
     cnt = ctypes.c_int64(int(n_tokens))
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _need_workspace(workspace, H.device)
     _check(lib().gptq_hessian_accumulate(_ptr(H), n, ctypes.byref(cnt), _ptr(X), _dtype_code(X), X.shape[0], ldx,
                                          _ptr(workspace), ws_bytes, _stream(stream, H.device)))
     return cnt.value
@@ -191,9 +240,16 @@ def gptq_prepare_workspace_bytes(n: int, cfg) -> int:
 
 
 def gptq_prepare_hinv(H, cfg, U, perm, dead, workspace, stream=None) -> None:
-    n = H.shape[0]
+    import torch
+    n = H.shape[0] if H.dim() == 2 else -1
+    dev = H.device
+    _need(H, "H", torch.float64, (n, n), dev)
+    _need(U, "U", torch.float32, (n, n), dev)
+    _need(perm, "perm", torch.int32, (n,), dev)
+    _need(dead, "dead", torch.uint8, (n,), dev)
+    ws_bytes = _need_workspace(workspace, dev)
     _check(lib().gptq_prepare_hinv(_ptr(H), n, _cfg(cfg), _ptr(U), _ptr(perm), _ptr(dead), _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), _stream(stream, H.device)))
+                                   ws_bytes, _stream(stream, dev)))
 
 
 def gptq_quantize_workspace_bytes(rows: int, n: int, cfg) -> int:
@@ -203,14 +259,37 @@ def gptq_quantize_workspace_bytes(rows: int, n: int, cfg) -> int:
 def gptq_quantize_layer(U, perm, dead, cfg, W, qweight, scales, zeros, g_idx, workspace, stream=None,
                         want_loss: bool = True):
     """Quantize W; writes qweight/scales/zeros/g_idx; returns the internal loss (or None)."""
+    import torch
+    if W.dim() != 2:
+        raise ValueError("W must be a 2-D tensor")
     rows, n = W.shape
+    c = _config(cfg)
+    dev = W.device
+    _need(U, "U", torch.float32, (n, n), dev)
+    _need(perm, "perm", torch.int32, (n,), dev)
+    _need(dead, "dead", torch.uint8, (n,), dev)
+    _need_outputs(qweight, scales, zeros, g_idx, rows, n, c, dev)
     ldw = _row_major_2d(W, "W")
+    ws_bytes = _need_workspace(workspace, dev)
     loss = ctypes.c_double(0.0)
-    _check(lib().gptq_quantize_layer(_ptr(U), _ptr(perm), _ptr(dead), n, _cfg(cfg), _ptr(W), _dtype_code(W), rows,
+    _check(lib().gptq_quantize_layer(_ptr(U), _ptr(perm), _ptr(dead), n, _cfg(c), _ptr(W), _dtype_code(W), rows,
                                      ldw, _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(g_idx),
                                      ctypes.byref(loss) if want_loss else None, _ptr(workspace),
-                                     workspace.numel() * workspace.element_size(), _stream(stream, W.device)))
+                                     ws_bytes, _stream(stream, dev)))
     return loss.value if want_loss else None
+
+
+def _need_outputs(qweight, scales, zeros, g_idx, rows, n, c: Config, dev) -> None:
+    """The packed outputs of one layer, shaped as gptq_quantize_layer writes them."""
+    import torch
+    words = n * c.bits // 32 if (n * c.bits) % 32 == 0 else -1
+    if words < 0:
+        raise ValueError(f"n={n} with {c.bits}-bit codes does not fill whole int32 words")
+    G = _groups(n, c.group_size)
+    _need(qweight, "qweight", torch.int32, (words, rows), dev)
+    _need(scales, "scales", torch.float16, (G, rows), dev)
+    _need(zeros, "zeros", torch.float16, (G, rows), dev)
+    _need(g_idx, "g_idx", torch.int32, (n,), dev)
 
 
 def gptq_layer_loss_workspace_bytes(rows: int, n: int) -> int:
@@ -218,12 +297,20 @@ def gptq_layer_loss_workspace_bytes(rows: int, n: int) -> int:
 
 
 def gptq_layer_loss(H, W, qweight, scales, zeros, g_idx, cfg, workspace, stream=None) -> float:
+    import torch
+    if W.dim() != 2:
+        raise ValueError("W must be a 2-D tensor")
     rows, n = W.shape
+    c = _config(cfg)
+    dev = W.device
+    _need(H, "H", torch.float64, (n, n), dev)
+    _need_outputs(qweight, scales, zeros, g_idx, rows, n, c, dev)
     ldw = _row_major_2d(W, "W")
+    ws_bytes = _need_workspace(workspace, dev)
     out = ctypes.c_double(0.0)
     _check(lib().gptq_layer_loss(_ptr(H), n, _ptr(W), _dtype_code(W), rows, ldw, _ptr(qweight), _ptr(scales),
-                                 _ptr(zeros), _ptr(g_idx), _cfg(cfg), ctypes.byref(out), _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(), _stream(stream, W.device)))
+                                 _ptr(zeros), _ptr(g_idx), _cfg(c), ctypes.byref(out), _ptr(workspace),
+                                 ws_bytes, _stream(stream, dev)))
     return out.value
 
 
@@ -234,12 +321,19 @@ def gptq_matmul_packed_bytes(rows: int, n: int, bits: int, group_size: int) -> i
 def gptq_matmul_pack(qweight, scales, zeros, g_idx, bits: int, group_size: int, packed, col_order,
                      stream=None) -> bool:
     """Tiled copy of a quantized layer for gptq_matmul; returns True if col_order is the identity."""
+    import torch
+    if qweight.dim() != 2 or g_idx.dim() != 1:
+        raise ValueError("qweight must be 2-D and g_idx 1-D")
     rows = qweight.shape[1]
     n = g_idx.shape[0]
+    dev = qweight.device
+    _need_outputs(qweight, scales, zeros, g_idx, rows, n, Config(bits=bits, group_size=group_size), dev)
+    _need(col_order, "col_order", torch.int32, (n,), dev)
+    packed_bytes = _need_workspace(packed, dev)
     ident = ctypes.c_int32(0)
     _check(lib().gptq_matmul_pack(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(g_idx), rows, n, bits, group_size,
-                                  _ptr(packed), packed.numel() * packed.element_size(), _ptr(col_order),
-                                  ctypes.byref(ident), _stream(stream, qweight.device)))
+                                  _ptr(packed), packed_bytes, _ptr(col_order),
+                                  ctypes.byref(ident), _stream(stream, dev)))
     return bool(ident.value)
 
 
@@ -250,9 +344,20 @@ def gptq_matmul_workspace_bytes(M: int, n: int, has_col_order: bool) -> int:
 def gptq_matmul(A, packed, col_order, rows: int, n: int, bits: int, group_size: int, Y, workspace=None,
                 stream=None) -> None:
     """Y[:M, :rows] = A W_hat^T for fp16 activations A [M, >= n]."""
+    import torch
+    dev = A.device
+    if A.dim() != 2 or A.shape[1] < n:
+        raise ValueError(f"A must be a 2-D tensor with at least n={n} columns")
+    _need_matrix(Y, "Y", rows, dev)
+    if Y.shape[0] != A.shape[0]:
+        raise ValueError(f"Y has {Y.shape[0]} rows, A has {A.shape[0]}")
+    if packed.device != dev or not packed.is_contiguous():
+        raise ValueError(f"packed must be a contiguous tensor on {dev}")
+    if col_order is not None:
+        _need(col_order, "col_order", torch.int32, (n,), dev)
     lda = _row_major_2d(A, "A")
     ldy = _row_major_2d(Y, "Y")
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _need_workspace(workspace, dev)
     _check(lib().gptq_matmul(_ptr(A), _dtype_code(A), A.shape[0], lda, _ptr(packed), _ptr(col_order), rows, n, bits,
                              group_size, _ptr(Y), _dtype_code(Y), ldy, _ptr(workspace), ws_bytes,
                              _stream(stream, A.device)))

@@ -146,3 +146,46 @@ def test_binding_fails_loudly_without_library(monkeypatch, g):
     monkeypatch.setattr(mod, "LIB_PATH", "/nonexistent/libgptq.so")
     with pytest.raises(RuntimeError, match="missing"):
         mod.lib()
+
+
+def test_binding_rejects_mismatched_tensors(g):
+    """The binding checks dtype, shape, contiguity and device of every tensor
+    against (n, rows, bits, group_size) before the C call: a float32 or
+    non-square H, U or outputs sized for another group size, or an X with the
+    wrong feature count would otherwise be read or written out of bounds.
+    Every case below raises ValueError before reaching the library (CPU
+    tensors; nothing is launched)."""
+    import torch
+    n, rows = 256, 8
+    cfg = g.Config(bits=4, group_size=128)
+    f64 = lambda *s: torch.zeros(s, dtype=torch.float64)
+    H, U = f64(n, n), torch.zeros((n, n), dtype=torch.float32)
+    perm, dead = torch.zeros(n, dtype=torch.int32), torch.zeros(n, dtype=torch.uint8)
+    W = torch.zeros((rows, n), dtype=torch.bfloat16)
+    qw = torch.zeros((n * 4 // 32, rows), dtype=torch.int32)
+    sc = torch.zeros((2, rows), dtype=torch.float16)
+    ze = torch.zeros((2, rows), dtype=torch.float16)
+    gi = torch.zeros(n, dtype=torch.int32)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    X = torch.zeros((10, n), dtype=torch.bfloat16)
+    bad = [
+        lambda: g.gptq_hessian_accumulate(H.float(), 0, X, ws),                 # H not fp64
+        lambda: g.gptq_hessian_accumulate(f64(n, n + 1), 0, X, ws),             # H not square
+        lambda: g.gptq_hessian_accumulate(H, 0, X[:, :200], ws),                # X narrower than n
+        lambda: g.gptq_hessian_accumulate(f64(2 * n, n)[::2], 0, X, ws),       # H strided
+        lambda: g.gptq_prepare_hinv(H, cfg, U.double(), perm, dead, ws),        # U not fp32
+        lambda: g.gptq_prepare_hinv(H, cfg, U, perm.long(), dead, ws),          # perm not int32
+        lambda: g.gptq_prepare_hinv(H, cfg, U, perm, dead[:10], ws),            # dead too short
+        lambda: g.gptq_quantize_layer(U, perm, dead, cfg, W, qw, sc[:1], ze, gi, ws),        # scales for gs 256
+        lambda: g.gptq_quantize_layer(U, perm, dead, g.Config(group_size=64), W, qw, sc, ze, gi, ws),
+        lambda: g.gptq_quantize_layer(U, perm, dead, g.Config(bits=3), W, qw, sc, ze, gi, ws),  # qweight for 4 bits
+        lambda: g.gptq_quantize_layer(U[:128, :128].contiguous(), perm, dead, cfg, W, qw, sc, ze, gi, ws),
+        lambda: g.gptq_quantize_layer(U, perm, dead, cfg, W, qw.t(), sc, ze, gi, ws),        # transposed view
+        lambda: g.gptq_quantize_layer(U, perm, dead, cfg, W, qw, sc.float(), ze, gi, ws),    # scales not fp16
+        lambda: g.gptq_layer_loss(H.float(), W, qw, sc, ze, gi, cfg, ws),
+        lambda: g.gptq_layer_loss(H, W, qw, sc, ze, gi[:100], cfg, ws),
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises(ValueError):
+            call()
+        print(f"case {i}: rejected")

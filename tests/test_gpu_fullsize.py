@@ -2,25 +2,38 @@
 Hessian call over all tokens, prepare, quantize).
 
 The default workload (W 4096x4096 bf16, X 65536 tokens x 4096 features, 4-bit
-asym g128): the oracle runs at full size here, the f64 Hessian chunk by chunk,
-the f64 inverse-Cholesky factor, and the sweep on every row (its lazy-block
-mode, which the CPU pins show equals the plain sweep), with codes decided in
-fp32 as the kernels decide them.
+asym g128): the oracle runs at full size here: the f64 Hessian chunk by
+chunk, the f64 inverse-Cholesky factor, then
+  * the plain per-column float64 sweep on 512 seeded rows (rows are
+    independent given U): the stated bar, then every difference verified as
+    a rounding tie, after which the oracle's path reproduces the GPU's
+    codes, zero points and scales on every one of those rows;
+  * the whole layer (all 4096 rows) with codes decided in binary32, the
+    kernels' decision precision, and lazy blocks (which the CPU pins show
+    equal the plain sweep): the stated bar over the whole layer.
 
 The larger workloads (the MLP-down layer, the 70B-shaped down projection and
-the whole Llama-2-7B-shaped block): the oracle's full-size results, too slow
-to recompute in a test, are stored for sampled rows and Hessian entries by
-tests/golden/make_fullsize_refs.py, which calls only the oracle and the input
-generators.
+the whole Llama-2-7B-shaped block): the plain float64 oracle's full-size
+results, too slow to recompute in a test, are stored for sampled rows and
+Hessian entries by tests/golden/make_fullsize_refs.py (which calls only the
+oracle and the input generators), with every near-tie of the oracle's path.
+Each sampled row's first parting from the oracle's path must be a verified
+tie, and every group up to it must match.
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from gpu_helpers import compare_layer, groups_before_first_flip, rel_frobenius
+from gpu_helpers import (TIE_TOL, assert_stated_bar, compare_layer, first_divergence_check, gpu_codes,
+                         plain_and_follow_rows, rel_frobenius)
 
 pytestmark = pytest.mark.gpu
+
+# diag(H) of the GPU against the oracle: measured <= 1.1e-7 relative; entries
+# are checked to 5e-7, so two diagonal entries can swap places in the
+# act-order sort only if they lie within 2 * 5e-7 of each other
+DIAG_TOL = 5e-7
 
 
 def test_attn4096_full_parity():
@@ -56,17 +69,44 @@ def test_attn4096_full_parity():
     uerr = rel_frobenius(U.cpu().numpy(), p["U"])
     print(f"[fullsize] U rel Frobenius {uerr:.3e}", flush=True)
     assert uerr <= 1e-5
-
     wv = synth.bf16_value(w_raw).astype(np.float64)
+
+    # 512 seeded rows against the plain float64 sweep, then the tie check
+    ridx = np.sort(np.concatenate([[0, rows - 1],
+                                   np.random.default_rng(4096).choice(np.arange(1, rows - 1), 510, replace=False)]))
+    plain, fol, st = plain_and_follow_rows(out, wv, p["U"], p["perm"], p["dead"], ocfg, wl.bits, ridx)
+    codes = gpu_codes(out, wl.bits, n)[ridx]
+    s_gpu = out["scales"].cpu().numpy().astype(np.float64)[:, ridx]
+    z_gpu = out["zeros"].cpu().numpy().astype(np.float64)[:, ridx]
+    agree = float(np.mean(codes == plain["codes"]))
+    s_ok = np.abs(s_gpu - plain["scales"].astype(np.float64)) <= 1e-3 * np.abs(plain["scales"].astype(np.float64))
+    z_ok = z_gpu == plain["zeros"].astype(np.float64)
+    What = oracle.dequantize(plain["qweight"], plain["scales"], plain["zeros"], out["g_idx"].cpu().numpy(),
+                             wl.bits, len(ridx), n)
+    What_g = oracle.dequantize(out["qweight"].cpu().numpy()[:, ridx], s_gpu.astype(np.float16),
+                               z_gpu.astype(np.float16), out["g_idx"].cpu().numpy(), wl.bits, len(ridx), n)
+    rl_ref, rl_gpu = oracle.rel_loss(wv[ridx], What, Href), oracle.rel_loss(wv[ridx], What_g, Href)
+    print(f"[fullsize] 512 rows vs the plain float64 sweep: codes {agree:.6f}, scales {float(np.mean(s_ok)):.6f}, "
+          f"zeros {float(np.mean(z_ok)):.6f}, rel loss {rl_gpu:.6e} vs {rl_ref:.6e}", flush=True)
+    assert agree >= 0.999 and np.mean(s_ok) >= 0.999 and np.mean(z_ok) >= 0.999
+    assert abs(rl_gpu - rl_ref) <= 0.01 * rl_ref
+    same = np.all(codes == plain["codes"], axis=1)
+    assert np.array_equal(out["qweight"].cpu().numpy()[:, ridx][:, same], plain["qweight"][:, same])
+    c_bad = int(np.sum(codes != fol["codes"]))
+    z_bad = int(np.sum(z_gpu != fol["zeros"].astype(np.float64)))
+    s_bad = int(np.sum(np.abs(s_gpu - fol["scales"].astype(np.float64)) > 1e-3 * np.abs(fol["scales"].astype(np.float64))))
+    print(f"[follow] 512 rows: ties taken {st['ties']} codes + {st['zero_ties']} zero points (largest |margin|/tol "
+          f"{st['ratio_max']:.3f}); unexplained {st['unexplained']}; after following: codes differing {c_bad}, "
+          f"zero points {z_bad}, scales beyond 1e-3 {s_bad}", flush=True)
+    assert st["unexplained"] == 0 and c_bad == 0 and z_bad == 0 and s_bad == 0
+
+    # the whole layer, codes decided in the kernels' binary32, lazy blocks
     ref = oracle.quantize_layer(wv, p["U"], p["perm"], p["dead"], ocfg, qdtype=np.float32, block=128)
     What16 = oracle.dequantize(ref["qweight"], ref["scales"], ref["zeros"], ref["g_idx"], wl.bits, rows, n)
     ref["rel_loss"] = oracle.rel_loss(wv, What16, Href)
     m = compare_layer(out, ref, wl.bits, n, wv, Href, rel)
-    print(f"[fullsize] {m}", flush=True)
-    assert m["agree"] >= 0.999
-    assert m["s_frac"] >= 0.999 and m["z_frac"] >= 0.999
-    assert m["gidx_ok"] and m["pack_ok"]
-    assert m["loss_rel"] <= 0.01
+    print(f"[fullsize] whole layer, binary32 decisions: {m}", flush=True)
+    assert_stated_bar(m)
     assert abs(out["loss"] - ref["L"]) <= 0.01 * ref["L"]
 
 
@@ -99,59 +139,63 @@ def test_mlpdown11008_full_sampled():
     print("[fullsize] GPU done; comparing with the stored oracle results", flush=True)
 
     _check_hessian(H, ref, "", wl.name)
-    _check_perm(perm, ref, "", wl.name)
-    _check_sampled_rows(out, ref, "", wl.bits, n, w_raw[ref["rows"]], lambda: H.cpu().numpy(), "down_proj")
+    p = _check_perm(perm, H, ref, "", wl.name)
+    _check_sampled_rows(out, ref, "", "", wl.bits, n, w_raw[ref["rows"]], lambda: H.cpu().numpy(), "down_proj", p,
+                        wl.group_size, wl.sym)
 
 
-def _check_sampled_rows(out, ref, pre, bits, n, w_raw_rows, H_host_fn, name):
+def _check_sampled_rows(out, ref, lp, sp, bits, n, w_raw_rows, H_host_fn, name, perm_gpu, gs, sym):
     """One linear's GPU outputs on the stored sampled rows (keys with prefix
-    ``pre``): codes >= 99.9 % identical, scales and zeros equal upstream of
-    each row's first differing code, g_idx and packing exact, relative loss of
-    the sampled rows within 1 % (computed with the GPU's Hessian)."""
-    ridx = ref[pre + "rows"]
+    ``lp``, its activation set's keys with prefix ``sp``): the stated bar in
+    aggregate (codes >= 99.9 % identical, zero points >= 99.9 % equal,
+    relative loss of the sampled rows within 1 %, computed with the GPU's
+    Hessian), g_idx exactly as the GPU's own permutation defines it, packing
+    exact on every row whose codes all agree, and each row's first parting
+    from the oracle's path a verified tie with every group up to it equal."""
+    ridx = ref[lp + "rows"]
     qw = out["qweight"].cpu().numpy()[:, ridx]
     codes = oracle.unpack(qw, bits, n)
-    rc = ref[pre + "codes"]
+    rc = ref[lp + "codes"].astype(np.int64)
     agree = float(np.mean(codes == rc))
     s_gpu = out["scales"].cpu().numpy()[:, ridx].astype(np.float64)
     z_gpu = out["zeros"].cpu().numpy()[:, ridx].astype(np.float64)
-    s_ref = ref[pre + "scales"].astype(np.float64)
-    s_ok = np.abs(s_gpu - s_ref) <= 1e-3 * np.abs(s_ref)
-    z_ok = z_gpu == ref[pre + "zeros"].astype(np.float64)
-    up = groups_before_first_flip(codes, rc, ref[pre + "g_idx"], s_ref.shape[0])
+    z_frac = float(np.mean(z_gpu == ref[lp + "zeros"].astype(np.float64)))
     gi = out["g_idx"].cpu().numpy()
+    g_own = np.empty(n, dtype=np.int64)
+    g_own[perm_gpu] = np.arange(n) // gs
     wv = synth.bf16_value(w_raw_rows).astype(np.float64)
     What = oracle.dequantize(qw, s_gpu.astype(np.float16), z_gpu.astype(np.float16), gi, bits, len(ridx), n)
     rel = oracle.rel_loss(wv, What, H_host_fn())
-    lrel = abs(rel - float(ref[pre + "rel_loss"])) / float(ref[pre + "rel_loss"])
-    flips = np.nonzero((codes != rc).any(axis=1))[0].tolist()
-    print(f"[fullsize] {name}: codes {agree:.5f}, scales {float(np.mean(s_ok)):.5f}, zeros {float(np.mean(z_ok)):.5f}, "
-          f"rows with a differing code {flips}, scale mismatches upstream {int((~s_ok & up).sum())}, "
-          f"rel loss {rel:.5e} vs {float(ref[pre + 'rel_loss']):.5e}", flush=True)
-    assert agree >= 0.999
-    assert (s_ok | ~up).all() and (z_ok | ~up).all()
-    assert float(np.mean(z_ok)) >= 0.999
-    assert np.array_equal(gi, ref[pre + "g_idx"])
-    assert np.array_equal(oracle.pack(codes, bits), qw)
+    lrel = abs(rel - float(ref[lp + "rel_loss"])) / float(ref[lp + "rel_loss"])
+    same = np.all(codes == rc, axis=1)
+    parted, worst = first_divergence_check(codes, s_gpu, z_gpu, perm_gpu, ref, lp, ref[sp + "perm"].astype(np.int64),
+                                           gs, sym, name)
+    print(f"[fullsize] {name}: codes {agree:.5f}, zeros {z_frac:.5f}, rows parting from the oracle's path "
+          f"{parted} (all at verified ties; largest |margin|/tol {worst:.3f}), rel loss {rel:.5e} vs "
+          f"{float(ref[lp + 'rel_loss']):.5e}", flush=True)
+    assert agree >= 0.999 and z_frac >= 0.999
+    assert np.array_equal(gi, g_own)
+    assert np.array_equal(qw[:, same], oracle.pack(rc[same], bits))
     assert lrel <= 0.01
 
 
-def _check_perm(perm_gpu, ref, pre, name, tol=1e-5):
-    """Act-order permutation: sorting diag(H) descending is unique only where
-    the diagonal entries differ by more than the Hessian's own tolerance, so
-    the GPU's order (taken from its H) must sort the oracle's diagonal
-    descending up to that tolerance, and wherever it differs from the
-    oracle's order the two entries it swaps must be such near-ties."""
-    d = ref[pre + "h_diag"]
+def _check_perm(perm_gpu, H, ref, pre, name):
+    """Act-order permutation: exactly the stable descending sort of the GPU's
+    own diag(H); against the oracle's order, any difference must swap
+    diagonal entries that lie within 2 * DIAG_TOL of each other (relative),
+    the window the diagonal check below allows."""
+    import torch
     p = perm_gpu.cpu().numpy().astype(np.int64)
+    d_gpu = torch.diagonal(H).cpu().numpy()
+    assert np.array_equal(p, np.argsort(-d_gpu, kind="stable"))
+    d = ref[pre + "h_diag"]
     q = ref[pre + "perm"].astype(np.int64)
-    assert np.array_equal(np.sort(p), np.arange(len(d)))
     dp, dq = d[p], d[q]
-    assert np.all(dp[:-1] >= dp[1:] - tol * np.abs(dp[1:]))
     diff = p != q
-    assert np.all(np.abs(dp[diff] - dq[diff]) <= tol * np.abs(dq[diff]))
+    assert np.all(np.abs(dp[diff] - dq[diff]) <= 2 * DIAG_TOL * np.abs(dq[diff]))
     print(f"[fullsize] {name}: act-order positions differing from the oracle's {int(diff.sum())} (near-ties)",
           flush=True)
+    return p
 
 
 def _check_hessian(H, ref, pre, name):
@@ -163,7 +207,7 @@ def _check_hessian(H, ref, pre, name):
     diag = torch.diagonal(H).cpu().numpy()
     hd = float(np.max(np.abs(diag - ref[pre + "h_diag"]) / np.abs(ref[pre + "h_diag"])))
     print(f"[fullsize] {name}: H sampled rel error {hs:.3e}, diagonal max rel error {hd:.3e}", flush=True)
-    assert hs <= 1e-5 and hd <= 1e-5
+    assert hs <= 1e-5 and hd <= DIAG_TOL
 
 
 def _golden(name):
@@ -205,14 +249,15 @@ def test_llama2block_full_sampled():
     torch.cuda.synchronize()
     del Xs
     print("[fullsize] GPU done; comparing with the stored oracle results", flush=True)
+    perms = []
     for s in range(len(wl.xsets)):
         _check_hessian(Hs[s], ref, f"set{s}_", f"set {s}")
         _, perm, _ = g.prepare(Hs[s], cfg)
-        _check_perm(perm, ref, f"set{s}_", f"set {s}")
+        perms.append(_check_perm(perm, Hs[s], ref, f"set{s}_", f"set {s}"))
     for li, lin in enumerate(wl.linears):
         pre = f"lin{li}_"
-        _check_sampled_rows(outs[li], ref, pre, wl.bits, lin.n, w_raw[li][ref[pre + "rows"]],
-                            lambda s=lin.xset: Hs[s].cpu().numpy(), lin.name)
+        _check_sampled_rows(outs[li], ref, pre, f"set{lin.xset}_", wl.bits, lin.n, w_raw[li][ref[pre + "rows"]],
+                            lambda s=lin.xset: Hs[s].cpu().numpy(), lin.name, perms[lin.xset], wl.group_size, wl.sym)
 
 
 def test_down28672_full_sampled():
@@ -241,5 +286,6 @@ def test_down28672_full_sampled():
     del U
     print("[fullsize] GPU done; comparing with the stored oracle results", flush=True)
     _check_hessian(H, ref, "", "down28672")
-    _check_perm(perm, ref, "", "down28672")
-    _check_sampled_rows(out, ref, "", wl.bits, wl.n, w_raw[ref["rows"]], lambda: H.cpu().numpy(), "down_proj")
+    p = _check_perm(perm, H, ref, "", "down28672")
+    _check_sampled_rows(out, ref, "", "", wl.bits, wl.n, w_raw[ref["rows"]], lambda: H.cpu().numpy(), "down_proj",
+                        p, wl.group_size, wl.sym)

@@ -152,3 +152,172 @@ def test_dead_column_is_zeroed():
     assert out["dead"][5]
     assert np.all(out["What"][:, 5] == 0.0)
     assert np.all(out["E"][:, 5] == 0.0)
+
+
+# --------------------------------------------------------------------------- several correct results
+TAU = 2.0 ** -15
+
+
+def test_follow_own_result_changes_nothing():
+    W, H = _layer(rows=12, n=128, seed=9)
+    cfg = oracle.QuantConfig(bits=4, group_size=32)
+    p = oracle.prepare(H, cfg.damp)
+    a = oracle.sweep(W, p["U"], cfg)
+    b = oracle.sweep(W, p["U"], cfg, follow=dict(codes=a["codes"], zeros=a["Z"]), tie_tol=TAU)
+    assert b["follow"] == dict(ties=0, zero_ties=0, unexplained=0, ratio_max=0.0)
+    for k in ("codes", "S", "Z", "What", "E"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["L"] == b["L"]
+
+
+def _tie_layer(seed=10):
+    """A correlated layer whose row 3 has an exact rounding midpoint in its first
+    column: the group of columns 0..31 spans [0, 15 * 2^-6] (s = 2^-6, z = 0)
+    and w[3, 0] = 2.5 * 2^-6, so w/s = 2.5 and codes 2 and 3 are both nearest."""
+    W, H = _layer(rows=6, n=64, seed=seed)
+    W[3, :32] = np.abs(W[3, :32]) * (14 * 2.0 ** -6 / np.abs(W[3, :32]).max())
+    W[3, 1] = 15 * 2.0 ** -6
+    W[3, 0] = 2.5 * 2.0 ** -6
+    return W, H
+
+
+def test_follow_takes_the_other_neighbour_at_an_exact_tie():
+    W, H = _tie_layer()
+    cfg = oracle.QuantConfig(bits=4, group_size=32)
+    p = oracle.prepare(H, cfg.damp)
+    a = oracle.sweep(W, p["U"], cfg)
+    assert a["S"][0, 3] == 2.0 ** -6 and a["Z"][0, 3] == 0 and a["codes"][3, 0] == 2     # half to even
+    # the other valid result: the plain sweep of a weight nudged to round up there
+    W2 = W.copy()
+    W2[3, 0] = 2.5 * 2.0 ** -6 * (1 + 1e-12)
+    c = oracle.sweep(W2, p["U"], cfg)
+    assert c["codes"][3, 0] == 3
+    assert not np.array_equal(c["codes"][3, 1:], a["codes"][3, 1:])        # the row's later codes move too
+    b = oracle.sweep(W, p["U"], cfg, follow=dict(codes=c["codes"]), tie_tol=TAU)
+    assert b["follow"]["ties"] == 1 and b["follow"]["unexplained"] == 0
+    assert b["follow"]["ratio_max"] == 0.0                     # exactly on the midpoint
+    assert np.array_equal(b["codes"], c["codes"])
+    np.testing.assert_allclose(b["What"], c["What"], rtol=0, atol=1e-12)
+    assert np.array_equal(b["codes"][[0, 1, 2, 4, 5]], a["codes"][[0, 1, 2, 4, 5]])   # other rows untouched
+    # following only the flipped code, not the row's consequences, leaves the
+    # later differences unexplained
+    alt = a["codes"].copy()
+    alt[3, 0] = 3
+    d = oracle.sweep(W, p["U"], cfg, follow=dict(codes=alt), tie_tol=TAU)
+    assert d["follow"]["ties"] == 1 and d["follow"]["unexplained"] > 0
+
+
+@pytest.mark.parametrize("alt_code", [4, 1])
+def test_follow_keeps_its_own_code_where_the_other_is_not_a_tie(alt_code):
+    # 4: not a neighbour of the rounding of 2.5; 1: a neighbour of 2, but 2.5 is
+    # 1.0 away from the midpoint 1.5 between them
+    W, H = _tie_layer()
+    cfg = oracle.QuantConfig(bits=4, group_size=32)
+    p = oracle.prepare(H, cfg.damp)
+    a = oracle.sweep(W, p["U"], cfg)
+    alt = a["codes"].copy()
+    alt[3, 0] = alt_code
+    b = oracle.sweep(W, p["U"], cfg, follow=dict(codes=alt), tie_tol=TAU)
+    assert b["follow"]["ties"] == 0 and b["follow"]["unexplained"] == 1
+    assert np.array_equal(a["codes"], b["codes"])
+
+
+def test_follow_tolerance_scales_with_the_compensation_magnitudes():
+    """A quotient 2.5 + d lies within the tolerance iff d <= TAU * (|w0| + sum
+    |e_k U_kj|) / s; at the first column the sum is empty: tol = TAU * |w0| / s."""
+    W, H = _tie_layer()
+    cfg = oracle.QuantConfig(bits=4, group_size=32)
+    p = oracle.prepare(H, cfg.damp)
+    tol = TAU * 2.5
+    for d, taken in ((0.9 * tol, True), (1.1 * tol, False)):
+        W2 = W.copy()
+        W2[3, 0] = (2.5 - d) * 2.0 ** -6            # rounds to 2 on its own
+        a = oracle.sweep(W2, p["U"], cfg)
+        assert a["codes"][3, 0] == 2
+        alt = a["codes"].copy()
+        alt[3, 0] = 3
+        b = oracle.sweep(W2, p["U"], cfg, follow=dict(codes=alt), tie_tol=TAU)
+        assert (b["follow"]["ties"] == 1) == taken, d
+        assert (b["codes"][3, 0] == 3) == taken
+
+
+def test_follow_zero_point_tie():
+    """Asymmetric 4-bit group spanning [-2^-4, 2^-4]: -xmin/s = 7.5, zero points
+    7 and 8 are both nearest; following 7 shifts every code of the group by -1
+    relative to 8 while the grid values s(c - z) stay where they are."""
+    rng = np.random.default_rng(11)
+    W = rng.uniform(-2.0 ** -4, 2.0 ** -4, size=(4, 64))
+    W[:, 0], W[:, 1] = -2.0 ** -4, 2.0 ** -4
+    cfg = oracle.QuantConfig(bits=4, group_size=32)
+    U = np.eye(64)
+    a = oracle.sweep(W, U, cfg)
+    assert np.all(a["Z"][0] == 8)
+    zalt = a["Z"].copy()
+    zalt[0, 2] = 7
+    alt = a["codes"].copy()
+    alt[2, :32] -= 1
+    b = oracle.sweep(W, U, cfg, follow=dict(codes=alt, zeros=zalt), tie_tol=TAU)
+    assert b["follow"]["zero_ties"] == 1 and b["follow"]["unexplained"] == 0
+    assert b["Z"][0, 2] == 7 and np.array_equal(b["codes"][2, :32], a["codes"][2, :32] - 1)
+    np.testing.assert_allclose(b["What"], a["What"], rtol=0, atol=1e-15)
+    zalt[0, 2] = 6                                               # not a neighbour of 7.5's rounding
+    c = oracle.sweep(W, U, cfg, follow=dict(codes=alt, zeros=zalt), tie_tol=TAU)
+    assert c["Z"][0, 2] == 8 and c["follow"]["zero_ties"] == 0 and c["follow"]["unexplained"] > 0
+
+
+# --------------------------------------------------------------------------- the layer objective
+def test_rel_loss_hand_worked_example():
+    """polydesk "Comment fonctionne l'algorithme GPTQ": the layer objective is the
+    squared output error ||W X - W_hat X||^2, relative to ||W X||^2.  One output,
+    two features, three tokens x = (1, 0), (0, 1), (1, 1):
+      W X     = (1, 2, 3)  -> ||.||^2 = 14
+      D X     = (0, 1, 1)  -> ||.||^2 = 2     (D = W - W_hat = (0, 1))
+    so the relative loss is 2 / 14 = 1/7 (the H = (2/N) X X^T factor cancels)."""
+    X = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]])          # [tokens, features]
+    H, _ = oracle.hessian(X)
+    assert oracle.rel_loss(np.array([[1.0, 2.0]]), np.array([[1.0, 1.0]]), H) == pytest.approx(1 / 7, rel=1e-15)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_rel_loss_equals_output_error_computed_from_x(seed):
+    """rel_loss(W, W_hat, hessian(X)) against ||(W - W_hat) X^T||_F^2 / ||W X^T||_F^2
+    formed from the activations themselves, on a layer whose D H D^T has large
+    off-diagonal entries, so that a trace and a sum of all entries (or a dropped
+    transpose) give different numbers."""
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((300, 24)) @ rng.standard_normal((24, 24))     # correlated features
+    W = rng.standard_normal((7, 24))
+    What = W + 0.1 * rng.standard_normal((7, 24))
+    H, _ = oracle.hessian(X)
+    direct = np.linalg.norm((W - What) @ X.T) ** 2 / np.linalg.norm(W @ X.T) ** 2
+    assert oracle.rel_loss(W, What, H) == pytest.approx(direct, rel=1e-12)
+    D = W - What
+    wrong = np.sum(D @ H @ D.T) / np.sum(W @ H @ W.T)                  # sum of all entries, not the trace
+    assert abs(wrong - direct) > 0.05 * direct
+    # with the GPTQ output of a correlated layer
+    Wl, Hl = _layer(rows=10, n=64, seed=12)
+    g = oracle.gptq_layer(Wl, Hl, oracle.QuantConfig(bits=3, group_size=32))
+    # rebuild an X with this H: H = (2/N) X^T X for X = sqrt(N/2) L^T (L L^T = H)
+    L = np.linalg.cholesky(Hl)
+    Xl = np.sqrt(64 / 2) * L.T
+    assert np.allclose(oracle.hessian(Xl)[0], Hl, rtol=1e-12, atol=1e-12)
+    What16 = oracle.dequantize(g["qweight"], g["scales"], g["zeros"], g["g_idx"], 3, 10, 64)
+    direct = np.linalg.norm((Wl - What16) @ Xl.T) ** 2 / np.linalg.norm(Wl @ Xl.T) ** 2
+    assert g["rel_loss"] == pytest.approx(direct, rel=1e-10)
+
+
+def test_record_positions_and_tolerance_scale():
+    """record=True: t is the unrounded code position (its clamped rounding is
+    the code) and tol_scale equals (|w0| + (|E| |U|_strict-upper)_j) / s formed
+    afterwards from the returned errors; with follow of its own result, the
+    recorded path is the same."""
+    W, H = _layer(rows=9, n=96, seed=13)
+    cfg = oracle.QuantConfig(bits=3, group_size=32)
+    p = oracle.prepare(H, cfg.damp)
+    r = oracle.sweep(W, p["U"], cfg, record=True)
+    assert np.array_equal(np.clip(np.rint(r["t"]), 0, 7), r["codes"])
+    s_col = np.repeat(r["S"].T, 32, axis=1)                      # [rows, n] scale of each column's group
+    A = np.abs(r["E"]) @ np.abs(np.triu(p["U"], 1))
+    np.testing.assert_allclose(r["tol_scale"], (np.abs(W) + A) / s_col, rtol=1e-12)
+    # zero-point positions: -xmin/s of each group's (compensated) weights rounds to Z
+    assert np.array_equal(np.rint(r["zq"]), r["Z"])
