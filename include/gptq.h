@@ -226,6 +226,28 @@ gptq_status gptq_matmul(const void* A, gptq_dtype adt, int64_t M, int64_t lda, c
                         void* Y, gptq_dtype ydt, int64_t ldy, void* workspace, size_t ws_bytes,
                         void* stream);
 
+/* ------------------------------------------------------------------------- *
+ * gptq_matmul without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, serving loops and harnesses that
+ * forbid hipMalloc.  Same arguments, result and rules as gptq_matmul, minus
+ * workspace/ws_bytes.  It calls no hipMalloc, hipFree or allocating routine.
+ * Act-order layers (col_order != NULL) gather their activations into a
+ * library-owned device array of gptq_matmul_static_scratch_bytes() bytes
+ * (4 MiB): one copy per device, reserved when the library is loaded on that
+ * device and held until the process ends.  Returns GPTQ_ERR_WORKSPACE if the
+ * gathered activations, M * n * 2 bytes rounded up to 256, do not fit it
+ * (nothing is launched then).  Layers without col_order use no scratch.
+ * All calls on one device share that array, and each call overwrites what it
+ * uses before reading it (nothing needs clearing); calls that overlap on one
+ * device (on different streams or host threads) race on it.  The first call
+ * on a device looks up the array's device address (hipGetSymbolAddress, with
+ * that device current).
+ * ------------------------------------------------------------------------- */
+size_t gptq_matmul_static_scratch_bytes(void);
+gptq_status gptq_matmul_static(const void* A, gptq_dtype adt, int64_t M, int64_t lda, const void* packed,
+                               const int32_t* col_order, int64_t rows, int64_t n, int32_t bits, int32_t group_size,
+                               void* Y, gptq_dtype ydt, int64_t ldy, void* stream);
+
 /* Message for the last failing call on this thread (empty string if none). */
 const char* gptq_last_error(void);
 /* Library version string. */

@@ -13,6 +13,7 @@ Functions keep the C names:
     gptq_layer_loss(H, W, qweight, scales, zeros, g_idx, cfg, ws) -> relative loss
     gptq_matmul_pack(qweight, scales, zeros, g_idx, bits, group_size, packed, col_order) -> identity
     gptq_matmul(A, packed, col_order, rows, n, bits, group_size, Y, ws)
+    gptq_matmul_static(A, packed, col_order, rows, n, bits, group_size, Y)   (no workspace)
 plus the workspace queries and small allocating helpers (``quantize_layer``,
 ``hessian``, ``prepare``, ``PackedLayer``) that create the output tensors with
 torch, and ``quantize_block``, which sequences those calls for the linears of a
@@ -44,6 +45,7 @@ EXPORTS = (
     "gptq_quantize_workspace_bytes", "gptq_quantize_layer",
     "gptq_layer_loss_workspace_bytes", "gptq_layer_loss",
     "gptq_matmul_packed_bytes", "gptq_matmul_pack", "gptq_matmul_workspace_bytes", "gptq_matmul",
+    "gptq_matmul_static_scratch_bytes", "gptq_matmul_static",
     "gptq_last_error", "gptq_version",
 )
 
@@ -119,6 +121,11 @@ def lib() -> ctypes.CDLL:
     L.gptq_matmul.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, i64, vp,
                               sz, vp]
     L.gptq_matmul.restype = ctypes.c_int
+    L.gptq_matmul_static_scratch_bytes.argtypes = []
+    L.gptq_matmul_static_scratch_bytes.restype = sz
+    L.gptq_matmul_static.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, i64,
+                                     vp]
+    L.gptq_matmul_static.restype = ctypes.c_int
     L.gptq_last_error.argtypes = []
     L.gptq_last_error.restype = ctypes.c_char_p
     L.gptq_version.argtypes = []
@@ -363,6 +370,31 @@ def gptq_matmul(A, packed, col_order, rows: int, n: int, bits: int, group_size: 
                              _stream(stream, A.device)))
 
 
+def gptq_matmul_static_scratch_bytes() -> int:
+    return lib().gptq_matmul_static_scratch_bytes()
+
+
+def gptq_matmul_static(A, packed, col_order, rows: int, n: int, bits: int, group_size: int, Y,
+                       stream=None) -> None:
+    """gptq_matmul with the act-order gather in the library's own device array
+    (no workspace argument; nothing is allocated)."""
+    import torch
+    dev = A.device
+    if A.dim() != 2 or A.shape[1] < n:
+        raise ValueError(f"A must be a 2-D tensor with at least n={n} columns")
+    _need_matrix(Y, "Y", rows, dev)
+    if Y.shape[0] != A.shape[0]:
+        raise ValueError(f"Y has {Y.shape[0]} rows, A has {A.shape[0]}")
+    if packed.device != dev or not packed.is_contiguous():
+        raise ValueError(f"packed must be a contiguous tensor on {dev}")
+    if col_order is not None:
+        _need(col_order, "col_order", torch.int32, (n,), dev)
+    lda = _row_major_2d(A, "A")
+    ldy = _row_major_2d(Y, "Y")
+    _check(lib().gptq_matmul_static(_ptr(A), _dtype_code(A), A.shape[0], lda, _ptr(packed), _ptr(col_order), rows, n,
+                                    bits, group_size, _ptr(Y), _dtype_code(Y), ldy, _stream(stream, dev)))
+
+
 def gptq_version() -> str:
     return lib().gptq_version().decode()
 
@@ -480,3 +512,4 @@ def quantize_block(X_sets, weights, xset_of, cfg, want_loss: bool = True):
         out["rel_loss"] = layer_loss(Hs[s], W, out, cfg) if want_loss else None
         outs.append(out)
     return outs, Hs
+

@@ -36,6 +36,8 @@ size_t matmul_workspace_bytes(int64_t M, int64_t n);
 hipError_t launch_matmul(const void* A, int64_t M, int64_t lda, const void* packed, const int32_t* col_order,
                          int64_t rows, int64_t n, int bits, int group_size, void* Y, int ydt, int64_t ldy,
                          void* ws, hipStream_t s);
+size_t matmul_static_scratch_bytes();
+hipError_t matmul_static_scratch(void** ptr);
 }  // namespace gptq
 
 namespace {
@@ -99,6 +101,26 @@ gptq_status check_matmul_format(int64_t rows, int64_t n, int32_t bits, int32_t g
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Checks shared by gptq_matmul and gptq_matmul_static (everything but the workspace).
+gptq_status check_matmul_call(const void* A, gptq_dtype adt, int64_t M, int64_t lda, const void* packed,
+                              const int32_t* col_order, int64_t rows, int64_t n, int32_t bits, int32_t group_size,
+                              const void* Y, gptq_dtype ydt, int64_t ldy) {
+  gptq_status st = check_matmul_format(rows, n, bits, group_size);
+  if (st != GPTQ_OK) return st;
+  if (adt != GPTQ_FP16) return fail(GPTQ_ERR_UNSUPPORTED, "activations must be fp16 (got dtype %d)", (int)adt);
+  if (ydt != GPTQ_FP16 && ydt != GPTQ_FP32)
+    return fail(GPTQ_ERR_UNSUPPORTED, "output must be fp16 or fp32 (got dtype %d)", (int)ydt);
+  if (M < 0 || M > (int64_t)65535 * 16) return fail(GPTQ_ERR_INVALID_ARG, "M=%lld out of range", (long long)M);
+  if (M == 0) return GPTQ_OK;
+  if (!A || !packed || !Y) return fail(GPTQ_ERR_INVALID_ARG, "NULL pointer argument");
+  if (lda < n || ldy < rows)
+    return fail(GPTQ_ERR_INVALID_ARG, "lda=%lld < n or ldy=%lld < rows", (long long)lda, (long long)ldy);
+  if (!aligned16(packed)) return fail(GPTQ_ERR_INVALID_ARG, "packed must be 16-byte aligned");
+  if (!col_order && (!aligned16(A) || lda % 8 != 0))
+    return fail(GPTQ_ERR_INVALID_ARG, "A must be 16-byte aligned with lda a multiple of 8");
+  return GPTQ_OK;
+}
 
 }  // namespace
 
@@ -262,6 +284,29 @@ gptq_status gptq_matmul_pack(const int32_t* qweight, const uint16_t* scales, con
 size_t gptq_matmul_workspace_bytes(int64_t M, int64_t n, int32_t has_col_order) {
   if (M < 1 || n < 1 || !has_col_order) return 0;
   return gptq::matmul_workspace_bytes(M, n);
+}
+
+size_t gptq_matmul_static_scratch_bytes(void) { return gptq::matmul_static_scratch_bytes(); }
+
+gptq_status gptq_matmul_static(const void* A, gptq_dtype adt, int64_t M, int64_t lda, const void* packed,
+                               const int32_t* col_order, int64_t rows, int64_t n, int32_t bits, int32_t group_size,
+                               void* Y, gptq_dtype ydt, int64_t ldy, void* stream) {
+  gptq_status st = check_matmul_call(A, adt, M, lda, packed, col_order, rows, n, bits, group_size, Y, ydt, ldy);
+  if (st != GPTQ_OK) return st;
+  if (M == 0) return ok();
+  void* ws = nullptr;
+  if (col_order) {
+    const size_t need = gptq::matmul_workspace_bytes(M, n);
+    if (need > gptq::matmul_static_scratch_bytes())
+      return fail(GPTQ_ERR_WORKSPACE, "M=%lld x n=%lld activations need %zu bytes of gather scratch, more than the "
+                  "%zu the library holds", (long long)M, (long long)n, need, gptq::matmul_static_scratch_bytes());
+    hipError_t e = gptq::matmul_static_scratch(&ws);
+    if (e != hipSuccess) return hip_fail("gptq_matmul_static (scratch address)", e);
+  }
+  hipError_t e = gptq::launch_matmul(A, M, lda, packed, col_order, rows, n, bits, group_size, Y,
+                                     static_cast<int>(ydt), ldy, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("gptq_matmul_static", e);
+  return ok();
 }
 
 gptq_status gptq_matmul(const void* A, gptq_dtype adt, int64_t M, int64_t lda, const void* packed,

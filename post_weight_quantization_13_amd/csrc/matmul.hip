@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -636,6 +637,38 @@ hipError_t launch_matmul_pack(const int32_t* qweight, const uint16_t* scales, co
 }
 
 size_t matmul_workspace_bytes(int64_t M, int64_t n) { return align256(static_cast<size_t>(M * n) * 2); }
+
+// Library-owned scratch of the allocation-free matmul entry point: the
+// gathered activations of act-order layers.  One copy per device, at its own
+// address on each, held until the process ends.
+constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+size_t matmul_static_scratch_bytes() { return kStaticScratchBytes; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept.  In host
+// code the array's name is only a stand-in for the device symbol: it is never
+// passed to a kernel or a copy; the looked-up address is.
+hipError_t matmul_static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static void* addr[kMaxDevices] = {};
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_matmul(const void* A, int64_t M, int64_t lda, const void* packed, const int32_t* col_order,
                          int64_t rows, int64_t n, int bits, int group_size, void* Y, int ydt, int64_t ldy,

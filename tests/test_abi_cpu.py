@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(g):
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     assert set(names) == set(g.EXPORTS)
     L = g.lib()
     for n in names:
@@ -138,6 +138,15 @@ def test_matmul_queries_and_validation(g):
     assert mm(A=ctypes.c_void_p(0x1002)) == g.GPTQ_ERR_INVALID_ARG
     assert mm(order=FAKE) == g.GPTQ_ERR_WORKSPACE                  # act-order needs the gather workspace
     assert mm(M=0, A=None) == g.GPTQ_OK                            # no tokens: nothing to do
+    # the allocation-free variant: the same checks, and the size of the library's gather array
+    st = lambda M=1, n=256, order=None, adt=g.GPTQ_FP16, lda=None: L.gptq_matmul_static(
+        FAKE, adt, M, lda or n, FAKE, order, 16, n, 4, 128, FAKE, g.GPTQ_FP32, 16, None)
+    assert g.gptq_matmul_static_scratch_bytes() == 4 << 20
+    assert st(adt=g.GPTQ_BF16) == g.GPTQ_ERR_UNSUPPORTED
+    assert st(lda=128) == g.GPTQ_ERR_INVALID_ARG
+    assert st(M=0) == g.GPTQ_OK
+    assert st(M=65, n=32768, order=FAKE) == g.GPTQ_ERR_WORKSPACE   # 65 x 32768 fp16 > 4 MiB
+    assert b"4194304" in L.gptq_last_error()
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, g):
