@@ -39,7 +39,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA (published)
+PEAK_FP64_TFLOPS = 78.6      # MI355X fp64 (vector and MFMA, published)
+PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 vector (published)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
+DTYPE = ("bf16 MFMA Hessian (fp32 chains of 256 tokens, fp64 accumulation); fp64 MFMA Cholesky + triangular "
+         "inverse; fp32 column sweep with split-bf16 (3 bf16 MFMA products, fp32 accumulation) lazy-block updates")
 METRIC = "GPTQ weights quantized/sec per layer (4096×4096, g128) + Hessian TFLOP/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hessian_attn4096_traffic.json")
 HESSIAN_SRC = os.path.join(ROOT, "post_weight_quantization_13_amd", "csrc", "hessian.hip")
@@ -67,6 +71,78 @@ def _traffic(path=TRAFFIC_FILE, src=HESSIAN_SRC, key="bytes_per_launch"):
     if t.get("source_sha") != _sha(src):
         return None
     return t.get(key)
+
+
+def layer_solve_roofline(layers, hess, stage_ms):
+    """t_roof per stage of one step against the peak of the arithmetic each
+    stage runs in, and t_roof / t_measured for the solve and the whole step.
+
+    layers: [(rows, n, bits, group_size)] quantized linears; hess: [(n, tokens)]
+    Hessians built (a factor shared by several linears is counted once).
+      Hessian   n(n+1) flop per token (unique entries of X^T X), bf16 MFMA.
+      prepare   2n^3/3 flop (Cholesky n^3/3 + triangular inverse n^3/3), fp64.
+      quantize  the column sweep rows*n*B flop on the fp32 vector ALUs
+                (each column updates the rest of its 128-column block);
+                the lazy-block updates rows*n*(n-B) flop issued as three bf16
+                MFMA products each, or their fp32 W read-modify-write per
+                512-column super-block if that takes longer; and the minimal
+                I/O (W bf16 in, U fp32 read, packed codes, scales and zeros,
+                g_idx out) at HBM speed."""
+    B, SB = 128, 512
+    t_h = sum(n * (n + 1) * tok for n, tok in hess) / (PEAK_BF16_TFLOPS * 1e12)
+    t_p = sum(2.0 * n ** 3 / 3 for n, _ in hess) / (PEAK_FP64_TFLOPS * 1e12)
+    t_sweep = t_upd = t_io = 0.0
+    for rows, n, bits, gs in layers:
+        t_sweep += rows * n * B / (PEAK_FP32_TFLOPS * 1e12)
+        flops = 3.0 * rows * n * max(n - B, 0)
+        sbs = n // SB
+        upd_bytes = 8.0 * rows * sum(max(n - (s + 2) * SB, 0) for s in range(sbs))
+        t_upd += max(flops / (PEAK_BF16_TFLOPS * 1e12), upd_bytes / (PEAK_HBM_GBS * 1e9))
+        G = n // gs if gs > 0 else 1
+        io = 2.0 * rows * n + 4.0 * n * n + rows * n * bits / 8 + 4.0 * rows * G + 4 * n
+        t_io += io / (PEAK_HBM_GBS * 1e9)
+    t_q = t_sweep + t_upd + t_io
+    ms = lambda t: t * 1e3
+    solve_meas = stage_ms["prepare"] + stage_ms["quantize"]
+    step_meas = solve_meas + stage_ms["hessian"]
+    return {
+        "stages": {
+            "hessian": {"t_roof_ms": ms(t_h), "t_ms": stage_ms["hessian"], "frac": ms(t_h) / stage_ms["hessian"],
+                        "peak": "bf16 MFMA 2500 TFLOP/s"},
+            "prepare": {"t_roof_ms": ms(t_p), "t_ms": stage_ms["prepare"], "frac": ms(t_p) / stage_ms["prepare"],
+                        "peak": "fp64 78.6 TFLOP/s"},
+            "quantize": {"t_roof_ms": ms(t_q), "t_ms": stage_ms["quantize"], "frac": ms(t_q) / stage_ms["quantize"],
+                         "parts_ms": {"sweep_fp32_valu": ms(t_sweep), "split_bf16_updates": ms(t_upd),
+                                      "io_hbm": ms(t_io)},
+                         "peak": "fp32 vector 157.3 TFLOP/s, bf16 MFMA 2500 TFLOP/s, HBM 8 TB/s"},
+        },
+        "solve": {"t_roof_ms": ms(t_p + t_q), "t_ms": solve_meas, "frac": ms(t_p + t_q) / solve_meas},
+        "step": {"t_roof_ms": ms(t_h + t_p + t_q), "t_ms": step_meas, "frac": ms(t_h + t_p + t_q) / step_meas},
+    }
+
+
+def _host_info():
+    """CPU model, the threads numpy's BLAS uses, and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas_threads, blas = 0, "unknown"
+    try:
+        import numpy  # noqa: F401  (loads the BLAS threadpoolctl reports on)
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas_threads = max(blas_threads, int(i.get("num_threads", 0)))
+                blas = f"{i.get('internal_api')} {i.get('version')}"
+    except Exception:  # pragma: no cover
+        pass
+    return model, blas, blas_threads, len(os.sched_getaffinity(0))
 
 
 def _device_inputs(wl, torch):
@@ -169,7 +245,7 @@ def block_bench(args, wl, g, torch):
         "metric": METRIC, "value": weights / (ms_step * 1e-3), "unit": "weights/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 mfma (fp32/fp64 accumulate) + fp64 cholesky + fp32 sweep", "data": "synthetic",
+        "dtype": DTYPE, "data": "synthetic",
         "config": {"workload": wl.name, "linears": [(lin.name, lin.rows, lin.n, lin.xset) for lin in wl.linears],
                    "xsets": [x[0] for x in wl.xsets], "tokens": wl.tokens, "bits": wl.bits,
                    "group_size": wl.group_size, "sym": wl.sym, "desc_act": wl.desc_act, "damp": wl.damp,
@@ -179,12 +255,64 @@ def block_bench(args, wl, g, torch):
         "stage_ms": st,
         "roofline": {"kernel": "syrk_dma_kernel<bf16> (Hessian, all sets)", "bound": "mfma",
                      "achieved": hess_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": hess_tflops / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": hess_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "layer_solve": layer_solve_roofline(
+                         [(lin.rows, lin.n, wl.bits, wl.group_size) for lin in wl.linears],
+                         [(n, wl.tokens) for n in ns], st)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         _log("timing the float64 oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline_block(wl)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def block_sequential_bench(args, wl, g, torch):
+    """One step = block-sequential calibration of the whole block: the block
+    forward in the library's kernels (RMSNorm, q/k/v through the dequantizing
+    matmul of the just-quantized weights, RoPE, causal attention, o, residual,
+    RMSNorm, gate/up, SiLU gate) with a Hessian, a prepare and the quantize
+    calls of each stage on the activations that reach it."""
+    import numpy as np
+    import synth
+    torch.cuda.set_device(0)
+    cfg = g.Config(bits=wl.bits, group_size=wl.group_size, sym=wl.sym, desc_act=wl.desc_act,
+                   damp_percent=wl.damp, block_size=wl.block_size)
+    seq_len = 2048
+    _log(f"generating the block input: {wl.tokens} x {wl.xsets[0][0]} ({wl.tokens // seq_len} sequences)")
+    X0 = _xset_on_device(wl, 0, torch)
+    Ws = []
+    for li, lin in enumerate(wl.linears):
+        w_raw = synth.weights_raw(wl, li)
+        Ws.append(torch.from_numpy(w_raw.view(np.int16)).view(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+
+    def step():
+        outs, Hs, _ = g.calibrate_block_sequential(X0, Ws, cfg, seq_len=seq_len)
+        return outs
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        _log(f"warmup step {i + 1}/{args.warmup} done")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+        torch.cuda.synchronize()
+        _log(f"step {i + 1}/{args.steps} done")
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    weights = sum(lin.rows * lin.n for lin in wl.linears)
+    out = {
+        "metric": "GPTQ weights quantized/sec, block-sequential calibration of one decoder block",
+        "value": weights / (ms_step * 1e-3), "unit": "weights/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": DTYPE + "; block forward: fp16 activations, fp32 attention, fp64 norms",
+        "data": "synthetic",
+        "config": {"workload": wl.name + "-sequential", "tokens": wl.tokens, "seq_len": seq_len,
+                   "linears": [(lin.name, lin.rows, lin.n) for lin in wl.linears], "bits": wl.bits,
+                   "group_size": wl.group_size, "desc_act": wl.desc_act, "damp": wl.damp},
+    }
     print(json.dumps(out), flush=True)
     return 0
 
@@ -198,12 +326,8 @@ def cpu_baseline_block(wl):
     import numpy as np
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"] or [0])
-    except Exception:  # pragma: no cover
-        cores = 0
-    cores = cores or len(os.sched_getaffinity(0))
+    model, blas, blas_threads, affinity = _host_info()
+    cores = blas_threads or affinity
     cfg = oracle.QuantConfig(bits=wl.bits, group_size=wl.group_size, sym=wl.sym, desc_act=wl.desc_act,
                              damp=wl.damp)
     tok_s = min(wl.tokens, synth.CHUNK)
@@ -231,6 +355,7 @@ def cpu_baseline_block(wl):
     weights = sum(lin.rows * lin.n for lin in wl.linears)
     return {
         "value": weights / total, "unit": "weights/s", "cores": cores, "kind": "oracle",
+        "cpu_model": model, "blas": blas, "blas_threads": blas_threads, "affinity_cores": affinity,
         "sample": (f"each set's Hessian on {tok_s} of {wl.tokens} tokens (time x{wl.tokens / tok_s:g}); prepare timed "
                    f"once at n={n0} ({t_p0:.2f} s) and scaled by (n/{n0})^3 per set; sweep on {rows_s} rows of "
                    f"width {n0} ({per_row * rows_s:.2f} s), scaled by rows and (n/{n0})^2 per linear"),
@@ -243,12 +368,8 @@ def cpu_baseline(wl, w_raw, x_raw):
     import numpy as np
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"] or [0])
-    except Exception:  # pragma: no cover
-        cores = 0
-    cores = cores or len(os.sched_getaffinity(0))
+    model, blas, blas_threads, affinity = _host_info()
+    cores = blas_threads or affinity
     rows, n = wl.rows, wl.n
     tok_s = min(wl.tokens, 8192)
     rows_s = min(rows, 256)
@@ -269,6 +390,7 @@ def cpu_baseline(wl, w_raw, x_raw):
     total = t_h + t_p + t_s
     return {
         "value": rows * n / total, "unit": "weights/s", "cores": cores, "kind": "oracle",
+        "cpu_model": model, "blas": blas, "blas_threads": blas_threads, "affinity_cores": affinity,
         "sample": (f"Hessian on {tok_s} of {wl.tokens} tokens (time x{wl.tokens / tok_s:g}), prepare at full "
                    f"n={n}, sweep on {rows_s} of {rows} rows (time x{rows / rows_s:g}; rows are independent); "
                    f"measured {t1 - t0:.2f}+{t2 - t1:.2f}+{t3 - t2:.2f} s"),
@@ -387,6 +509,8 @@ def main() -> int:
     ap.add_argument("--damp", type=float, default=None)
     ap.add_argument("--matmul-only", action="store_true", help="only the dequant_matmul measurement")
     ap.add_argument("--no-matmul", action="store_true", help="skip the dequant_matmul measurement")
+    ap.add_argument("--sequential", action="store_true",
+                    help="block workloads: block-sequential calibration (the block forward between the stages)")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="copy 1 GiB (counter calibration) then 3 Hessian launches; no timing output")
     args = ap.parse_args()
@@ -415,6 +539,8 @@ def main() -> int:
     if over:
         wl = dataclasses.replace(wl, **over)
     if len(wl.linears) != 1:
+        if args.sequential:
+            return block_sequential_bench(args, wl, g, torch)
         return block_bench(args, wl, g, torch)
     torch.cuda.set_device(0)
     w_raw, x_raw, W, X = _device_inputs(wl, torch)
@@ -483,7 +609,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 mfma (fp32/fp64 accumulate) + fp64 cholesky + fp32 sweep",
+        "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": wl.name, "rows": rows, "n": n, "tokens": tokens, "bits": wl.bits,
                    "group_size": wl.group_size, "sym": wl.sym, "desc_act": wl.desc_act, "damp": wl.damp,
@@ -499,6 +625,7 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": hess_tflops / PEAK_BF16_TFLOPS,
             "traffic": traffic,
+            "layer_solve": layer_solve_roofline([(rows, n, wl.bits, wl.group_size)], [(n, tokens)], st),
         },
         "cpu_baseline": None,
     }

@@ -248,6 +248,44 @@ gptq_status gptq_matmul_static(const void* A, gptq_dtype adt, int64_t M, int64_t
                                const int32_t* col_order, int64_t rows, int64_t n, int32_t bits, int32_t group_size,
                                void* Y, gptq_dtype ydt, int64_t ldy, void* stream);
 
+/* ------------------------------------------------------------------------- *
+ * Forward of one decoder block, for block-sequential calibration (wikiprompt.org
+ * "GPTQ", "Approche technique": the layers are treated one after another;
+ * polydesk.ai "GPTQ", "Comment fonctionne l'algorithme GPTQ": each linear is
+ * solved on the activations that reach it).  Together with gptq_matmul (fp32
+ * output) they produce the inputs of o_proj, gate/up and down_proj of a
+ * Llama-2-shaped block from the already-quantized q/k/v and gate/up weights.
+ * All pointers are device pointers; arrays are row-major; T tokens are whole
+ * sequences of seq_len tokens, one after another.  Every call only enqueues
+ * work on `stream`, allocates nothing and returns GPTQ_ERR_INVALID_ARG /
+ * GPTQ_ERR_UNSUPPORTED before any launch on bad arguments; T == 0 is a no-op.
+ *
+ * gptq_rmsnorm: h = X (+ R when R != NULL), per token
+ *     Y = fp16(h / sqrt(mean(h^2) + eps))        (unit norm weight)
+ *   X   [T, ldx] of xdt, ldx >= d; R fp32 [T, d] or NULL;
+ *   H_out fp32 [T, d] or NULL: receives h;  Y fp16 bits [T, d].
+ *   The mean and the scaling are computed in fp64, Y rounded once (to nearest
+ *   even).
+ * gptq_rope: rotary position embedding, in place on Q and K (fp32 [T, d],
+ *   heads of head_dim): inside each head, features i and i + head_dim/2 are
+ *   rotated by the angle p * base^(-2i/head_dim), p = token index mod seq_len.
+ *   Angles, sines and cosines in fp64; the rotation in fp32.
+ * gptq_causal_attention: O = fp16(softmax(q k^T / sqrt(head_dim)) v) per head
+ *   and sequence, each token attending to itself and the tokens before it in
+ *   its sequence.  Q, K, V fp32 [T, d] (16-byte aligned), O fp16 bits [T, d].
+ *   fp32 arithmetic (online softmax over key steps of 32), one rounding to
+ *   fp16.  head_dim must be 128 (GPTQ_ERR_UNSUPPORTED otherwise).
+ * gptq_silu_mul: Y[i] = fp16(silu(G[i]) * U[i]), silu(x) = x / (1 + e^-x),
+ *   in fp64 with one rounding; G, U fp32 [count], Y fp16 bits [count].
+ * ------------------------------------------------------------------------- */
+gptq_status gptq_rmsnorm(const void* X, gptq_dtype xdt, int64_t ldx, const float* R, int64_t T, int64_t d,
+                         double eps, float* H_out, uint16_t* Y, void* stream);
+gptq_status gptq_rope(float* Q, float* K, int64_t T, int64_t d, int64_t head_dim, int64_t seq_len, double base,
+                      void* stream);
+gptq_status gptq_causal_attention(const float* Q, const float* K, const float* V, int64_t T, int64_t d,
+                                  int64_t head_dim, int64_t seq_len, uint16_t* O, void* stream);
+gptq_status gptq_silu_mul(const float* G, const float* U, int64_t count, uint16_t* Y, void* stream);
+
 /* Message for the last failing call on this thread (empty string if none). */
 const char* gptq_last_error(void);
 /* Library version string. */

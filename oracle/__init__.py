@@ -22,3 +22,4 @@ from .gptq import (  # noqa: F401
     quantize_layer, gptq_layer, rtn, obs_bruteforce, pack, unpack,
     dequantize, dequant_matmul, grouped_order, rel_loss, to_fp16,
 )
+from . import block  # noqa: F401  (block-sequential calibration: forward of one decoder block)

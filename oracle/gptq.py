@@ -245,12 +245,21 @@ def sweep(Wp, U, cfg: QuantConfig, qdtype=np.float64, block=None, stop=None, fol
               of the columns already quantized on this path;
       zeros:  tol = 2 * tie_tol * (tol scale at the group's argmin column +
               at its argmax column), from the first-order error of -xmin/s.
+      stored scales ("scales" [n/gs, rows], fp16 values): the scale is kept
+              in working precision for the sweep and stored rounded to fp16;
+              where the other solver stored the other fp16 neighbour, it is
+              taken if s lies within tol_s * s of the fp16 midpoint between
+              the two, tol_s = tie_tol * (tol scale at the argmin column +
+              at the argmax column) / (range of the grid in steps) + 2^-22
+              (the first-order error of s from its extremes, plus the
+              binary32 rounding of s).
     ``tie_tol`` is the relative arithmetic error allowed on the magnitudes
     that make up the compensated weight.  Otherwise it keeps its own choice.
-    The result then carries "follow" = dict(ties, zero_ties, unexplained,
-    ratio_max): how many choices were taken from ``follow`` as verified ties,
-    how many differing choices were not ties (kept), and the largest
-    |distance to the midpoint| / tol among the ties taken.
+    The result then carries "follow" = dict(ties, zero_ties, scale_ties,
+    unexplained, ratio_max): how many choices were taken from ``follow`` as
+    verified ties, how many differing choices were not ties (kept), and the
+    largest |distance to the midpoint| / tol among the ties taken; and "S16",
+    the stored fp16 scales with the followed ones in place.
     ``record=True`` (unblocked only) also returns, in sweep order, the
     position of every decision on its own path: "t" [rows, n] = w/s + z before
     rounding, "tol_scale" [rows, n] = (|w0_j| + sum_k |e_k||U_kj|) / s, and for
@@ -282,10 +291,12 @@ def sweep(Wp, U, cfg: QuantConfig, qdtype=np.float64, block=None, stop=None, fol
     if follow is not None:
         f_codes = np.asarray(follow["codes"], dtype=np.int64)
         f_zeros = follow.get("zeros")
+        f_scales = follow.get("scales")
         tau = float(tie_tol)
-        fst = dict(ties=0, zero_ties=0, unexplained=0, ratio_max=0.0)
+        fst = dict(ties=0, zero_ties=0, scale_ties=0, unexplained=0, ratio_max=0.0)
+        S16 = np.zeros((ngroups, rows), dtype=np.float16)
     else:
-        f_codes = f_zeros = None
+        f_codes = f_zeros = f_scales = None
     if record:
         rec_t = np.zeros((rows, n))
         rec_scale = np.zeros((rows, n))
@@ -299,15 +310,34 @@ def sweep(Wp, U, cfg: QuantConfig, qdtype=np.float64, block=None, stop=None, fol
                 return dict(W=W, codes=codes, E=E, L=loss)
             if j % gs == 0:
                 s, z = grid_params(W[:, j:j + gs], cfg.bits, cfg.sym, qdtype)
-                if tracking and not cfg.sym:
+                if tracking:
                     wg = W[:, j:j + gs]
                     scale = (w0[:, j:j + gs] + A[:, j:j + gs]) / np.abs(s)[:, None]
                     r = np.arange(rows)
-                    zscale = 2 * (scale[r, wg.argmin(axis=1)] + scale[r, wg.argmax(axis=1)])
+                    ext = scale[r, wg.argmin(axis=1)] + scale[r, wg.argmax(axis=1)]
+                    zscale = 2 * ext
                     xmin = np.minimum(wg.astype(dt).min(axis=1), dt(0))
-                    if record:
+                    if record and not cfg.sym:
                         rec_zq[j // gs] = -xmin / s
                         rec_zs[j // gs] = zscale
+                if f_codes is not None:
+                    s16 = to_fp16(s)
+                    if f_scales is not None:
+                        xmax = np.maximum(wg.astype(dt).max(axis=1), dt(0))
+                        span = np.maximum(xmax - xmin, np.maximum(-xmin, xmax)) / s   # the grid's range in steps
+                        tol_s = tau * ext / np.maximum(span, 1.0) + 2.0 ** -22
+                        alt = np.asarray(f_scales[j // gs], dtype=np.float16)
+                        adjacent = np.nextafter(s16, alt) == alt
+                        mid = (s16.astype(np.float64) + alt.astype(np.float64)) / 2
+                        m_s = np.abs(np.asarray(s, dtype=np.float64) - mid) / (tol_s * np.abs(s))
+                        differ = alt != s16
+                        ok = differ & adjacent & (m_s <= 1.0)
+                        fst["scale_ties"] += int(np.sum(ok))
+                        fst["unexplained"] += int(np.sum(differ & ~ok))
+                        if np.any(ok):
+                            fst["ratio_max"] = max(fst["ratio_max"], float(m_s[ok].max()))
+                        s16 = np.where(ok, alt, s16)
+                    S16[j // gs] = s16
                 if f_zeros is not None and not cfg.sym:
                     tol = tau * zscale
                     alt = np.asarray(f_zeros[j // gs], dtype=np.float64)
@@ -351,6 +381,7 @@ def sweep(Wp, U, cfg: QuantConfig, qdtype=np.float64, block=None, stop=None, fol
     out = dict(codes=codes, S=S, Z=Z, What=What, E=E, L=loss)
     if follow is not None:
         out["follow"] = fst
+        out["S16"] = S16
     if record:
         out.update(t=rec_t, tol_scale=rec_scale, zq=rec_zq, zq_scale=rec_zs)
     return out
@@ -387,7 +418,8 @@ def quantize_layer(W, U, perm, dead, cfg: QuantConfig, qdtype=np.float64, block=
     What[:, perm] = r["What"]
     g_idx = np.empty(n, dtype=np.int32)
     g_idx[perm] = np.arange(n) // gs
-    out = dict(qweight=pack(codes, cfg.bits), scales=to_fp16(r["S"]), zeros=to_fp16(r["Z"]),
+    out = dict(qweight=pack(codes, cfg.bits), scales=r["S16"] if "S16" in r else to_fp16(r["S"]),
+               zeros=to_fp16(r["Z"]),
                g_idx=g_idx, codes=codes, What=What, L=r["L"], S=r["S"], Z=r["Z"],
                codes_sweep=r["codes"], E=r["E"])
     for k in ("follow", "t", "tol_scale", "zq", "zq_scale"):

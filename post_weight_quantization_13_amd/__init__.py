@@ -46,6 +46,7 @@ EXPORTS = (
     "gptq_layer_loss_workspace_bytes", "gptq_layer_loss",
     "gptq_matmul_packed_bytes", "gptq_matmul_pack", "gptq_matmul_workspace_bytes", "gptq_matmul",
     "gptq_matmul_static_scratch_bytes", "gptq_matmul_static",
+    "gptq_rmsnorm", "gptq_rope", "gptq_causal_attention", "gptq_silu_mul",
     "gptq_last_error", "gptq_version",
 )
 
@@ -126,6 +127,15 @@ def lib() -> ctypes.CDLL:
     L.gptq_matmul_static.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, i64,
                                      vp]
     L.gptq_matmul_static.restype = ctypes.c_int
+    dbl = ctypes.c_double
+    L.gptq_rmsnorm.argtypes = [vp, ctypes.c_int, i64, vp, i64, i64, dbl, vp, vp, vp]
+    L.gptq_rmsnorm.restype = ctypes.c_int
+    L.gptq_rope.argtypes = [vp, vp, i64, i64, i64, i64, dbl, vp]
+    L.gptq_rope.restype = ctypes.c_int
+    L.gptq_causal_attention.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, vp]
+    L.gptq_causal_attention.restype = ctypes.c_int
+    L.gptq_silu_mul.argtypes = [vp, vp, i64, vp, vp]
+    L.gptq_silu_mul.restype = ctypes.c_int
     L.gptq_last_error.argtypes = []
     L.gptq_last_error.restype = ctypes.c_char_p
     L.gptq_version.argtypes = []
@@ -395,6 +405,58 @@ def gptq_matmul_static(A, packed, col_order, rows: int, n: int, bits: int, group
                                     bits, group_size, _ptr(Y), _dtype_code(Y), ldy, _stream(stream, dev)))
 
 
+def gptq_rmsnorm(X, Y, R=None, H_out=None, eps: float = 1e-5, stream=None) -> None:
+    """Y (fp16 [T, d]) = rmsnorm(X + R); H_out (fp32 [T, d], optional) = X + R."""
+    import torch
+    if X.dim() != 2:
+        raise ValueError("X must be a 2-D tensor")
+    T, d = X.shape
+    dev = X.device
+    _need(Y, "Y", torch.float16, (T, d), dev)
+    if R is not None:
+        _need(R, "R", torch.float32, (T, d), dev)
+    if H_out is not None:
+        _need(H_out, "H_out", torch.float32, (T, d), dev)
+    ldx = _row_major_2d(X, "X")
+    _check(lib().gptq_rmsnorm(_ptr(X), _dtype_code(X), ldx, _ptr(R), T, d, float(eps), _ptr(H_out), _ptr(Y),
+                              _stream(stream, dev)))
+
+
+def gptq_rope(Q, K, head_dim: int, seq_len: int, base: float = 10000.0, stream=None) -> None:
+    """Rotary embedding of Q and K (fp32 [T, d]) in place; positions are token index mod seq_len."""
+    import torch
+    if Q.dim() != 2:
+        raise ValueError("Q must be a 2-D tensor")
+    T, d = Q.shape
+    _need(Q, "Q", torch.float32, (T, d), Q.device)
+    _need(K, "K", torch.float32, (T, d), Q.device)
+    _check(lib().gptq_rope(_ptr(Q), _ptr(K), T, d, head_dim, seq_len, float(base), _stream(stream, Q.device)))
+
+
+def gptq_causal_attention(Q, K, V, head_dim: int, seq_len: int, O, stream=None) -> None:
+    """O (fp16 [T, d]) = causal softmax attention of fp32 Q, K, V per head and sequence."""
+    import torch
+    if Q.dim() != 2:
+        raise ValueError("Q must be a 2-D tensor")
+    T, d = Q.shape
+    dev = Q.device
+    for t, name in ((Q, "Q"), (K, "K"), (V, "V")):
+        _need(t, name, torch.float32, (T, d), dev)
+    _need(O, "O", torch.float16, (T, d), dev)
+    _check(lib().gptq_causal_attention(_ptr(Q), _ptr(K), _ptr(V), T, d, head_dim, seq_len, _ptr(O),
+                                       _stream(stream, dev)))
+
+
+def gptq_silu_mul(G, U, Y, stream=None) -> None:
+    """Y (fp16) = silu(G) * U elementwise (G, U fp32 of Y's shape)."""
+    import torch
+    dev = G.device
+    _need(G, "G", torch.float32, tuple(Y.shape), dev)
+    _need(U, "U", torch.float32, tuple(Y.shape), dev)
+    _need(Y, "Y", torch.float16, tuple(Y.shape), dev)
+    _check(lib().gptq_silu_mul(_ptr(G), _ptr(U), Y.numel(), _ptr(Y), _stream(stream, dev)))
+
+
 def gptq_version() -> str:
     return lib().gptq_version().decode()
 
@@ -513,3 +575,81 @@ def quantize_block(X_sets, weights, xset_of, cfg, want_loss: bool = True):
         outs.append(out)
     return outs, Hs
 
+
+# The linears of a Llama-2-shaped decoder block, in calibration order, and the
+# stage whose activations each one reads.
+BLOCK_LINEARS = ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")
+BLOCK_STAGES = (("attn_in", (0, 1, 2)), ("o_in", (3,)), ("mlp_in", (4, 5)), ("down_in", (6,)))
+
+
+def calibrate_block_sequential(X0, weights, cfg, seq_len: int, head_dim: int = 128, eps: float = 1e-5,
+                               rope_base: float = 10000.0, keep_acts: bool = False):
+    """Block-sequential calibration of one Llama-2-shaped decoder block: each
+    linear is quantized on the activations that reach it through the
+    already-quantized linears before it (wikiprompt "Approche technique": the
+    layers are treated one after another).
+
+      Xa = rmsnorm(X0)                          -> Hessian, quantize q, k, v
+      Q, K, V = Xa (q, k, v)^T (gptq_matmul), rope(Q), rope(K)
+      Xo = causal attention                     -> Hessian, quantize o
+      h1 = X0 + Xo o^T, Xm = rmsnorm(h1)        -> Hessian, quantize gate, up
+      Xd = silu(Xm gate^T) * (Xm up^T)          -> Hessian, quantize down
+
+    X0: [T, d] device tensor (bf16, fp16 or fp32), whole sequences of seq_len
+    tokens; weights: the seven [rows, n] device tensors in BLOCK_LINEARS order.
+    Every step runs in the library's kernels; this function only sequences
+    the calls and allocates their outputs.  Returns (outs, Hs, acts): outs a
+    list of seven dicts (qweight, scales, zeros, g_idx, loss), Hs the four
+    stages' Hessians by stage name, acts the stages' fp16 inputs by name (only
+    with keep_acts; otherwise each is freed once its consumers ran).
+    """
+    import torch
+    T, d = X0.shape
+    dev = X0.device
+    f = weights[4].shape[0]
+    outs, Hs, acts = [None] * 7, {}, {}
+    f32, f16 = torch.float32, torch.float16
+
+    def solve(stage, X, idx):
+        H, _ = hessian(X)
+        Hs[stage] = H
+        U, perm, dead = prepare(H, cfg)
+        for li in idx:
+            outs[li] = quantize_layer(U, perm, dead, cfg, weights[li])
+        del U, perm, dead
+        return [PackedLayer(outs[li]["qweight"], outs[li]["scales"], outs[li]["zeros"], outs[li]["g_idx"],
+                            cfg.bits, cfg.group_size) for li in idx]
+
+    Xa = torch.empty((T, d), dtype=f16, device=dev)
+    gptq_rmsnorm(X0, Xa, eps=eps)
+    pq, pk, pv = solve("attn_in", Xa, (0, 1, 2))
+    Q, K, V = (p.matmul(Xa, out_dtype=f32) for p in (pq, pk, pv))
+    del pq, pk, pv
+    if keep_acts:
+        acts["attn_in"] = Xa
+    del Xa
+    gptq_rope(Q, K, head_dim, seq_len, rope_base)
+    Xo = torch.empty((T, d), dtype=f16, device=dev)
+    gptq_causal_attention(Q, K, V, head_dim, seq_len, Xo)
+    del Q, K, V
+    (po,) = solve("o_in", Xo, (3,))
+    O = po.matmul(Xo, out_dtype=f32)
+    if keep_acts:
+        acts["o_in"] = Xo
+    del Xo, po
+    Xm = torch.empty((T, d), dtype=f16, device=dev)
+    gptq_rmsnorm(X0, Xm, R=O, eps=eps)
+    del O
+    pg, pu = solve("mlp_in", Xm, (4, 5))
+    G = pg.matmul(Xm, out_dtype=f32)
+    Uu = pu.matmul(Xm, out_dtype=f32)
+    if keep_acts:
+        acts["mlp_in"] = Xm
+    del Xm, pg, pu
+    Xd = torch.empty((T, f), dtype=f16, device=dev)
+    gptq_silu_mul(G, Uu, Xd)
+    del G, Uu
+    solve("down_in", Xd, (6,))
+    if keep_acts:
+        acts["down_in"] = Xd
+    return outs, Hs, acts

@@ -38,6 +38,13 @@ hipError_t launch_matmul(const void* A, int64_t M, int64_t lda, const void* pack
                          void* ws, hipStream_t s);
 size_t matmul_static_scratch_bytes();
 hipError_t matmul_static_scratch(void** ptr);
+int attention_head_dim();
+hipError_t launch_rmsnorm(const void* X, int dt, int64_t ldx, const float* R, int64_t T, int64_t d, double eps,
+                          float* hout, uint16_t* Y, hipStream_t s);
+hipError_t launch_rope(float* Q, float* K, int64_t T, int64_t d, int64_t hd, int64_t L, double base, hipStream_t s);
+hipError_t launch_attention(const float* Q, const float* K, const float* V, int64_t T, int64_t d, int64_t L,
+                            uint16_t* O, hipStream_t s);
+hipError_t launch_silu_mul(const float* G, const float* U, int64_t count, uint16_t* Y, hipStream_t s);
 }  // namespace gptq
 
 namespace {
@@ -334,6 +341,68 @@ gptq_status gptq_matmul(const void* A, gptq_dtype adt, int64_t M, int64_t lda, c
   hipError_t e = gptq::launch_matmul(A, M, lda, packed, col_order, rows, n, bits, group_size, Y,
                                      static_cast<int>(ydt), ldy, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("gptq_matmul", e);
+  return ok();
+}
+
+// ----------------------------------------------------------------------------- block forward
+gptq_status gptq_rmsnorm(const void* X, gptq_dtype xdt, int64_t ldx, const float* R, int64_t T, int64_t d,
+                         double eps, float* H_out, uint16_t* Y, void* stream) {
+  if (T < 0 || T > ((int64_t)1 << 31) - 4) return fail(GPTQ_ERR_INVALID_ARG, "T=%lld out of range", (long long)T);
+  if (d < 1 || d > kMaxDim) return fail(GPTQ_ERR_INVALID_ARG, "d=%lld out of range", (long long)d);
+  if (!valid_dtype(xdt)) return fail(GPTQ_ERR_INVALID_ARG, "unknown dtype %d", (int)xdt);
+  if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(GPTQ_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (T == 0) return ok();
+  if (!X || !Y) return fail(GPTQ_ERR_INVALID_ARG, "NULL X or Y");
+  if (ldx < d) return fail(GPTQ_ERR_INVALID_ARG, "ldx=%lld < d=%lld", (long long)ldx, (long long)d);
+  hipError_t e = gptq::launch_rmsnorm(X, static_cast<int>(xdt), ldx, R, T, d, eps, H_out, Y,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("gptq_rmsnorm", e);
+  return ok();
+}
+
+gptq_status gptq_rope(float* Q, float* K, int64_t T, int64_t d, int64_t head_dim, int64_t seq_len, double base,
+                      void* stream) {
+  if (head_dim < 2 || head_dim % 2 || head_dim > 1024)
+    return fail(GPTQ_ERR_INVALID_ARG, "head_dim=%lld must be even, 2..1024", (long long)head_dim);
+  if (d < head_dim || d % head_dim || d > kMaxDim)
+    return fail(GPTQ_ERR_INVALID_ARG, "d=%lld must be a multiple of head_dim=%lld", (long long)d, (long long)head_dim);
+  if (seq_len < 1 || T < 0 || T % seq_len)
+    return fail(GPTQ_ERR_INVALID_ARG, "T=%lld must be a multiple of seq_len=%lld >= 1", (long long)T,
+                (long long)seq_len);
+  if (T * (head_dim / 2) > ((int64_t)1 << 40)) return fail(GPTQ_ERR_INVALID_ARG, "T too large");
+  if (!(base > 0.0) || !std::isfinite(base)) return fail(GPTQ_ERR_INVALID_ARG, "base must be finite and > 0");
+  if (T == 0) return ok();
+  if (!Q || !K) return fail(GPTQ_ERR_INVALID_ARG, "NULL Q or K");
+  hipError_t e = gptq::launch_rope(Q, K, T, d, head_dim, seq_len, base, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("gptq_rope", e);
+  return ok();
+}
+
+gptq_status gptq_causal_attention(const float* Q, const float* K, const float* V, int64_t T, int64_t d,
+                                  int64_t head_dim, int64_t seq_len, uint16_t* O, void* stream) {
+  if (head_dim != gptq::attention_head_dim())
+    return fail(GPTQ_ERR_UNSUPPORTED, "head_dim=%lld (supported: %d)", (long long)head_dim,
+                gptq::attention_head_dim());
+  if (d < head_dim || d % head_dim || d / head_dim > 65535)
+    return fail(GPTQ_ERR_INVALID_ARG, "d=%lld must be a multiple of head_dim=%lld", (long long)d, (long long)head_dim);
+  if (seq_len < 1 || seq_len > ((int64_t)1 << 24) || T < 0 || T % seq_len || T / seq_len > 65535)
+    return fail(GPTQ_ERR_INVALID_ARG, "T=%lld must be a multiple of seq_len=%lld (at most 65535 sequences)",
+                (long long)T, (long long)seq_len);
+  if (T == 0) return ok();
+  if (!Q || !K || !V || !O) return fail(GPTQ_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V))
+    return fail(GPTQ_ERR_INVALID_ARG, "Q, K and V must be 16-byte aligned");
+  hipError_t e = gptq::launch_attention(Q, K, V, T, d, seq_len, O, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("gptq_causal_attention", e);
+  return ok();
+}
+
+gptq_status gptq_silu_mul(const float* G, const float* U, int64_t count, uint16_t* Y, void* stream) {
+  if (count < 0) return fail(GPTQ_ERR_INVALID_ARG, "count=%lld < 0", (long long)count);
+  if (count == 0) return ok();
+  if (!G || !U || !Y) return fail(GPTQ_ERR_INVALID_ARG, "NULL pointer argument");
+  hipError_t e = gptq::launch_silu_mul(G, U, count, Y, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("gptq_silu_mul", e);
   return ok();
 }
 

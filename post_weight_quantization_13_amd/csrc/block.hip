@@ -1,0 +1,304 @@
+// Forward of one decoder block on gfx950, for block-sequential calibration.
+//
+// wikiprompt.org "GPTQ", "Approche technique": the layers are treated one after
+// another; polydesk.ai "GPTQ", "Comment fonctionne l'algorithme GPTQ": each
+// linear is solved on the input activations that calibration data produce.
+// Inside a Llama-2-shaped block the inputs of o_proj and down_proj are
+// therefore produced by the already-quantized q/k/v and gate/up projections
+// (gptq_matmul, fp32 outputs) through the pieces below:
+//   rmsnorm_kernel      y = fp16(h / sqrt(mean(h^2) + eps)), h = x (+ residual)
+//   rope_kernel         rotary embedding of q and k, in place (fp32)
+//   attention_kernel    causal softmax(q k^T / sqrt(128)) v per head -> fp16
+//   silu_mul_kernel     y = fp16(silu(g) * u)
+// Every linear's input is held in fp16 (rounded to nearest even), the form the
+// dequantizing matmul reads.  The row statistics of the norm, the rotation
+// angles and the gating are computed in fp64 so that the only rounding that
+// matters is the final one to fp16; the attention runs in fp32.
+#include "common.hpp"
+
+#include <cmath>
+
+namespace gptq {
+namespace {
+
+// ---------------------------------------------------------------- fp64 -> fp16
+__device__ __forceinline__ double half_value(uint16_t b) {
+  _Float16 h;
+  __builtin_memcpy(&h, &b, 2);
+  return static_cast<double>(h);
+}
+
+// Next fp16 bit pattern toward +inf / -inf (finite inputs).
+__device__ __forceinline__ uint16_t half_up(uint16_t b) {
+  if (b & 0x8000u) return b == 0x8000u ? uint16_t(1) : uint16_t(b - 1);
+  return uint16_t(b + 1);
+}
+__device__ __forceinline__ uint16_t half_down(uint16_t b) {
+  if (b & 0x8000u) return uint16_t(b + 1);
+  return b == 0 ? uint16_t(0x8001u) : uint16_t(b - 1);
+}
+
+// fp64 -> fp16 bit pattern, round to nearest even, in one rounding: the
+// conversion through fp32 can round twice when the fp32 value falls exactly
+// on an fp16 midpoint; the neighbour on v's side is then the nearer one.
+__device__ __forceinline__ uint16_t double_to_half_bits(double v) {
+  uint16_t b = float_to_half_bits(static_cast<float>(v));
+  const double hv = half_value(b);
+  if (hv != v && fabs(hv) < 65504.0) {
+    const uint16_t nb = v > hv ? half_up(b) : half_down(b);
+    if (fabs(v - half_value(nb)) < fabs(v - hv)) b = nb;
+  }
+  return b;
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// One wave per row: h = x + r (r optional, fp32), s = sum h^2 in fp64,
+// y = fp16(h / sqrt(s / d + eps)); h is also written as fp32 when hout != null.
+template <int DT>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ X, int64_t ldx,
+                                                      const float* __restrict__ R, int64_t T, int d, double eps,
+                                                      float* __restrict__ hout, uint16_t* __restrict__ Y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= T) return;
+  const int64_t xo = row * ldx, ro = row * static_cast<int64_t>(d);
+  double ss = 0.0;
+  for (int c = lane; c < d; c += 64) {
+    double h = load_as_float<DT>(X, xo + c);
+    if (R) h += R[ro + c];
+    ss = fma(h, h, ss);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+  const double inv = 1.0 / sqrt(ss / d + eps);
+  for (int c = lane; c < d; c += 64) {
+    double h = load_as_float<DT>(X, xo + c);
+    if (R) h += R[ro + c];
+    if (hout) hout[ro + c] = static_cast<float>(h);
+    Y[ro + c] = double_to_half_bits(h * inv);
+  }
+}
+
+// ---------------------------------------------------------------- RoPE
+// Thread (t, i): position p = t mod L, frequency base^(-2i/hd); rotates the
+// pair (i, i + hd/2) of every head of q and k at token t.  Angle and its sine
+// and cosine in fp64, the rotation in fp32.
+__global__ __launch_bounds__(256) void rope_kernel(float* __restrict__ Q, float* __restrict__ K, int64_t T, int d,
+                                                   int hd, int L, double base) {
+  const int half = hd / 2;
+  const int64_t id = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (id >= T * half) return;
+  const int64_t t = id / half;
+  const int i = static_cast<int>(id % half);
+  const double ang = static_cast<double>(t % L) * pow(base, -2.0 * i / hd);
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  const float s = static_cast<float>(sd), c = static_cast<float>(cd);
+  float* q = Q + t * d;
+  float* k = K + t * d;
+  for (int h = 0; h < d / hd; ++h) {
+    const int a = h * hd + i, b = a + half;
+    const float qa = q[a], qb = q[b], ka = k[a], kb = k[b];
+    q[a] = qa * c - qb * s;
+    q[b] = qb * c + qa * s;
+    k[a] = ka * c - kb * s;
+    k[b] = kb * c + ka * s;
+  }
+}
+
+// ---------------------------------------------------------------- attention
+// Work-group: 64 queries of one head of one sequence; keys in steps of 32
+// with an online softmax (running max and sum per query).  Thread t: query
+// group qg = t/16 (queries 4qg..4qg+3) and lane-in-group g = t%16, which
+// scores keys g and g+16 of a step and accumulates output dims 4g..4g+3 and
+// 64+4g..64+4g+3.  LDS rows are padded so that the 16 lanes of a group read
+// 16 different rows (scores) or 16 consecutive float4 (values) without bank
+// conflicts.  fp32 throughout; the output is divided by the softmax sum and
+// rounded to fp16 once.
+constexpr int kHD = 128;
+constexpr int kQB = 64;
+constexpr int kKB = 32;
+constexpr int kRow = kHD + 4;
+struct AttnSmem {
+  float q[kQB][kRow];
+  float k[kKB][kRow];
+  float v[kKB][kHD];
+  float p[kQB][kKB + 1];
+};
+
+__global__ __launch_bounds__(256, 2) void attention_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                           const float* __restrict__ V, int d, int L,
+                                                           uint16_t* __restrict__ O) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
+  const int tid = threadIdx.x, qg = tid >> 4, g = tid & 15;
+  const int q0 = blockIdx.x * kQB;
+  const int64_t base = static_cast<int64_t>(blockIdx.z) * L;
+  const int col = blockIdx.y * kHD;
+  const float scale = 0.08838834764831845f;   // 1 / sqrt(128)
+
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int e = tid + 256 * r, row = e >> 5, c4 = (e & 31) * 4;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (q0 + row < L) v = *reinterpret_cast<const f32x4*>(Q + (base + q0 + row) * d + col + c4);
+    *reinterpret_cast<f32x4*>(&sm.q[row][c4]) = v;
+  }
+  float m[4], l[4], acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[i][c] = 0.f;
+  }
+  const int kend = min(q0 + kQB, L);
+  for (int k0 = 0; k0 < kend; k0 += kKB) {
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = tid + 256 * r, row = e >> 5, c4 = (e & 31) * 4;
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      if (k0 + row < L) {
+        kv = *reinterpret_cast<const f32x4*>(K + (base + k0 + row) * d + col + c4);
+        vv = *reinterpret_cast<const f32x4*>(V + (base + k0 + row) * d + col + c4);
+      }
+      *reinterpret_cast<f32x4*>(&sm.k[row][c4]) = kv;
+      *reinterpret_cast<f32x4*>(&sm.v[row][c4]) = vv;
+    }
+    __syncthreads();
+    float s[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i][0] = s[i][1] = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < kHD; c += 4) {
+      f32x4 qv[4], kv[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[i] = *reinterpret_cast<const f32x4*>(&sm.q[4 * qg + i][c]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) kv[j] = *reinterpret_cast<const f32x4*>(&sm.k[g + 16 * j][c]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float t = fmaf(qv[i][0], kv[j][0], s[i][j]);
+          t = fmaf(qv[i][1], kv[j][1], t);
+          t = fmaf(qv[i][2], kv[j][2], t);
+          s[i][j] = fmaf(qv[i][3], kv[j][3], t);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qi = q0 + 4 * qg + i;
+      float bm = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int kj = k0 + g + 16 * j;
+        s[i][j] = (kj <= qi && kj < L) ? s[i][j] * scale : -INFINITY;
+        bm = fmaxf(bm, s[i][j]);
+      }
+#pragma unroll
+      for (int w = 8; w >= 1; w >>= 1) bm = fmaxf(bm, __shfl_xor(bm, w, 16));
+      const float mn = fmaxf(m[i], bm);   // key k0 <= qi always: finite
+      const float alpha = expf(m[i] - mn);
+      float bs = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float p = expf(s[i][j] - mn);
+        sm.p[4 * qg + i][g + 16 * j] = p;
+        bs += p;
+      }
+#pragma unroll
+      for (int w = 8; w >= 1; w >>= 1) bs += __shfl_xor(bs, w, 16);
+      l[i] = l[i] * alpha + bs;
+      m[i] = mn;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[i][c] *= alpha;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < kKB; ++kk) {
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(&sm.v[kk][4 * g]);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&sm.v[kk][64 + 4 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = sm.p[4 * qg + i][kk];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[i][c] = fmaf(p, v0[c], acc[i][c]);
+          acc[i][4 + c] = fmaf(p, v1[c], acc[i][4 + c]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qi = q0 + 4 * qg + i;
+    if (qi >= L) continue;
+    const float inv = 1.0f / l[i];
+    uint16_t* o = O + (base + qi) * d + col;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      o[4 * g + c] = float_to_half_bits(acc[i][c] * inv);
+      o[64 + 4 * g + c] = float_to_half_bits(acc[i][4 + c] * inv);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- SiLU gate
+__global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__ G, const float* __restrict__ U,
+                                                       int64_t count, uint16_t* __restrict__ Y) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < count;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    const double gv = G[i];
+    Y[i] = double_to_half_bits(gv / (1.0 + exp(-gv)) * static_cast<double>(U[i]));
+  }
+}
+
+}  // namespace
+
+int attention_head_dim() { return kHD; }
+
+hipError_t launch_rmsnorm(const void* X, int dt, int64_t ldx, const float* R, int64_t T, int64_t d, double eps,
+                          float* hout, uint16_t* Y, hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>((T + 3) / 4);
+  const int dd = static_cast<int>(d);
+  switch (dt) {
+    case DT_BF16: hipLaunchKernelGGL(rmsnorm_kernel<DT_BF16>, dim3(blocks), dim3(256), 0, s, X, ldx, R, T, dd, eps, hout, Y); break;
+    case DT_FP16: hipLaunchKernelGGL(rmsnorm_kernel<DT_FP16>, dim3(blocks), dim3(256), 0, s, X, ldx, R, T, dd, eps, hout, Y); break;
+    case DT_FP32: hipLaunchKernelGGL(rmsnorm_kernel<DT_FP32>, dim3(blocks), dim3(256), 0, s, X, ldx, R, T, dd, eps, hout, Y); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rope(float* Q, float* K, int64_t T, int64_t d, int64_t hd, int64_t L, double base, hipStream_t s) {
+  const int64_t threads = T * (hd / 2);
+  hipLaunchKernelGGL(rope_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, Q, K, T,
+                     static_cast<int>(d), static_cast<int>(hd), static_cast<int>(L), base);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const float* Q, const float* K, const float* V, int64_t T, int64_t d, int64_t L,
+                            uint16_t* O, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attention_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sizeof(AttnSmem)));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  dim3 grid(static_cast<unsigned>((L + kQB - 1) / kQB), static_cast<unsigned>(d / kHD), static_cast<unsigned>(T / L));
+  hipLaunchKernelGGL(attention_kernel, grid, dim3(256), sizeof(AttnSmem), s, Q, K, V, static_cast<int>(d),
+                     static_cast<int>(L), O);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul(const float* G, const float* U, int64_t count, uint16_t* Y, hipStream_t s) {
+  int64_t blocks = (count + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(silu_mul_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, G, U, count, Y);
+  return hipGetLastError();
+}
+
+}  // namespace gptq

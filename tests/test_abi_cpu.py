@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(g):
     names = _declared()
-    assert len(names) == 17, names
+    assert len(names) == 21, names
     assert set(names) == set(g.EXPORTS)
     L = g.lib()
     for n in names:
@@ -147,6 +147,32 @@ def test_matmul_queries_and_validation(g):
     assert st(M=0) == g.GPTQ_OK
     assert st(M=65, n=32768, order=FAKE) == g.GPTQ_ERR_WORKSPACE   # 65 x 32768 fp16 > 4 MiB
     assert b"4194304" in L.gptq_last_error()
+
+
+def test_block_forward_validation(g):
+    L = g.lib()
+    # rmsnorm: X, xdt, ldx, R, T, d, eps, H_out, Y, stream
+    assert L.gptq_rmsnorm(FAKE, 0, 64, None, 4, 0, 1e-5, None, FAKE, None) == g.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_rmsnorm(FAKE, 0, 32, None, 4, 64, 1e-5, None, FAKE, None) == g.GPTQ_ERR_INVALID_ARG   # ldx < d
+    assert L.gptq_rmsnorm(FAKE, 9, 64, None, 4, 64, 1e-5, None, FAKE, None) == g.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_rmsnorm(FAKE, 0, 64, None, 4, 64, -1.0, None, FAKE, None) == g.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_rmsnorm(None, 0, 64, None, 4, 64, 1e-5, None, FAKE, None) == g.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_rmsnorm(None, 0, 64, None, 0, 64, 1e-5, None, None, None) == g.GPTQ_OK             # T == 0
+    # rope: Q, K, T, d, head_dim, seq_len, base, stream
+    assert L.gptq_rope(FAKE, FAKE, 512, 256, 127, 256, 1e4, None) == g.GPTQ_ERR_INVALID_ARG       # odd head_dim
+    assert L.gptq_rope(FAKE, FAKE, 512, 200, 128, 256, 1e4, None) == g.GPTQ_ERR_INVALID_ARG       # d % head_dim
+    assert L.gptq_rope(FAKE, FAKE, 500, 256, 128, 256, 1e4, None) == g.GPTQ_ERR_INVALID_ARG       # T % seq_len
+    assert L.gptq_rope(FAKE, FAKE, 512, 256, 128, 256, 0.0, None) == g.GPTQ_ERR_INVALID_ARG
+    # attention: Q, K, V, T, d, head_dim, seq_len, O, stream
+    assert L.gptq_causal_attention(FAKE, FAKE, FAKE, 512, 256, 64, 256, FAKE, None) == g.GPTQ_ERR_UNSUPPORTED
+    assert L.gptq_causal_attention(FAKE, FAKE, FAKE, 500, 256, 128, 256, FAKE, None) == g.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_causal_attention(FAKE, FAKE, None, 512, 256, 128, 256, FAKE, None) == g.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_causal_attention(ctypes.c_void_p(0x1004), FAKE, FAKE, 512, 256, 128, 256, FAKE,
+                                   None) == g.GPTQ_ERR_INVALID_ARG                               # unaligned Q
+    assert L.gptq_causal_attention(None, None, None, 0, 256, 128, 256, None, None) == g.GPTQ_OK
+    assert L.gptq_silu_mul(FAKE, FAKE, -1, FAKE, None) == g.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_silu_mul(None, FAKE, 10, FAKE, None) == g.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_silu_mul(None, None, 0, None, None) == g.GPTQ_OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, g):

@@ -163,8 +163,10 @@ def test_follow_own_result_changes_nothing():
     cfg = oracle.QuantConfig(bits=4, group_size=32)
     p = oracle.prepare(H, cfg.damp)
     a = oracle.sweep(W, p["U"], cfg)
-    b = oracle.sweep(W, p["U"], cfg, follow=dict(codes=a["codes"], zeros=a["Z"]), tie_tol=TAU)
-    assert b["follow"] == dict(ties=0, zero_ties=0, unexplained=0, ratio_max=0.0)
+    b = oracle.sweep(W, p["U"], cfg, follow=dict(codes=a["codes"], zeros=a["Z"], scales=oracle.to_fp16(a["S"])),
+                     tie_tol=TAU)
+    assert b["follow"] == dict(ties=0, zero_ties=0, scale_ties=0, unexplained=0, ratio_max=0.0)
+    assert np.array_equal(b["S16"], oracle.to_fp16(a["S"]))
     for k in ("codes", "S", "Z", "What", "E"):
         assert np.array_equal(a[k], b[k]), k
     assert a["L"] == b["L"]
@@ -321,3 +323,32 @@ def test_record_positions_and_tolerance_scale():
     np.testing.assert_allclose(r["tol_scale"], (np.abs(W) + A) / s_col, rtol=1e-12)
     # zero-point positions: -xmin/s of each group's (compensated) weights rounds to Z
     assert np.array_equal(np.rint(r["zq"]), r["Z"])
+
+
+def test_follow_stored_scale_tie():
+    """A group whose scale lies exactly on the midpoint between two adjacent
+    fp16 values: both roundings are correct stored forms; the other one is
+    taken (and only the stored scale changes, not the sweep), while a scale
+    two fp16 steps away is not."""
+    h1 = np.float16(0.0034)
+    h2 = np.nextafter(h1, np.float16(1))
+    s_mid = (float(h1) + float(h2)) / 2                     # exact in float64
+    rng = np.random.default_rng(14)
+    W = rng.uniform(0, 15 * s_mid, size=(3, 32))
+    W[:, 0] = 15 * s_mid                                     # xmax; xmin = 0 -> s = s_mid exactly
+    cfg = oracle.QuantConfig(bits=4, group_size=32)
+    a = oracle.sweep(W, np.eye(32), cfg)
+    assert np.all(a["S"][0] == s_mid)
+    mine = oracle.to_fp16(a["S"])
+    other = np.where(mine == h1, h2, h1).astype(np.float16)
+    b = oracle.sweep(W, np.eye(32), cfg, follow=dict(codes=a["codes"], scales=other), tie_tol=TAU)
+    assert b["follow"]["scale_ties"] == 3 and b["follow"]["unexplained"] == 0
+    assert np.array_equal(b["S16"], other)
+    assert np.array_equal(b["codes"], a["codes"]) and np.array_equal(b["S"], a["S"])
+    far = np.nextafter(other, np.float16(1) if other[0, 0] > mine[0, 0] else np.float16(0))
+    c = oracle.sweep(W, np.eye(32), cfg, follow=dict(codes=a["codes"], scales=far), tie_tol=TAU)
+    assert c["follow"]["scale_ties"] == 0 and c["follow"]["unexplained"] == 3
+    assert np.array_equal(c["S16"], mine)
+    q = oracle.quantize_layer(W, np.eye(32), np.arange(32), np.zeros(32, bool), cfg,
+                              follow=dict(codes=a["codes"], scales=other), tie_tol=TAU)
+    assert np.array_equal(q["scales"], other)              # the stored output carries the followed scale
