@@ -35,6 +35,17 @@ constexpr int kBlk = 128;     // lazy-batch block = group size
 constexpr int kSuper = 512;   // columns per outer lazy batch (a multiple of kBlk)
 constexpr int kSub = 16;      // sub-block kept in registers inside the sweep
 constexpr int kRowsSweep = 64;
+// Row stride of the sweep's staged block of W (Ws[column][row]): one float of
+// padding, so that 32 lanes reading 32 different columns at one row offset
+// (the MFMA accumulator layout of the far and pending updates) hit 32
+// different banks, while the chain's reads (one column, lane = row) stay
+// conflict-free.
+constexpr int kWs = kRowsSweep + 1;
+// The errors of a sub-block, Es[t][row ^ es_swz(t)]: the far update's MFMA
+// operand has lanes 0-31 on column t and lanes 32-63 on t + 1 at the same
+// rows; flipping bit 5 of the row on odd t puts the two halves on disjoint
+// banks.
+__device__ __forceinline__ int es_swz(int t) { return (t & 1) << 5; }
 
 // ---------------------------------------------------------------- gather
 // Wk[r][j] = W[r][perm[j]] as fp32 (0 for dead columns).  Four consecutive
@@ -165,7 +176,7 @@ struct PendSeg {
   int urow;            // first row of U matching column 0 of E
 };
 
-__device__ __forceinline__ void pending_update(float (*Ws)[kRowsSweep], const uint16_t* __restrict__ UTh,
+__device__ __forceinline__ void pending_update(float (*Ws)[kWs], const uint16_t* __restrict__ UTh,
                                                const uint16_t* __restrict__ UTl, int n, int rows, int rbase, int i1,
                                                int ldE, const PendSeg& sa, const PendSeg& sb, PendSmem& sm) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -324,8 +335,9 @@ __global__ void __launch_bounds__(256) row_params_kernel(const float* __restrict
 //   wave 0   : the sequential chain -- quantize column j, e_j = (w - q) / U_jj,
 //              rank-1 update of the remaining columns of the sub-block (the
 //              16x16 block of U is read into registers first);
-//   waves 1-3: meanwhile apply the errors of sub-block s-1 to the columns
-//              from sub-block s+1 on ("far" update, fp32 MFMA);
+//   waves 1-3: meanwhile write the split errors of sub-block s-1 and apply
+//              them to the columns from sub-block s+1 on ("far" update, fp32
+//              MFMA);
 //   barrier; all waves apply the errors of sub-block s to the columns of
 //   sub-block s+1 ("near" update, which the next chain step needs); barrier.
 // Codes: c = clamp(rint(w / s) + z).  Each sub-block's chain first runs with
@@ -349,7 +361,7 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
     uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, double* __restrict__ rowloss, int gs,
     const float* __restrict__ rowsz) {
   __shared__ __attribute__((aligned(16))) float UT[kBlk][kBlk + 4];
-  __shared__ float Ws[kBlk][kRowsSweep];
+  __shared__ float Ws[kBlk][kWs];
   __shared__ __attribute__((aligned(16))) PendSmem psm;
   __shared__ float Es[2][kSub][kRowsSweep];
   __shared__ float rdiag[kBlk];
@@ -462,7 +474,7 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
 #pragma unroll
       for (int ks = 0; ks < kSub / 2; ++ks) {
         const int t = 2 * ks + (lane >> 5);
-        a[ks] = Ep[t][32 * rt + (lane & 31)];
+        a[ks] = Ep[t][(32 * rt + (lane & 31)) ^ es_swz(t)];
         b[ks] = on ? UT[col][jp + t] : 0.0f;
       }
 #pragma unroll
@@ -478,13 +490,36 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
       }
     }
   };
+  // Waves 1-3: the errors of sub-block sp as split bf16 planes (hi, lo) into
+  // Eh/El for the later lazy updates, off the chain wave.  Wave 1 writes
+  // columns 0-7 of the sub-block, wave 2 columns 8-15 (four per 8-byte store).
+  auto store_split = [&](int sp) {
+    if (!valid || wave == 3) return;
+    const int jp = sp * kSub + 8 * (wave - 1);
+#pragma unroll
+    for (int h4 = 0; h4 < 2; ++h4) {
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int t = 8 * (wave - 1) + 4 * h4 + d;
+        const float v = Es[sp & 1][t][lane ^ es_swz(t)];
+        h[d] = bf16_rne_bits(v);
+        l[d] = bf16_rne_bits(v - __uint_as_float(h[d] << 16));
+      }
+      *reinterpret_cast<uint2*>(ehrow + jp + 4 * h4) = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      *reinterpret_cast<uint2*>(elrow + jp + 4 * h4) = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+    }
+  };
   for (int sb = 0; sb < kSubs; ++sb) {
     const int j0 = sb * kSub;
     // A group starting inside the block: the errors of sub-block sb-1 reach
     // all of its columns first, then its parameters are taken.
     const bool gstart = sb > 0 && sb % gsub == 0;
     if (gstart) {
-      if (wave > 0) far_update(sb);
+      if (wave > 0) {
+        store_split(sb - 1);
+        far_update(sb);
+      }
       __syncthreads();
       if (wave == 0) group_params(j0, gs);
     }
@@ -510,6 +545,9 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
       // The chain of one sub-block.  EXACT = false forms w / s as w * (1/s)
       // and reports whether any quotient came within near_midpoint<BITS>() of
       // a rounding midpoint; EXACT = true uses IEEE division throughout.
+      float rd[kSub];  // 1 / U_jj of the sub-block, read once, off the chain
+#pragma unroll
+      for (int t = 0; t < kSub; ++t) rd[t] = rdiag[j0 + t];
       auto chain = [&](auto exact_tag, uint32_t (&cw)[kSub / 4], float& lsum) -> bool {
         constexpr bool EXACT = decltype(exact_tag)::value;
         float w[kSub];
@@ -527,8 +565,8 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
           }
           const float c = fminf(fmaxf(rintf(qt) + zv, lo), maxq);
           const float q = sv * (c - zv);
-          const float et = (w[t] - q) * rdiag[j0 + t];
-          Es[sb & 1][t][lane] = et;
+          const float et = (w[t] - q) * rd[t];
+          Es[sb & 1][t][lane ^ es_swz(t)] = et;
           lsum = fmaf(et, et, lsum);
           cw[t >> 2] |= static_cast<uint32_t>(c) << (8 * (t & 3));
 #pragma unroll
@@ -548,28 +586,19 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
       loss += static_cast<double>(lsum);
       if (valid) {
 #pragma unroll
-        for (int t4 = 0; t4 < kSub / 4; ++t4) {
-          *reinterpret_cast<uint32_t*>(crow + j0 + 4 * t4) = cw[t4];
-          uint32_t h[4], l[4];
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const float v = Es[sb & 1][4 * t4 + d][lane];
-            h[d] = bf16_rne_bits(v);
-            l[d] = bf16_rne_bits(v - __uint_as_float(h[d] << 16));
-          }
-          *reinterpret_cast<uint2*>(ehrow + j0 + 4 * t4) = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-          *reinterpret_cast<uint2*>(elrow + j0 + 4 * t4) = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
-        }
+        for (int t4 = 0; t4 < kSub / 4; ++t4) *reinterpret_cast<uint32_t*>(crow + j0 + 4 * t4) = cw[t4];
       }
     } else if (sb >= 1 && !gstart) {
+      store_split(sb - 1);
       far_update(sb);
     }
     __syncthreads();
     if (sb + 1 < kSubs) {
-      // near update: errors of sub-block sb onto the 16 columns of sub-block sb+1
+      // near update: errors of sub-block sb onto the 16 columns of sub-block
+      // sb+1, four columns per wave
       float ec[kSub];
 #pragma unroll
-      for (int t = 0; t < kSub; ++t) ec[t] = Es[sb & 1][t][lane];
+      for (int t = 0; t < kSub; ++t) ec[t] = Es[sb & 1][t][lane ^ es_swz(t)];
       const int kn = j0 + kSub + wave * (kSub / 4);
       float acc[kSub / 4];
 #pragma unroll
@@ -591,6 +620,7 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
       __syncthreads();
     }
   }
+  if (wave > 0) store_split(kSubs - 1);   // Es of the last sub-block is final after the last barrier
   if (wave == 0 && valid) rowloss[r] += 0.5 * loss;
 }
 
@@ -851,9 +881,12 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
 
   // Lazy updates in super-blocks of kSuper columns.  A block's sweep applies
   // to its own rows and columns the errors of the earlier blocks of its
-  // super-block and of the whole previous super-block (pending_update); the
-  // errors of super-block j reach the columns from super-block j+2 on in one
-  // wide update (K = kSuper) on a second stream, overlapping the sweeps of
+  // super-block (pending_update).  The errors of super-block j reach the next
+  // super-block's columns in one update over the whole chip on the caller's
+  // stream right after its sweeps (K = kSuper; a sweep work-group would apply
+  // the same product to its 64 x 128 block through a latency-bound chunk
+  // pipeline, several times slower), and the columns from super-block j+2
+  // on in one wide update on a second stream, overlapping the sweeps of
   // super-block j+1.  Super-block j+2 waits for that update before it starts.
   // E holds the errors of two super-blocks (alternating), [rows, kSuper] each.
   const dim3 grid((rows + kRowsSweep - 1) / kRowsSweep);
@@ -888,7 +921,7 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
       if (e != hipSuccess) return e;
       joined[j & 1] = true;
     }
-    const PendSeg sa{Eph, Epl, (j > 0) ? kSuper : 0, s1 - kSuper};
+    const PendSeg sa{Eph, Epl, 0, s1 - kSuper};  // the previous super-block: already applied
     for (int i1 = s1; i1 < s2; i1 += kBlk) {
       const PendSeg sb{Ejh, Ejl, i1 - s1, s1};
       uint16_t* Ebh = Ejh + (i1 - s1);
@@ -897,6 +930,12 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
   launch_sweep<B, S>(grid, s, Wk, U, UTh, UTl, n, rows, i1, codes, Ebh, Ebl, sa, sb, scales, zeros, rowloss, gs, rowsz)
       GPTQ_BY_BITS_SYM(GPTQ_SWEEP);
 #undef GPTQ_SWEEP
+      GPTQ_CHECK_LAUNCH();
+    }
+    if (s2 < n) {  // the next super-block's columns, before its sweeps
+      const int ne = (s2 + kSuper < n) ? s2 + kSuper : n;
+      hipLaunchKernelGGL(trailing_kernel, dim3((ne - s2 + 127) / 128, rt), dim3(256), 0, s, Wk, Ejh, Ejl, kSuper,
+                         UTh, UTl, n, rows, s1, s2 - s1, s2, ne);
       GPTQ_CHECK_LAUNCH();
     }
     const int wide = s2 + kSuper;  // first column of super-block j+2
