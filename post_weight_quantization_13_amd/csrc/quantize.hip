@@ -887,7 +887,9 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
   // the same product to its 64 x 128 block through a latency-bound chunk
   // pipeline, several times slower), and the columns from super-block j+2
   // on in one wide update on a second stream, overlapping the sweeps of
-  // super-block j+1.  Super-block j+2 waits for that update before it starts.
+  // super-block j+1.  The caller's stream joins that wide update before the
+  // update of super-block j+2's columns from super-block j+1, the next write
+  // of those columns there.
   // E holds the errors of two super-blocks (alternating), [rows, kSuper] each.
   const dim3 grid((rows + kRowsSweep - 1) / kRowsSweep);
   const int rt = (rows + 127) / 128;
@@ -933,6 +935,14 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
       GPTQ_CHECK_LAUNCH();
     }
     if (s2 < n) {  // the next super-block's columns, before its sweeps
+      // The wide update of super-block j-1 writes these columns too (it
+      // covers every column from super-block j+1 on): join it first, or the
+      // two read-modify-writes of the same columns race.
+      if (!joined[(j + 1) & 1]) {
+        e = hipStreamWaitEvent(s, ev_join[(j + 1) & 1], 0);
+        if (e != hipSuccess) return e;
+        joined[(j + 1) & 1] = true;
+      }
       const int ne = (s2 + kSuper < n) ? s2 + kSuper : n;
       hipLaunchKernelGGL(trailing_kernel, dim3((ne - s2 + 127) / 128, rt), dim3(256), 0, s, Wk, Ejh, Ejl, kSuper,
                          UTh, UTl, n, rows, s1, s2 - s1, s2, ne);
