@@ -21,7 +21,8 @@
  *   - All array pointers are DEVICE pointers (memory of the current HIP device)
  *     unless a comment says "host".  The caller owns every buffer; the library
  *     never allocates or frees device memory.  Scratch space is passed in as a
- *     workspace whose size is given by the matching *_workspace_bytes() query.
+ *     workspace whose size is given by the matching *_workspace_bytes() query;
+ *     a query returns 0 for sizes its call rejects.
  *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
  *     enqueued on it in order; calls return once the work is enqueued, except
  *     where a comment says the call synchronizes the stream.
@@ -53,7 +54,15 @@ typedef enum {
   GPTQ_ERR_WORKSPACE = -5     /* workspace null or smaller than the query returned    */
 } gptq_status;
 
+/* In C++ the element type's underlying type is fixed to int32_t, so every
+ * int32 a caller passes is a value of the type and an unknown code can be
+ * rejected (without a fixed type C++ leaves such a value undefined); the
+ * layout is the same 32-bit integer as the C declaration's. */
+#ifdef __cplusplus
+typedef enum : int32_t { GPTQ_BF16 = 0, GPTQ_FP16 = 1, GPTQ_FP32 = 2 } gptq_dtype;
+#else
 typedef enum { GPTQ_BF16 = 0, GPTQ_FP16 = 1, GPTQ_FP32 = 2 } gptq_dtype;
+#endif
 
 /* The quantize config of the pages ("Configurações de quantização", "Paramètres clés"). */
 typedef struct {

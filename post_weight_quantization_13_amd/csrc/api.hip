@@ -174,7 +174,7 @@ gptq_status gptq_hessian_accumulate(double* H, int64_t n, int64_t* n_tokens, con
 // ----------------------------------------------------------------------------- prepare
 size_t gptq_prepare_workspace_bytes(int64_t n, const gptq_config* cfg) {
   (void)cfg;
-  if (n < 1) return 0;
+  if (n < 1 || n > 65535) return 0;  // the sizes gptq_prepare_hinv accepts
   return gptq::prepare_workspace(n);
 }
 
@@ -198,7 +198,7 @@ gptq_status gptq_prepare_hinv(const double* H, int64_t n, const gptq_config* cfg
 // ----------------------------------------------------------------------------- quantize
 size_t gptq_quantize_workspace_bytes(int64_t rows, int64_t n, const gptq_config* cfg) {
   (void)cfg;
-  if (rows < 1 || n < 1) return 0;
+  if (rows < 1 || rows > (int64_t)1 << 30 || n < 1 || n > kMaxDim) return 0;  // as gptq_quantize_layer
   return gptq::quantize_workspace(rows, n);
 }
 
@@ -232,7 +232,7 @@ gptq_status gptq_quantize_layer(const float* U, const int32_t* perm, const uint8
 
 // ----------------------------------------------------------------------------- loss
 size_t gptq_layer_loss_workspace_bytes(int64_t rows, int64_t n) {
-  if (rows < 1 || n < 1) return 0;
+  if (rows < 1 || rows > (int64_t)1 << 30 || n < 1 || n > kMaxDim) return 0;  // as gptq_layer_loss
   return gptq::loss_workspace(rows, n);
 }
 
@@ -289,7 +289,7 @@ gptq_status gptq_matmul_pack(const int32_t* qweight, const uint16_t* scales, con
 }
 
 size_t gptq_matmul_workspace_bytes(int64_t M, int64_t n, int32_t has_col_order) {
-  if (M < 1 || n < 1 || !has_col_order) return 0;
+  if (M < 1 || M > (int64_t)65535 * 16 || n < 1 || n > kMaxDim || !has_col_order) return 0;  // as gptq_matmul
   return gptq::matmul_workspace_bytes(M, n);
 }
 
@@ -369,7 +369,7 @@ gptq_status gptq_rope(float* Q, float* K, int64_t T, int64_t d, int64_t head_dim
   if (seq_len < 1 || T < 0 || T % seq_len)
     return fail(GPTQ_ERR_INVALID_ARG, "T=%lld must be a multiple of seq_len=%lld >= 1", (long long)T,
                 (long long)seq_len);
-  if (T * (head_dim / 2) > ((int64_t)1 << 40)) return fail(GPTQ_ERR_INVALID_ARG, "T too large");
+  if (T > ((int64_t)1 << 40) / (head_dim / 2)) return fail(GPTQ_ERR_INVALID_ARG, "T too large");
   if (!(base > 0.0) || !std::isfinite(base)) return fail(GPTQ_ERR_INVALID_ARG, "base must be finite and > 0");
   if (T == 0) return ok();
   if (!Q || !K) return fail(GPTQ_ERR_INVALID_ARG, "NULL Q or K");
