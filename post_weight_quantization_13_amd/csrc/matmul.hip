@@ -40,6 +40,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -526,6 +527,214 @@ __global__ __launch_bounds__(NW * 64) void dequant_matmul_kernel(
   }
 }
 
+// ------------------------------------------------------------------ prefill
+// Many tokens (M >= kPrefillMin): one workgroup of 4 waves per tile of 128
+// tokens x 64 outputs, wave (wm, wn) owning 64 x 32 as 4 x 2 MFMA tiles of
+// 16 x 16 (at 64 x 64 a wave needs every register, one wave per SIMD, and
+// cannot hide its own loads: 315 TFLOP/s on a 262144-token projection).  For
+// each 128-column chunk the tile's activations (128 x 128 halves) are staged
+// in LDS, double buffered, rows padded to 136 halves so a fragment read (16
+// lanes on 16 tokens, 16 bytes each) touches distinct banks; the activations
+// and codes of the two chunks after it are in flight in registers meanwhile.
+// Each wave loads its output tiles' codes straight from the
+// packed layer (a lane's bytes of a chunk are its B operand for the chunk's
+// four steps), turns them into the exact fp16 integers code - zero and scales
+// each group's fp32 partial sum by the group's scale when the group ends, as
+// the decode kernel does, so the two kernels round alike.  The hardware
+// deals work-group b to XCD b % 8; the tiles are ordered so that all output
+// tiles of a token tile go to one XCD, which then fetches those 128 token
+// rows from memory once and serves the rest from its L2.
+constexpr int kPM = 128;                 // tokens per tile
+constexpr int kPNT = 2;                  // 16-output tiles per wave
+constexpr int kPN = 2 * 16 * kPNT;       // outputs per tile (two waves across)
+constexpr int kPStride = kChunk + 8;     // halves per staged token row
+constexpr int kPrefillMin = 1024;        // tokens from which the prefill kernel runs
+// activations two chunks ahead where that fits in registers without spilling
+// (not with two groups per chunk), else one
+template <int BITS, int SPC>
+constexpr int kPrefillDepth = 2;
+
+template <int BITS, int SPC, int DEPTH>
+__global__ __launch_bounds__(256, 2) void prefill_matmul_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
+                                                             const uint32_t* __restrict__ Q,
+                                                             const uint32_t* __restrict__ SZ, int rows, int n, int gs,
+                                                             void* __restrict__ Y, int ydt, int64_t ldy, int tm_count,
+                                                             int tn_count) {
+  using U = Unpack<BITS>;
+  __shared__ __align__(16) _Float16 abuf[2][kPM][kPStride];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+  const int tmt = 8 * (local / tn_count) + xcd, tnt = local % tn_count;
+  if (tmt >= tm_count) return;  // the grid is rounded up to whole groups of 8 token tiles
+  const int m0 = tmt * kPM, o0 = tnt * kPN;
+  const int C = n / kChunk;
+  const int Cs = gs > 0 ? C : 1;
+  const int j = lane & 15, q = lane >> 4;
+  const int Tcount = (rows + 15) / 16;
+  // this wave's packed output tiles (clamped past the last: loaded, dropped)
+  const uint32_t* qb[kPNT];
+  const uint32_t* szb[kPNT];
+#pragma unroll
+  for (int nt = 0; nt < kPNT; ++nt) {
+    const int T = min(o0 / 16 + kPNT * wn + nt, Tcount - 1);
+    qb[nt] = Q + (static_cast<int64_t>(T) * C * 64 + lane) * U::kWords;
+    szb[nt] = SZ + static_cast<int64_t>(T) * Cs * 16 * SPC + j * SPC;
+  }
+  // activations: piece p = tid + 256 v is token p / 16, halves 8 (p % 16) ..
+  // of the chunk; tokens past M read token M - 1 (their outputs are dropped)
+  u32x4 areg[DEPTH][8];  // DEPTH register sets of activations on their way to LDS
+  auto a_load = [&](int c, int set) {
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int p = tid + 256 * v;
+      const int tm = min(m0 + (p >> 4), M - 1);
+      areg[set][v] = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(tm) * lda + c * kChunk + 8 * (p & 15));
+    }
+  };
+  auto a_store = [&](int buf, int set) {
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int p = tid + 256 * v;
+      *reinterpret_cast<u32x4*>(&abuf[buf][p >> 4][8 * (p & 15)]) = areg[set][v];
+    }
+  };
+  // codes and scale/zero words of a chunk, two slots
+  uint32_t breg[2][kPNT][U::kWords];
+  uint32_t szr[2][kPNT][SPC];
+  auto b_load = [&](int c, int d) {
+#pragma unroll
+    for (int nt = 0; nt < kPNT; ++nt) {
+      load_chunk<BITS>(qb[nt] + static_cast<int64_t>(c) * 64 * U::kWords, breg[d][nt]);
+#pragma unroll
+      for (int g = 0; g < SPC; ++g) szr[d][nt][g] = szb[nt][(gs > 0 ? c : 0) * 16 * SPC + g];
+    }
+  };
+  f4 yacc[4][kPNT], gacc[4][kPNT];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < kPNT; ++nt) {
+      yacc[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+      gacc[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+  constexpr int kGroupSteps = 4 / SPC;
+
+  // one chunk from LDS buffer `buf` and code slot `d`
+  auto chunk = [&](int buf, int d) {
+    h2 zc[kPNT][4];
+    float sc[kPNT];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t % kGroupSteps == 0) {
+#pragma unroll
+        for (int nt = 0; nt < kPNT; ++nt) {
+          const uint32_t sz = szr[d][nt][t / kGroupSteps];
+          sc[nt] = half_bits_to_float(static_cast<uint16_t>(sz & 0xFFFFu));
+          const _Float16 z = __builtin_bit_cast(_Float16, static_cast<uint16_t>(sz >> 16));
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const _Float16 c0 = -(static_cast<_Float16>(U::kBase[v]) + z);
+            zc[nt][v] = h2{c0, c0};
+          }
+        }
+      }
+      h8 bb[kPNT], aa[4];
+#pragma unroll
+      for (int nt = 0; nt < kPNT; ++nt) bb[nt] = U::step(breg[d][nt], t, zc[nt]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        aa[mt] = *reinterpret_cast<const h8*>(&abuf[buf][64 * wm + 16 * mt + j][32 * t + 8 * q]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < kPNT; ++nt)
+          gacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aa[mt], bb[nt], gacc[mt][nt], 0, 0, 0);
+      if (t % kGroupSteps == kGroupSteps - 1) {  // the group ends: scale its partial sums
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < kPNT; ++nt) {
+            yacc[mt][nt] += sc[nt] * gacc[mt][nt];
+            gacc[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+          }
+        if constexpr (SPC == 2) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // Chunk c is computed from LDS buffer c & 1 and code slot c & 1; the chunk
+  // after it is staged into the other buffer (last read in chunk c - 1,
+  // before the previous barrier).  DEPTH 2: chunk c + 2's activations are
+  // loaded before chunk c is computed, its codes after; DEPTH 1: chunk c + 1's
+  // codes before, chunk c + 2's activations after.  Loads past the last chunk
+  // re-read it, so every step issues the same loads with no branch (a branch
+  // around a load makes the compiler wait for all loads in flight where the
+  // paths join); the loop is unrolled by two so that the register slots are
+  // compile-time constants (indexed at run time they would live in scratch).
+  const int last = C - 1;
+  a_load(0, 0);
+  b_load(0, 0);
+  if constexpr (DEPTH == 2) {
+    a_load(min(1, last), 1);
+    b_load(min(1, last), 1);
+    a_store(0, 0);
+  } else {
+    a_store(0, 0);
+    a_load(min(1, last), 0);
+  }
+  __syncthreads();
+  auto step = [&](auto par, int c) {
+    constexpr int P = decltype(par)::value;
+    if constexpr (DEPTH == 2) {
+      a_load(min(c + 2, last), P);
+      __builtin_amdgcn_sched_barrier(0);  // issued before the chunk, not sunk below it
+      chunk(P, P);
+      b_load(min(c + 2, last), P);
+      a_store(P ^ 1, P ^ 1);
+    } else {
+      b_load(min(c + 1, last), P ^ 1);
+      chunk(P, P);
+      a_store(P ^ 1, 0);
+      a_load(min(c + 2, last), 0);
+    }
+    __syncthreads();
+  };
+  int c = 0;
+  for (; c + 1 < C; c += 2) {
+    step(std::integral_constant<int, 0>{}, c);
+    step(std::integral_constant<int, 1>{}, c + 1);
+  }
+  if (c < C) step(std::integral_constant<int, 0>{}, c);
+
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < kPNT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = m0 + 64 * wm + 16 * mt + acc_row(lane, r);
+        const int o = o0 + 16 * kPNT * wn + 16 * nt + j;
+        if (tok < M && o < rows) {
+          const int64_t idx = static_cast<int64_t>(tok) * ldy + o;
+          if (ydt == DT_FP32) static_cast<float*>(Y)[idx] = yacc[mt][nt][r];
+          else static_cast<uint16_t*>(Y)[idx] = float_to_half_bits(yacc[mt][nt][r]);
+        }
+      }
+}
+
+template <int BITS, int SPC>
+hipError_t launch_prefill(const uint16_t* A, int64_t lda, int M, const uint32_t* Q, const uint32_t* SZ, int rows,
+                          int n, int gs, void* Y, int ydt, int64_t ldy, hipStream_t s) {
+  const int tm = (M + kPM - 1) / kPM, tn = (rows + kPN - 1) / kPN;
+  const int64_t blocks = static_cast<int64_t>((tm + 7) / 8) * 8 * tn;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_matmul_kernel<BITS, SPC, kPrefillDepth<BITS, SPC>>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, A, lda,
+                     M, Q, SZ, rows, n, gs, Y, ydt, ldy, tm, tn);
+  return hipGetLastError();
+}
+
 template <int BITS, int SPC, bool FULL, int NW, int PIECES = 1>
 hipError_t launch_mm_v(const uint16_t* A, int64_t lda, int M, const uint32_t* Q, const uint32_t* SZ, int rows,
                        int n, int gs, void* Y, int ydt, int64_t ldy, size_t lds, hipStream_t s) {
@@ -547,6 +756,7 @@ hipError_t launch_mm_v(const uint16_t* A, int64_t lda, int M, const uint32_t* Q,
 template <int BITS, int SPC>
 hipError_t launch_mm(const uint16_t* A, int64_t lda, int M, const uint32_t* Q, const uint32_t* SZ, int rows, int n,
                      int gs, void* Y, int ydt, int64_t ldy, hipStream_t s) {
+  if (M >= kPrefillMin) return launch_prefill<BITS, SPC>(A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy, s);
   const int ms = M < kMTile ? M : kMTile;
   const int T = (rows + 15) / 16;
   const int64_t tiles = static_cast<int64_t>(T) * ((M + kMTile - 1) / kMTile);

@@ -82,6 +82,13 @@ CASES = [
     (4, 128, False, 32, 4096, 16, "fp32"),   # activations beyond the LDS budget: windowed staging
     (2, 32, False, 16, 5120, 9, "fp32"),     # windowed, odd number of rounds
     (3, 64, True, 48, 3072, 12, "fp32"),
+    # prefill sizes (1024 tokens and up): 128-token x 128-output tiles
+    (4, 128, False, 200, 1152, 1100, "fp32"),   # ragged token and output tiles, 9 chunks
+    (4, 32, True, 300, 1024, 1024, "fp16"),     # act-order, four groups per chunk
+    (3, 64, True, 96, 512, 1030, "fp16"),
+    (2, -1, False, 64, 640, 1500, "fp32"),      # one group per row
+    (8, 128, False, 130, 384, 2048, "fp32"),
+    (8, 32, False, 16, 256, 1024, "fp32"),
 ]
 
 
