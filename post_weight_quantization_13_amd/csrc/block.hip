@@ -107,23 +107,33 @@ __global__ __launch_bounds__(256) void rope_kernel(float* __restrict__ Q, float*
 }
 
 // ---------------------------------------------------------------- attention
-// Work-group: 64 queries of one head of one sequence; keys in steps of 32
-// with an online softmax (running max and sum per query).  Thread t: query
-// group qg = t/16 (queries 4qg..4qg+3) and lane-in-group g = t%16, which
-// scores keys g and g+16 of a step and accumulates output dims 4g..4g+3 and
-// 64+4g..64+4g+3.  LDS rows are padded so that the 16 lanes of a group read
-// 16 different rows (scores) or 16 consecutive float4 (values) without bank
-// conflicts.  fp32 throughout; the output is divided by the softmax sum and
-// rounded to fp16 once.
+// Work-group: 64 queries of one head of one sequence, wave w owning queries
+// 16w .. 16w+15; keys in steps of 64 with an online softmax (running max and
+// sum per query).  Both products run on the fp32 MFMA 16x16x4, transposed so
+// that a lane's query never changes:
+//   scores  S^T = K Q^T: A = a key row from LDS, B = the lane's own query
+//           (128 dims held in registers), 32 steps over the head dimension;
+//           lane (i, g) = (lane % 16, lane / 16) gets keys 16t + 4g + r of
+//           query i for r = 0..3;
+//   output  O^T += V^T P^T: B = those same probabilities, straight from the
+//           lane's registers (the MFMA's k index r is the key 16t + 4g + r),
+//           A = V[16t + 4g + r][16u + i] read from LDS one float at a time;
+//           lane (i, g) holds dims 16u + 4g + r of query i.
+// The dimension order of a dot product is free as long as K and Q agree: lane
+// group g takes dims 32g .. 32g+31, so a K fragment is a 16-byte LDS read.
+// K and V are staged as loaded, rows padded to 132 floats: the 16 lanes of a
+// group read 16 K rows on distinct banks, and a V read puts lane (i, g) on
+// bank 16g + i (+ a constant).  (V staged transposed, for 16-byte reads,
+// took 4-byte writes that met eight to a bank.)  fp32 products and sums; the
+// output is divided by the softmax sum and rounded to fp16 once.  Query
+// blocks are dealt longest first (the causal key range grows with them).
 constexpr int kHD = 128;
 constexpr int kQB = 64;
-constexpr int kKB = 32;
-constexpr int kRow = kHD + 4;
+constexpr int kKB = 64;
+constexpr int kKRow = kHD + 4;
 struct AttnSmem {
-  float q[kQB][kRow];
-  float k[kKB][kRow];
-  float v[kKB][kHD];
-  float p[kQB][kKB + 1];
+  float k[kKB][kKRow];
+  float v[kKB][kKRow];
 };
 
 __global__ __launch_bounds__(256, 2) void attention_kernel(const float* __restrict__ Q, const float* __restrict__ K,
@@ -131,117 +141,112 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const float* __restri
                                                            uint16_t* __restrict__ O) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
-  const int tid = threadIdx.x, qg = tid >> 4, g = tid & 15;
-  const int q0 = blockIdx.x * kQB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int q0 = (gridDim.x - 1 - blockIdx.x) * kQB;
   const int64_t base = static_cast<int64_t>(blockIdx.z) * L;
   const int col = blockIdx.y * kHD;
+  const int qi = q0 + 16 * wave + i16;   // this lane's query; past L it reads row L - 1, output dropped
   const float scale = 0.08838834764831845f;   // 1 / sqrt(128)
 
+  float qf[32];
+  {
+    const float* qp = Q + (base + min(qi, L - 1)) * d + col + 32 * g;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int e = tid + 256 * r, row = e >> 5, c4 = (e & 31) * 4;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (q0 + row < L) v = *reinterpret_cast<const f32x4*>(Q + (base + q0 + row) * d + col + c4);
-    *reinterpret_cast<f32x4*>(&sm.q[row][c4]) = v;
+    for (int v = 0; v < 8; ++v) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(qp + 4 * v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[4 * v + e] = t[e];
+    }
   }
-  float m[4], l[4], acc[4][8];
+  f32x4 acc[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.f;
+  for (int u = 0; u < 8; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;   // lsum: this lane's share of the query's sum
+
+  // K and V of a key step, 8 pieces of 16 bytes each per thread; rows past
+  // L re-read row L - 1 (their scores are masked, their probabilities 0)
+  f32x4 kreg[8], vreg[8];
+  auto load = [&](int k0) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[i][c] = 0.f;
-  }
+    for (int r = 0; r < 8; ++r) {
+      const int e = tid + 256 * r, row = min(k0 + (e >> 5), L - 1), c4 = (e & 31) * 4;
+      kreg[r] = *reinterpret_cast<const f32x4*>(K + (base + row) * d + col + c4);
+      vreg[r] = *reinterpret_cast<const f32x4*>(V + (base + row) * d + col + c4);
+    }
+  };
   const int kend = min(q0 + kQB, L);
+  const int klast = (kend - 1) / kKB * kKB;
+  load(0);
   for (int k0 = 0; k0 < kend; k0 += kKB) {
-    __syncthreads();
+    __syncthreads();   // every wave is done with the previous step's tiles
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 8; ++r) {
       const int e = tid + 256 * r, row = e >> 5, c4 = (e & 31) * 4;
-      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-      if (k0 + row < L) {
-        kv = *reinterpret_cast<const f32x4*>(K + (base + k0 + row) * d + col + c4);
-        vv = *reinterpret_cast<const f32x4*>(V + (base + k0 + row) * d + col + c4);
-      }
-      *reinterpret_cast<f32x4*>(&sm.k[row][c4]) = kv;
-      *reinterpret_cast<f32x4*>(&sm.v[row][c4]) = vv;
+      *reinterpret_cast<f32x4*>(&sm.k[row][c4]) = kreg[r];
+      *reinterpret_cast<f32x4*>(&sm.v[row][c4]) = vreg[r];
     }
     __syncthreads();
-    float s[4][2];
+    // the next step's tiles load while this one is computed (the last step
+    // re-reads its own: no branch around the loads)
+    load(min(k0 + kKB, klast));
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 st[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i][0] = s[i][1] = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < kHD; c += 4) {
-      f32x4 qv[4], kv[2];
+    for (int t = 0; t < 4; ++t) {
+      st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qv[i] = *reinterpret_cast<const f32x4*>(&sm.q[4 * qg + i][c]);
+      for (int c = 0; c < 8; ++c) {
+        const f32x4 kf = *reinterpret_cast<const f32x4*>(&sm.k[16 * t + i16][32 * g + 4 * c]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) kv[j] = *reinterpret_cast<const f32x4*>(&sm.k[g + 16 * j][c]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          float t = fmaf(qv[i][0], kv[j][0], s[i][j]);
-          t = fmaf(qv[i][1], kv[j][1], t);
-          t = fmaf(qv[i][2], kv[j][2], t);
-          s[i][j] = fmaf(qv[i][3], kv[j][3], t);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int qi = q0 + 4 * qg + i;
-      float bm = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int kj = k0 + g + 16 * j;
-        s[i][j] = (kj <= qi && kj < L) ? s[i][j] * scale : -INFINITY;
-        bm = fmaxf(bm, s[i][j]);
-      }
-#pragma unroll
-      for (int w = 8; w >= 1; w >>= 1) bm = fmaxf(bm, __shfl_xor(bm, w, 16));
-      const float mn = fmaxf(m[i], bm);   // key k0 <= qi always: finite
-      const float alpha = expf(m[i] - mn);
-      float bs = 0.f;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float p = expf(s[i][j] - mn);
-        sm.p[4 * qg + i][g + 16 * j] = p;
-        bs += p;
-      }
-#pragma unroll
-      for (int w = 8; w >= 1; w >>= 1) bs += __shfl_xor(bs, w, 16);
-      l[i] = l[i] * alpha + bs;
-      m[i] = mn;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[i][c] *= alpha;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int kk = 0; kk < kKB; ++kk) {
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(&sm.v[kk][4 * g]);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&sm.v[kk][64 + 4 * g]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = sm.p[4 * qg + i][kk];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          acc[i][c] = fmaf(p, v0[c], acc[i][c]);
-          acc[i][4 + c] = fmaf(p, v1[c], acc[i][4 + c]);
-        }
+        for (int e = 0; e < 4; ++e) st[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[e], qf[4 * c + e], st[t], 0, 0, 0);
       }
     }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kj = k0 + 16 * t + 4 * g + r;
+        st[t][r] = (kj <= qi && kj < L) ? st[t][r] * scale : -INFINITY;
+        bm = fmaxf(bm, st[t][r]);
+      }
+    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    const float mn = fmaxf(m, bm);   // key k0 <= q0 <= qi and k0 < L: finite
+    const float alpha = expf(m - mn);
+    float bs = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        st[t][r] = expf(st[t][r] - mn);
+        bs += st[t][r];
+      }
+    lsum = lsum * alpha + bs;
+    m = mn;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[u][r] *= alpha;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.v[16 * t + 4 * g + r][16 * u + i16], st[t][r], acc[u], 0, 0, 0);
+      }
   }
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (qi < L) {
+    const float inv = 1.0f / lsum;
+    uint16_t* o = O + (base + qi) * d + col + 4 * g;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int qi = q0 + 4 * qg + i;
-    if (qi >= L) continue;
-    const float inv = 1.0f / l[i];
-    uint16_t* o = O + (base + qi) * d + col;
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      o[4 * g + c] = float_to_half_bits(acc[i][c] * inv);
-      o[64 + 4 * g + c] = float_to_half_bits(acc[i][4 + c] * inv);
-    }
+      for (int r = 0; r < 4; ++r) o[16 * u + r] = float_to_half_bits(acc[u][r] * inv);
   }
 }
 
