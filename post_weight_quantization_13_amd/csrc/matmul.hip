@@ -625,6 +625,10 @@ __global__ __launch_bounds__(256, 2) void prefill_matmul_kernel(const uint16_t* 
   auto chunk = [&](int buf, int d) {
     h2 zc[kPNT][4];
     float sc[kPNT];
+    // activation fragments one k-step ahead of the products that use them
+    h8 an[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) an[mt] = *reinterpret_cast<const h8*>(&abuf[buf][64 * wm + 16 * mt + j][8 * q]);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if (t % kGroupSteps == 0) {
@@ -642,10 +646,14 @@ __global__ __launch_bounds__(256, 2) void prefill_matmul_kernel(const uint16_t* 
       }
       h8 bb[kPNT], aa[4];
 #pragma unroll
-      for (int nt = 0; nt < kPNT; ++nt) bb[nt] = U::step(breg[d][nt], t, zc[nt]);
+      for (int mt = 0; mt < 4; ++mt) aa[mt] = an[mt];
+      if (t < 3) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        aa[mt] = *reinterpret_cast<const h8*>(&abuf[buf][64 * wm + 16 * mt + j][32 * t + 8 * q]);
+        for (int mt = 0; mt < 4; ++mt)
+          an[mt] = *reinterpret_cast<const h8*>(&abuf[buf][64 * wm + 16 * mt + j][32 * (t + 1) + 8 * q]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < kPNT; ++nt) bb[nt] = U::step(breg[d][nt], t, zc[nt]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
