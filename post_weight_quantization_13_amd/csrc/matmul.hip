@@ -185,7 +185,41 @@ __global__ __launch_bounds__(256) void pack_sz_kernel(const uint16_t* __restrict
 }
 
 // Activations in the packed column order (act-order layers): At[m, k] =
-// A[m, col_order[k]], row stride n.
+// A[m, col_order[k]], row stride n.  A work-group takes whole rows: the row
+// is staged in LDS (16-byte loads when A is 16-byte aligned with lda a
+// multiple of 8, else 2-byte loads, both coalesced), then each thread
+// gathers 8 consecutive outputs from LDS and writes them as one 16-byte
+// store.  Rows up to kGatherLdsMax columns; longer ones use the plain kernel
+// below.
+constexpr int kGatherLdsMax = 32768;
+template <bool VEC>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ A, int64_t lda,
+                                                          const int32_t* __restrict__ col_order, int M, int n,
+                                                          uint16_t* __restrict__ At) {
+  extern __shared__ __align__(16) uint16_t row_lds[];
+  const int tid = threadIdx.x, pieces = n / 8;
+  for (int m = blockIdx.x; m < M; m += gridDim.x) {
+    const uint16_t* row = A + static_cast<int64_t>(m) * lda;
+    if constexpr (VEC) {
+      for (int p = tid; p < pieces; p += 256)
+        *reinterpret_cast<u32x4*>(&row_lds[8 * p]) = *reinterpret_cast<const u32x4*>(row + 8 * p);
+    } else {
+      for (int k = tid; k < n; k += 256) row_lds[k] = row[k];
+    }
+    __syncthreads();
+    uint16_t* out = At + static_cast<int64_t>(m) * n;
+    for (int p = tid; p < pieces; p += 256) {
+      const int32_t* ix = col_order + 8 * p;   // 4-byte aligned only: plain loads
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = row_lds[ix[2 * e]] | (static_cast<uint32_t>(row_lds[ix[2 * e + 1]]) << 16);
+      *reinterpret_cast<u32x4*>(out + 8 * p) = v;
+    }
+    __syncthreads();  // the row buffer is reloaded next
+  }
+}
+
 __global__ __launch_bounds__(256) void gather_cols_kernel(const uint16_t* __restrict__ A, int64_t lda,
                                                          const int32_t* __restrict__ col_order, int M, int n,
                                                          uint16_t* __restrict__ At) {
@@ -901,11 +935,23 @@ hipError_t launch_matmul(const void* A, int64_t M, int64_t lda, const void* pack
   const uint16_t* a = static_cast<const uint16_t*>(A);
   if (col_order) {
     uint16_t* at = static_cast<uint16_t*>(ws);
-    unsigned gx = static_cast<unsigned>((n + 255) / 256);
-    if (gx > 64) gx = 64;
-    const unsigned gy = static_cast<unsigned>(M < 1024 ? M : 1024);
-    hipLaunchKernelGGL(gather_cols_kernel, dim3(gx, gy), dim3(256), 0, s, a, lda, col_order, static_cast<int>(M),
-                       static_cast<int>(n), at);
+    if (n <= kGatherLdsMax) {
+      const bool vec = (reinterpret_cast<uintptr_t>(a) & 15) == 0 && lda % 8 == 0;
+      const unsigned blocks = static_cast<unsigned>(M < 2048 ? M : 2048);
+      const size_t lds = static_cast<size_t>(n) * 2;
+      if (vec)
+        hipLaunchKernelGGL(gather_rows_kernel<true>, dim3(blocks), dim3(256), lds, s, a, lda, col_order,
+                           static_cast<int>(M), static_cast<int>(n), at);
+      else
+        hipLaunchKernelGGL(gather_rows_kernel<false>, dim3(blocks), dim3(256), lds, s, a, lda, col_order,
+                           static_cast<int>(M), static_cast<int>(n), at);
+    } else {
+      unsigned gx = static_cast<unsigned>((n + 255) / 256);
+      if (gx > 64) gx = 64;
+      const unsigned gy = static_cast<unsigned>(M < 1024 ? M : 1024);
+      hipLaunchKernelGGL(gather_cols_kernel, dim3(gx, gy), dim3(256), 0, s, a, lda, col_order, static_cast<int>(M),
+                         static_cast<int>(n), at);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a = at;

@@ -111,6 +111,33 @@ def test_random_layers(g, bits, gs, act, rows, n, M, out):
     print(f"matmul bits={bits} gs={gs} act={act} {rows}x{n} M={M} {out}: rel {rel:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("n,M,offset,pad", [
+    (1152, 1030, 1, 3),    # unaligned activations, odd row stride: the 2-byte staging of the row gather
+    (32896, 3, 0, 0),      # rows longer than the LDS row buffer: the plain gather
+])
+def test_act_order_gather_paths(g, n, M, offset, pad):
+    """The act-order column gather for activations that are not 16-byte
+    aligned (a view one element into a buffer with an odd row stride) and for
+    rows too long to stage in LDS, against the oracle."""
+    import torch
+    bits, gs, rows = 4, 128, 48
+    seed = 77 + n
+    codes, scales, zeros, g_idx = synth.quantized_layer(seed, rows, n, bits, gs, act_order=True)
+    qw, sc, ze, gi, qweight = _device_layer(codes, scales, zeros, g_idx, bits)
+    layer = g.PackedLayer(qw, sc, ze, gi, bits, gs)
+    assert layer.col_order is not None
+    a16 = synth.decode_activations_raw(seed, M, n).view(np.float16)
+    big = torch.zeros((M, n + pad), dtype=torch.float16, device="cuda")
+    A = big[:, offset:offset + n]
+    A.copy_(torch.from_numpy(a16).cuda())
+    assert (A.data_ptr() % 16 != 0) == (offset != 0) and A.stride(0) == n + pad
+    Y = layer.matmul(A, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Yref, mag = _reference(a16, qweight, scales, zeros, g_idx, bits, rows, n)
+    rel = _check(Y.cpu().numpy().astype(np.float64), Yref, mag, n, "fp32")
+    print(f"act-order gather n={n} M={M} offset={offset} lda={n + pad}: rel {rel:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("desc_act", [False, True])
 def test_layer_from_the_oracle_quantizer(g, desc_act):
     """Codes, scales, zeros and g_idx as the GPTQ sweep itself produces them
