@@ -217,8 +217,9 @@ gptq_status gptq_layer_loss(const double* H, int64_t n, const void* W, gptq_dtyp
  *            columns 0..rows-1 of rows 0..M-1 are written.
  * Products of the fp16 activations with the exact integers code - zero are
  * summed in fp32, each group's sum is scaled by its fp16 scale in fp32, and the
- * result is rounded once to ydt.  Tokens are processed 16 at a time: beyond 16
- * tokens the weights are read once per 16 (the kernel targets decoding).
+ * result is rounded once to ydt.  Up to 255 tokens they are processed 16 at a
+ * time, the weights read once per 16 (the decoding path); from 256 tokens a
+ * tiled kernel reads each weight tile once per 128 tokens.  Both round alike.
  * Does not synchronize, allocate or clear memory, so it can be captured in a
  * graph; calls that share a workspace must not overlap.  M == 0 is a no-op.  Deterministic.
  * Supported: bits 2, 3, 4, 8; group_size 32, 64, 128, -1; n a multiple of 128

@@ -82,7 +82,10 @@ CASES = [
     (4, 128, False, 32, 4096, 16, "fp32"),   # activations beyond the LDS budget: windowed staging
     (2, 32, False, 16, 5120, 9, "fp32"),     # windowed, odd number of rounds
     (3, 64, True, 48, 3072, 12, "fp32"),
-    # prefill sizes (1024 tokens and up): 128-token x 128-output tiles
+    (4, 64, False, 48, 512, 255, "fp32"),       # the decode kernel's largest size: 16 slices
+    # prefill sizes (256 tokens and up): 128-token x 64-output tiles
+    (4, 128, False, 96, 640, 256, "fp16"),      # the smallest prefill size: two token tiles
+    (3, 32, True, 70, 768, 700, "fp32"),        # ragged token and output tiles, act-order
     (4, 128, False, 200, 1152, 1100, "fp32"),   # ragged token and output tiles, 9 chunks
     (4, 32, True, 300, 1024, 1024, "fp16"),     # act-order, four groups per chunk
     (3, 64, True, 96, 512, 1030, "fp16"),
