@@ -561,6 +561,177 @@ __global__ __launch_bounds__(NW * 64) void dequant_matmul_kernel(
   }
 }
 
+// ------------------------------------------------------------------ persistent decode
+// One slice of up to 16 tokens whose activations fit LDS whole beside two
+// tiles' scale/zero words (10-16 tokens at n = 4096), where the decode kernel
+// above would stage the activations window by window for every 16-output
+// tile (four times the tile's weight bytes at 16 tokens): one work-group of
+// 8 waves per compute unit stages the activations once and walks the output
+// tiles b, b + G, b + 2G, ... (G work-groups).  The waves split each tile's
+// chunks as in the decode kernel, and their rounds run as one sequence across
+// the tiles, so the code prefetch (kAhead chunks per wave) runs on into the
+// next tile while the current one is summed.  A tile's scale/zero words are
+// loaded when the tile two before it starts (before that tile's code loads,
+// so no wait for them ever waits for codes) and staged after that tile's
+// closing barrier, into the LDS buffer it has just finished reading.  The
+// per-chunk arithmetic is the decode kernel's, so the two round alike.
+constexpr int kPersistWaves = 8;
+constexpr size_t kPersistLds = 160 * 1024;
+constexpr int kPersistSzPieces = 2;   // 16-byte pieces of scale/zero words per thread
+
+inline size_t persist_lds_bytes(int ms, int n, int szw) {
+  return static_cast<size_t>(ms) * (n + 8) * 2 + static_cast<size_t>(2) * szw * 4 +
+         static_cast<size_t>(2) * kPersistWaves * 64 * 4 * sizeof(float);
+}
+
+template <int BITS, int SPC>
+__global__ __launch_bounds__(kPersistWaves * 64) void decode_persist_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, int ms, const uint32_t* __restrict__ Q,
+    const uint32_t* __restrict__ SZ, int rows, int n, int gs, void* __restrict__ Y, int ydt, int64_t ldy, int T) {
+  using U = Unpack<BITS>;
+  constexpr int NW = kPersistWaves, kThreads = NW * 64;
+  extern __shared__ __align__(16) unsigned char mm_smem[];
+  _Float16* abuf = reinterpret_cast<_Float16*>(mm_smem);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int C = n / kChunk;
+  const int Rp = ((C + NW - 1) / NW + kAhead - 1) / kAhead * kAhead;   // rounds per tile, whole groups of kAhead
+  const int j = lane & 15, q = lane >> 4;
+  const int arow = min(j, ms - 1);               // rows >= ms repeat the last one; their outputs are dropped
+  const int Cs = gs > 0 ? C : 1;
+  const int szw = Cs * 16 * SPC;                 // scale/zero words of a tile
+  const int szp = szw / 4;                       // ... in 16-byte pieces (<= kPersistSzPieces * kThreads)
+  const int astride = n + 8;
+  uint32_t* szs = reinterpret_cast<uint32_t*>(abuf + ms * astride);   // [2][szw]
+  float* red = reinterpret_cast<float*>(szs + 2 * szw);               // [2][NW * 64 * 4]
+  const int G = gridDim.x;
+  const int ntiles = (T - 1 - static_cast<int>(blockIdx.x)) / G + 1;  // blockIdx.x < T
+  const int nrounds = ntiles * Rp;
+  auto tile_of = [&](int k) { return static_cast<int>(blockIdx.x) + min(k, ntiles - 1) * G; };
+
+  // codes of flat round rho = k * Rp + r (tile k, chunk wave + NW r), clamped
+  // past the last round and the last chunk: loaded, never used
+  uint32_t breg[kAhead][U::kWords];
+  auto b_load = [&](int rho, int d) {
+    const int rr = min(rho, nrounds - 1);
+    const int k = rr / Rp;
+    const int c = min(wave + NW * (rr - k * Rp), C - 1);
+    load_chunk<BITS>(Q + ((static_cast<int64_t>(tile_of(k)) * C + c) * 64 + lane) * U::kWords, breg[d]);
+  };
+  u32x4 szr[kPersistSzPieces];
+  auto sz_load = [&](int k) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(SZ + static_cast<int64_t>(tile_of(k)) * szw);
+#pragma unroll
+    for (int v = 0; v < kPersistSzPieces; ++v) szr[v] = src[min(tid + v * kThreads, szp - 1)];
+  };
+  auto sz_store = [&](int buf) {
+#pragma unroll
+    for (int v = 0; v < kPersistSzPieces; ++v) {
+      const int p = tid + v * kThreads;
+      if (p < szp) reinterpret_cast<u32x4*>(szs + buf * szw)[p] = szr[v];
+    }
+  };
+
+  // The code prefetch first, so that the codes are on their way while the
+  // activations are staged (once, 16 pieces of 16 bytes per thread in flight
+  // at a time: 16 tokens at n = 4096 in one batch), then the first two
+  // tiles' scale/zero words.
+#pragma unroll
+  for (int d = 0; d < kAhead; ++d) b_load(d, d);
+  {
+    constexpr int kBatch = 16;
+    const int per_row = n / 8, total_a = ms * per_row;
+    for (int p0 = 0; p0 < total_a; p0 += kBatch * kThreads) {
+      u32x4 x[kBatch];
+#pragma unroll
+      for (int v = 0; v < kBatch; ++v) {
+        const int p = min(p0 + tid + v * kThreads, total_a - 1);
+        const int m = p / per_row, kp = p - m * per_row;
+        x[v] = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(m) * lda + 8 * kp);
+      }
+#pragma unroll
+      for (int v = 0; v < kBatch; ++v) {
+        const int p = p0 + tid + v * kThreads;
+        if (p < total_a) {
+          const int m = p / per_row, kp = p - m * per_row;
+          *reinterpret_cast<u32x4*>(abuf + m * astride + 8 * kp) = x[v];
+        }
+      }
+    }
+  }
+  sz_load(0);
+  sz_store(0);
+  sz_load(1);
+  sz_store(1);
+  lds_barrier();
+
+  f4 yacc = {0.f, 0.f, 0.f, 0.f};
+  f4 gacc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int kGroupSteps = 4 / SPC;
+  auto chunk = [&](int d, int cc, bool live, const uint32_t* szb, const _Float16* ap) {
+    const uint32_t* szc = szb + ((gs > 0 ? cc : 0) * 16 + j) * SPC;
+    h2 zc[4];
+    float s = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t % kGroupSteps == 0) {
+        const uint32_t sz = szc[t / kGroupSteps];
+        s = live ? half_bits_to_float(static_cast<uint16_t>(sz & 0xFFFFu)) : 0.f;
+        const _Float16 z = __builtin_bit_cast(_Float16, static_cast<uint16_t>(sz >> 16));
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const _Float16 c0 = -(static_cast<_Float16>(U::kBase[v]) + z);
+          zc[v] = h2{c0, c0};
+        }
+      }
+      const h8 b = U::step(breg[d], t, zc);
+      const h8 a = *reinterpret_cast<const h8*>(ap + 32 * t);
+      gacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, gacc, 0, 0, 0);
+      if (t % kGroupSteps == kGroupSteps - 1) {
+        yacc += s * gacc;
+        gacc = f4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+
+  for (int k = 0; k < ntiles; ++k) {
+    sz_load(k + 2);   // staged at the end of this tile, into the buffer this tile reads
+    const uint32_t* szb = szs + (k & 1) * szw;
+    for (int r0 = 0; r0 < Rp; r0 += kAhead) {
+#pragma unroll
+      for (int d = 0; d < kAhead; ++d) {
+        const int r = r0 + d;
+        const int c = wave + NW * r;
+        const bool live = c < C;
+        const int cc = live ? c : C - 1;
+        chunk(d, cc, live, szb, abuf + arow * astride + cc * kChunk + 8 * q);
+        b_load(k * Rp + r + kAhead, d);
+      }
+    }
+    // the 8 waves' partial tiles: summed and stored; then the scale/zero
+    // words of tile k + 2 replace this tile's
+    float* rk = red + (k & 1) * (NW * 64 * 4);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) rk[(wave * 64 + lane) * 4 + rr] = yacc[rr];
+    __syncthreads();
+    if (tid < kMTile * 16) {
+      const int mm = tid >> 4, o_in = tid & 15;
+      const int l = 16 * (mm >> 2) + o_in, rr = mm & 3;   // inverse of acc_row
+      float sum = 0.f;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) sum += rk[(v * 64 + l) * 4 + rr];
+      const int o = tile_of(k) * 16 + o_in;
+      if (mm < ms && o < rows) {
+        const int64_t idx = static_cast<int64_t>(mm) * ldy + o;
+        if (ydt == DT_FP32) static_cast<float*>(Y)[idx] = sum;
+        else static_cast<uint16_t*>(Y)[idx] = float_to_half_bits(sum);
+      }
+    }
+    sz_store(k & 1);
+    yacc = f4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
 // ------------------------------------------------------------------ prefill
 // Many tokens (M >= kPrefillMin): one workgroup of 4 waves per tile of 128
 // tokens x 64 outputs, wave (wm, wn) owning 64 x 32 as 4 x 2 MFMA tiles of
@@ -780,6 +951,43 @@ hipError_t launch_prefill(const uint16_t* A, int64_t lda, int M, const uint32_t*
   return hipGetLastError();
 }
 
+// Compute units of the current device (looked up once per device).
+inline hipError_t device_cus(int* cus) {
+  static int cached[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!cached[dev]) {
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cached[dev] = v;
+  }
+  *cus = cached[dev];
+  return hipSuccess;
+}
+
+template <int BITS, int SPC>
+hipError_t launch_persist(const uint16_t* A, int64_t lda, int M, const uint32_t* Q, const uint32_t* SZ, int rows,
+                          int n, int gs, void* Y, int ydt, int64_t ldy, size_t lds, hipStream_t s) {
+  auto kern = decode_persist_kernel<BITS, SPC>;
+  static bool attr_set = false;   // per instantiation; idempotent if raced
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kPersistLds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  int cus = 0;
+  hipError_t e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  const int T = (rows + 15) / 16;
+  const int G = T < cus ? T : cus;   // one work-group per compute unit (its LDS holds one)
+  hipLaunchKernelGGL(kern, dim3(G), dim3(kPersistWaves * 64), lds, s, A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy, T);
+  return hipGetLastError();
+}
+
 template <int BITS, int SPC, bool FULL, int NW, int PIECES = 1>
 hipError_t launch_mm_v(const uint16_t* A, int64_t lda, int M, const uint32_t* Q, const uint32_t* SZ, int rows,
                        int n, int gs, void* Y, int ydt, int64_t ldy, size_t lds, hipStream_t s) {
@@ -828,6 +1036,14 @@ hipError_t launch_mm(const uint16_t* A, int64_t lda, int M, const uint32_t* Q, c
     }
     GPTQ_MM_FULL(4)
 #undef GPTQ_MM_FULL
+  }
+  // one slice whose activations fit LDS whole beside two tiles' scale/zero
+  // words: staged once per compute unit instead of once per tile
+  if (M <= kMTile) {
+    const int szw = (gs > 0 ? n / kChunk : 1) * 16 * SPC;
+    const size_t plds = persist_lds_bytes(ms, n, szw);
+    if (plds <= kPersistLds && szw / 4 <= kPersistSzPieces * kPersistWaves * 64)
+      return launch_persist<BITS, SPC>(A, lda, M, Q, SZ, rows, n, gs, Y, ydt, ldy, plds, s);
   }
   const size_t win = static_cast<size_t>(2) * ms * kWinStride * sizeof(_Float16) + sz_bytes;
   if (win > kWinLds) return hipErrorInvalidValue;   // the entry point bounds n so this cannot happen

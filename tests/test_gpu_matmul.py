@@ -82,6 +82,14 @@ CASES = [
     (4, 128, False, 32, 4096, 16, "fp32"),   # activations beyond the LDS budget: windowed staging
     (2, 32, False, 16, 5120, 9, "fp32"),     # windowed, odd number of rounds
     (3, 64, True, 48, 3072, 12, "fp32"),
+    # one slice too large to stage per tile: the persistent kernel, several
+    # tiles per work-group (one per compute unit), ragged last tile
+    (4, 128, False, 8200, 4096, 16, "fp16"),
+    (3, 32, True, 4500, 3584, 12, "fp32"),    # four groups per chunk, act-order
+    (8, -1, False, 4200, 4096, 10, "fp32"),   # one group per row
+    # windowed staging: one slice too wide for the persistent kernel, and several slices
+    (4, 128, False, 40, 11008, 16, "fp32"),
+    (3, 64, False, 48, 4096, 40, "fp16"),
     (4, 64, False, 48, 512, 255, "fp32"),       # the decode kernel's largest size: 16 slices
     # prefill sizes (256 tokens and up): 128-token x 64-output tiles
     (4, 128, False, 96, 640, 256, "fp16"),      # the smallest prefill size: two token tiles
