@@ -40,7 +40,8 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA (published)
 PEAK_FP64_TFLOPS = 78.6      # MI355X fp64 (vector and MFMA, published)
-PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 vector (published)
+PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 vector and fp32 MFMA (published)
+PEAK_FP16_TFLOPS = 2500.0    # MI355X dense fp16 MFMA (published)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
 DTYPE = ("bf16 MFMA Hessian (fp32 chains of 256 tokens, fp64 accumulation); fp64 MFMA Cholesky + triangular "
          "inverse; fp32 column sweep with split-bf16 (3 bf16 MFMA products, fp32 accumulation) lazy-block updates")
@@ -288,30 +289,50 @@ def block_sequential_bench(args, wl, g, torch):
         Ws.append(torch.from_numpy(w_raw.view(np.int16)).view(torch.bfloat16).cuda())
     torch.cuda.synchronize()
 
-    def step():
-        outs, Hs, _ = g.calibrate_block_sequential(X0, Ws, cfg, seq_len=seq_len)
+    def step(timings=None):
+        outs, Hs, _ = g.calibrate_block_sequential(X0, Ws, cfg, seq_len=seq_len, timings=timings)
         return outs
 
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()
         _log(f"warmup step {i + 1}/{args.warmup} done")
+    # HIP events around the forward's projections (the prefill dequantizing
+    # matmul, with the act-order gather that precedes it in the same call) and
+    # the attention, on the stream they run on, over the timed steps
+    timings = []
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step()
+        step(timings)
         torch.cuda.synchronize()
         _log(f"step {i + 1}/{args.steps} done")
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    part = {}
+    for name, flop, a, b in timings:
+        ms, fl, k = part.get(name, (0.0, 0.0, 0))
+        part[name] = (ms + a.elapsed_time(b), fl + flop, k + 1)
+    mm_ms, mm_flop, mm_calls = part["matmul"]
+    at_ms, at_flop, at_calls = part["attention"]
+    mm_tf = mm_flop / (mm_ms * 1e-3) / 1e12
+    at_tf = at_flop / (at_ms * 1e-3) / 1e12
     weights = sum(lin.rows * lin.n for lin in wl.linears)
     out = {
         "metric": "GPTQ weights quantized/sec, block-sequential calibration of one decoder block",
         "value": weights / (ms_step * 1e-3), "unit": "weights/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": DTYPE + "; block forward: fp16 activations, fp32 attention, fp64 norms",
+        "vs_baseline": None, "dtype": DTYPE + "; block forward: fp16 activations, fp16 MFMA projections with fp32 sums, fp32 MFMA attention, fp64 norms",
         "data": "synthetic",
         "config": {"workload": wl.name + "-sequential", "tokens": wl.tokens, "seq_len": seq_len,
                    "linears": [(lin.name, lin.rows, lin.n) for lin in wl.linears], "bits": wl.bits,
                    "group_size": wl.group_size, "desc_act": wl.desc_act, "damp": wl.damp},
+        "stage_ms": {"forward_projections": mm_ms / args.steps, "attention": at_ms / args.steps},
+        "roofline": {"kernel": "prefill_matmul_kernel (the forward's six projections, act-order gathers included)",
+                     "bound": "mfma", "achieved": mm_tf, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": mm_tf / PEAK_FP16_TFLOPS, "traffic": None,
+                     "work": "2 * tokens * rows * n flop per projection, %d launches per step" % (mm_calls // args.steps),
+                     "attention": {"kernel": "attention_kernel (fp32 MFMA)", "achieved": at_tf,
+                                   "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": at_tf / PEAK_FP32_TFLOPS,
+                                   "work": "2 * tokens * seq_len * d flop (the causal half of QK^T and PV)"}},
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -583,7 +583,7 @@ BLOCK_STAGES = (("attn_in", (0, 1, 2)), ("o_in", (3,)), ("mlp_in", (4, 5)), ("do
 
 
 def calibrate_block_sequential(X0, weights, cfg, seq_len: int, head_dim: int = 128, eps: float = 1e-5,
-                               rope_base: float = 10000.0, keep_acts: bool = False):
+                               rope_base: float = 10000.0, keep_acts: bool = False, timings=None):
     """Block-sequential calibration of one Llama-2-shaped decoder block: each
     linear is quantized on the activations that reach it through the
     already-quantized linears before it (wikiprompt "Approche technique": the
@@ -602,6 +602,9 @@ def calibrate_block_sequential(X0, weights, cfg, seq_len: int, head_dim: int = 1
     list of seven dicts (qweight, scales, zeros, g_idx, loss), Hs the four
     stages' Hessians by stage name, acts the stages' fp16 inputs by name (only
     with keep_acts; otherwise each is freed once its consumers ran).
+    timings: a list to receive (name, flop, start, end) for each projection
+    of the forward and the attention, with start/end events recorded on the
+    current stream around the call (for measurement).
     """
     import torch
     T, d = X0.shape
@@ -609,6 +612,19 @@ def calibrate_block_sequential(X0, weights, cfg, seq_len: int, head_dim: int = 1
     f = weights[4].shape[0]
     outs, Hs, acts = [None] * 7, {}, {}
     f32, f16 = torch.float32, torch.float16
+
+    def timed(name, flop, fn):
+        if timings is None:
+            return fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        r = fn()
+        b.record()
+        timings.append((name, flop, a, b))
+        return r
+
+    def project(p, A):   # Y = A W_hat^T in fp32 through the packed layer
+        return timed("matmul", 2.0 * A.shape[0] * p.rows * p.n, lambda: p.matmul(A, out_dtype=f32))
 
     def solve(stage, X, idx):
         H, _ = hessian(X)
@@ -623,17 +639,17 @@ def calibrate_block_sequential(X0, weights, cfg, seq_len: int, head_dim: int = 1
     Xa = torch.empty((T, d), dtype=f16, device=dev)
     gptq_rmsnorm(X0, Xa, eps=eps)
     pq, pk, pv = solve("attn_in", Xa, (0, 1, 2))
-    Q, K, V = (p.matmul(Xa, out_dtype=f32) for p in (pq, pk, pv))
+    Q, K, V = (project(p, Xa) for p in (pq, pk, pv))
     del pq, pk, pv
     if keep_acts:
         acts["attn_in"] = Xa
     del Xa
     gptq_rope(Q, K, head_dim, seq_len, rope_base)
     Xo = torch.empty((T, d), dtype=f16, device=dev)
-    gptq_causal_attention(Q, K, V, head_dim, seq_len, Xo)
+    timed("attention", 2.0 * T * seq_len * d, lambda: gptq_causal_attention(Q, K, V, head_dim, seq_len, Xo))
     del Q, K, V
     (po,) = solve("o_in", Xo, (3,))
-    O = po.matmul(Xo, out_dtype=f32)
+    O = project(po, Xo)
     if keep_acts:
         acts["o_in"] = Xo
     del Xo, po
@@ -641,8 +657,8 @@ def calibrate_block_sequential(X0, weights, cfg, seq_len: int, head_dim: int = 1
     gptq_rmsnorm(X0, Xm, R=O, eps=eps)
     del O
     pg, pu = solve("mlp_in", Xm, (4, 5))
-    G = pg.matmul(Xm, out_dtype=f32)
-    Uu = pu.matmul(Xm, out_dtype=f32)
+    G = project(pg, Xm)
+    Uu = project(pu, Xm)
     if keep_acts:
         acts["mlp_in"] = Xm
     del Xm, pg, pu
