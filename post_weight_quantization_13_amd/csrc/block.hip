@@ -120,11 +120,15 @@ __global__ __launch_bounds__(256) void rope_kernel(float* __restrict__ Q, float*
 //           A = V[16t + 4g + r][16u + i] read from LDS one float at a time;
 //           lane (i, g) holds dims 16u + 4g + r of query i.
 // The dimension order of a dot product is free as long as K and Q agree: lane
-// group g takes dims 32g .. 32g+31, so a K fragment is a 16-byte LDS read.
-// K and V are staged as loaded, rows padded to 132 floats: the 16 lanes of a
-// group read 16 K rows on distinct banks, and a V read puts lane (i, g) on
-// bank 16g + i (+ a constant).  (V staged transposed, for 16-byte reads,
-// took 4-byte writes that met eight to a bank.)  fp32 products and sums; the
+// group g takes the 32 dims 32 s(g) .. 32 s(g) + 31, s = (0, 2, 1, 3), so a K
+// fragment is a 16-byte LDS read.  K and V are staged as loaded, rows padded
+// to 132 floats.  A 16-byte LDS read on this chip serves each half-wave in two
+// cycles, lanes split by the parity of lane bits 2-4, and is conflict-free
+// when each such set of 16 lanes touches 16 distinct 16-byte bank groups
+// (measured with a probe): with 132-float rows the order s meets that, the
+// plain order g conflicts 2-way.  A V read puts lane (i, g) on bank 16g + i
+// (+ a constant).  (V staged transposed, for 16-byte reads, took 4-byte
+// writes that met eight to a bank.)  fp32 products and sums; the
 // output is divided by the softmax sum and rounded to fp16 once.  Query
 // blocks are dealt longest first (the causal key range grows with them).
 constexpr int kHD = 128;
@@ -149,9 +153,10 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const float* __restri
   const int qi = q0 + 16 * wave + i16;   // this lane's query; past L it reads row L - 1, output dropped
   const float scale = 0.08838834764831845f;   // 1 / sqrt(128)
 
+  const int gs32 = 32 * (2 * (g & 1) + (g >> 1));   // this lane group's 32 dims
   float qf[32];
   {
-    const float* qp = Q + (base + min(qi, L - 1)) * d + col + 32 * g;
+    const float* qp = Q + (base + min(qi, L - 1)) * d + col + gs32;
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
       const f32x4 t = *reinterpret_cast<const f32x4*>(qp + 4 * v);
@@ -197,7 +202,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(const float* __restri
       st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const f32x4 kf = *reinterpret_cast<const f32x4*>(&sm.k[16 * t + i16][32 * g + 4 * c]);
+        const f32x4 kf = *reinterpret_cast<const f32x4*>(&sm.k[16 * t + i16][gs32 + 4 * c]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) st[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[e], qf[4 * c + e], st[t], 0, 0, 0);
       }

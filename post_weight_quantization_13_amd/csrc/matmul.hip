@@ -738,8 +738,13 @@ __global__ __launch_bounds__(kPersistWaves * 64) void decode_persist_kernel(
 // 16 x 16 (at 64 x 64 a wave needs every register, one wave per SIMD, and
 // cannot hide its own loads: 315 TFLOP/s on a 262144-token projection).  For
 // each 128-column chunk the tile's activations (128 x 128 halves) are staged
-// in LDS, double buffered, rows padded to 136 halves so a fragment read (16
-// lanes on 16 tokens, 16 bytes each) touches distinct banks; the activations
+// in LDS, double buffered, rows padded to 144 halves.  On this chip a 16-byte
+// LDS read serves each half-wave in two cycles, lanes split by the parity of
+// lane bits 2-4, and is conflict-free when each such set of 16 lanes touches
+// 16 distinct 16-byte bank groups (measured with a probe); a fragment read
+// (lane j of 16 on token j, 16 bytes at column 32t + 8q) meets that with
+// 18-unit rows, not with 17.  A 16-byte write serves 8 consecutive lanes per
+// cycle, which the staging stores (consecutive columns) always meet.  The activations
 // and codes of the two chunks after it are in flight in registers meanwhile.
 // Each wave loads its output tiles' codes straight from the
 // packed layer (a lane's bytes of a chunk are its B operand for the chunk's
@@ -752,7 +757,8 @@ __global__ __launch_bounds__(kPersistWaves * 64) void decode_persist_kernel(
 constexpr int kPM = 128;                 // tokens per tile
 constexpr int kPNT = 2;                  // 16-output tiles per wave
 constexpr int kPN = 2 * 16 * kPNT;       // outputs per tile (two waves across)
-constexpr int kPStride = kChunk + 8;     // halves per staged token row
+constexpr int kPStride = kChunk + 16;    // halves per staged token row (18 units of 16 bytes: the
+                                         // fragment reads are conflict-free, 17 units conflict 2-way)
 constexpr int kPrefillMin = 256;         // tokens from which the prefill kernel runs: from here on it
                                          // is no slower than the decode kernel's 16-token slices
                                          // (4096 x 4096 layer, 256 tokens: 52.7 against 51.4 us;
