@@ -371,15 +371,23 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
   const bool valid = r < rows;
 
   // Staging: every global load of the block is issued before the LDS stores.
+  // LDS banks on this chip: 4-byte stores see word % 32 per half-wave, 16-byte
+  // stores unit % 8 per 8 consecutive lanes.  UT[k][j] = U[i1+j][i1+k] is
+  // staged with the lanes on consecutive columns k (coalesced loads), four
+  // rows j .. j+3 per 16-byte store, which lands 8 consecutive lanes on 8
+  // distinct units (rows of 33 units); a lane per row j with 4-byte stores
+  // met 16 to a bank.  Ws[k][row] takes a row per lane and a quarter of the
+  // 32-column range per wave: a half-wave's stores hit 32 distinct banks
+  // (with four lanes per row they met 4 to a bank).
   {
-    f32x4 ut[16];  // U rows: unit i -> row j = e4 / 32, columns 4*(e4 % 32) ..
+    float ut[16][4];  // unit i: column k = e & 127, rows 4 (e >> 7) .. + 3, e = tid + 256 i
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int e4 = tid + 256 * i;
-      ut[i] = *reinterpret_cast<const f32x4*>(U + static_cast<int64_t>(i1 + (e4 >> 5)) * n + i1 + 4 * (e4 & 31));
+      const int e = tid + 256 * i, k = e & 127, j = 4 * (e >> 7);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ut[i][r] = U[static_cast<int64_t>(i1 + j + r) * n + i1 + k];
     }
-    // Ws[k][row]: thread -> (row rr, quarter q of 32 columns)
-    const int rr = tid >> 2, q = tid & 3;
+    const int rr = tid & 63, q = tid >> 6;
     const int gr = blockIdx.x * kRowsSweep + rr;
     f32x4 wv[8];
 #pragma unroll
@@ -389,12 +397,8 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
     const float dg = (tid < kBlk) ? U[static_cast<int64_t>(i1 + tid) * n + i1 + tid] : 1.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int e4 = tid + 256 * i;
-      const int j = e4 >> 5, k = 4 * (e4 & 31);
-      UT[k][j] = ut[i][0];
-      UT[k + 1][j] = ut[i][1];
-      UT[k + 2][j] = ut[i][2];
-      UT[k + 3][j] = ut[i][3];
+      const int e = tid + 256 * i, k = e & 127, j = 4 * (e >> 7);
+      *reinterpret_cast<f32x4*>(&UT[k][j]) = f32x4{ut[i][0], ut[i][1], ut[i][2], ut[i][3]};
     }
 #pragma unroll
     for (int k4 = 0; k4 < 8; ++k4) {
