@@ -1014,19 +1014,6 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
   } while (0)
   e = zero_words(info, 1, s);
   if (e != hipSuccess) return e;
-  e = zero_words(Linv, static_cast<size_t>(n) * n, s);
-  if (e != hipSuccess) return e;
-  const int nb = (n + 255) / 256;
-  hipLaunchKernelGGL(prep_diag_kernel, dim3(nb), dim3(256), 0, s, H, n, dd, dead, info);
-  GPTQ_CHECK_LAUNCH();
-  hipLaunchKernelGGL(prep_rank_kernel, dim3(nb), dim3(256), 0, s, dd, n, desc_act, perm);
-  GPTQ_CHECK_LAUNCH();
-  hipLaunchKernelGGL(prep_lambda_kernel, dim3(1), dim3(256), 0, s, dd, n, damp, lam);
-  GPTQ_CHECK_LAUNCH();
-  const unsigned gy = n < 65535 ? n : 65535;
-  hipLaunchKernelGGL(prep_gather_kernel, dim3((n + 255) / 256, gy), dim3(256), 0, s, H, perm, dd, lam, n, A);
-  GPTQ_CHECK_LAUNCH();
-
   const int nblk = (n + kB - 1) / kB;
   // Look-ahead: after a group, only the next group's block columns are
   // updated on the caller's stream (the strip); the rest of the trailing
@@ -1042,6 +1029,31 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
     if (e != hipSuccess) return e;
   }
   hipEvent_t ev_fork = ev.fork, ev_join = ev.join;
+  // Linv is cleared on the side stream beside the prologue kernels below,
+  // none of which touch it; the first panel step, its first writer, waits.
+  if (side) {
+    e = hipEventRecord(ev_fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, ev_fork, 0);
+    if (e == hipSuccess) e = zero_words(Linv, static_cast<size_t>(n) * n, side);
+    if (e == hipSuccess) e = hipEventRecord(ev_join, side);
+  } else {
+    e = zero_words(Linv, static_cast<size_t>(n) * n, s);
+  }
+  if (e != hipSuccess) return e;
+  const int nb = (n + 255) / 256;
+  hipLaunchKernelGGL(prep_diag_kernel, dim3(nb), dim3(256), 0, s, H, n, dd, dead, info);
+  GPTQ_CHECK_LAUNCH();
+  hipLaunchKernelGGL(prep_rank_kernel, dim3(nb), dim3(256), 0, s, dd, n, desc_act, perm);
+  GPTQ_CHECK_LAUNCH();
+  hipLaunchKernelGGL(prep_lambda_kernel, dim3(1), dim3(256), 0, s, dd, n, damp, lam);
+  GPTQ_CHECK_LAUNCH();
+  const unsigned gy = n < 65535 ? n : 65535;
+  hipLaunchKernelGGL(prep_gather_kernel, dim3((n + 255) / 256, gy), dim3(256), 0, s, H, perm, dd, lam, n, A);
+  GPTQ_CHECK_LAUNCH();
+  if (side) {
+    e = hipStreamWaitEvent(s, ev_join, 0);   // Linv cleared
+    if (e != hipSuccess) return e;
+  }
   // Triangular inverse by recursive doubling over levels sz = 64, 128, ...,
   // h, where h (the largest such size below n) is the top level: one pair,
   // [0, h) and [h, n).  The levels inside [0, h) and the top level's first
