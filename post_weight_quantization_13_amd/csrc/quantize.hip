@@ -60,13 +60,24 @@ __global__ void gather_w_kernel(const void* __restrict__ W, int64_t ldw, const i
     for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += gridDim.x * blockDim.x) {
       const int j0 = 4 * q;
       float v[4];
+      // Without act-order perm is the identity: the four weights and dead
+      // flags are then loaded at once instead of through perm.
+      bool ident = vec;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + e;
-        v[e] = 0.0f;
-        if (j < n) {
-          const int src = perm[j];
-          if (!dead[src]) v[e] = load_as_float<DT>(W, static_cast<int64_t>(r) * ldw + src);
+      for (int e = 0; e < 4; ++e) ident = ident && perm[j0 + e] == j0 + e;
+      if (ident) {
+        const int64_t o = static_cast<int64_t>(r) * ldw + j0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = dead[j0 + e] ? 0.0f : load_as_float<DT>(W, o + e);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = j0 + e;
+          v[e] = 0.0f;
+          if (j < n) {
+            const int src = perm[j];
+            if (!dead[src]) v[e] = load_as_float<DT>(W, static_cast<int64_t>(r) * ldw + src);
+          }
         }
       }
       float* dst = Wk + static_cast<int64_t>(r) * n + j0;
@@ -759,9 +770,24 @@ __global__ void pack_kernel(const uint8_t* __restrict__ codes, const int32_t* __
   uint32_t words[BITS];
 #pragma unroll
   for (int t = 0; t < BITS; ++t) words[t] = 0u;
+  // Without act-order the 32 codes are consecutive in the row: two 16-byte
+  // loads instead of 32 byte loads (the check is uniform: c is the block's).
+  bool ident = (n % 16) == 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) ident = ident && invperm[c * 32 + i] == c * 32 + i;
+  uint8_t cv[32];
+  if (ident) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(crow + c * 32);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(crow + c * 32 + 16);
+    __builtin_memcpy(cv, &a, 16);
+    __builtin_memcpy(cv + 16, &b, 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) cv[i] = crow[invperm[c * 32 + i]];
+  }
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const uint32_t v = crow[invperm[c * 32 + i]];
+    const uint32_t v = cv[i];
     const int bit = BITS * i;
     const int wi = bit >> 5, off = bit & 31;
     words[wi] |= v << off;
