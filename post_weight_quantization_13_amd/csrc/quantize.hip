@@ -53,22 +53,38 @@ __device__ __forceinline__ int es_swz(int t) { return (t & 1) << 5; }
 // and Wk is 16-byte aligned (every row start then is), else one by one.
 template <int DT>
 __global__ void gather_w_kernel(const void* __restrict__ W, int64_t ldw, const int32_t* __restrict__ perm,
-                                const uint8_t* __restrict__ dead, int rows, int n, float* __restrict__ Wk) {
+                                const uint8_t* __restrict__ dead, int rows, int n, float* __restrict__ Wk,
+                                bool aligned) {
   const int nq = (n + 3) / 4;
   const bool vec = (n % 4) == 0 && (reinterpret_cast<uintptr_t>(Wk) & 15) == 0;
   for (int r = blockIdx.y; r < rows; r += gridDim.y) {
     for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += gridDim.x * blockDim.x) {
       const int j0 = 4 * q;
       float v[4];
-      // Without act-order perm is the identity: the four weights and dead
-      // flags are then loaded at once instead of through perm.
-      bool ident = vec;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ident = ident && perm[j0 + e] == j0 + e;
+      // Without act-order perm is the identity: with W, perm and dead aligned
+      // (checked by the caller) the four weights, their indexes and their
+      // dead flags then come in one load each instead of through perm.
+      bool ident = false;
+      if (aligned && vec) {
+        const int4 pj = *reinterpret_cast<const int4*>(perm + j0);
+        ident = pj.x == j0 && pj.y == j0 + 1 && pj.z == j0 + 2 && pj.w == j0 + 3;
+      }
       if (ident) {
         const int64_t o = static_cast<int64_t>(r) * ldw + j0;
+        const uint32_t dflags = *reinterpret_cast<const uint32_t*>(dead + j0);
+        float w[4];
+        if constexpr (DT == DT_FP32) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(static_cast<const float*>(W) + o);
+          w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
+        } else {
+          const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(W) + o);
+          const uint16_t h[4] = {static_cast<uint16_t>(x.x), static_cast<uint16_t>(x.x >> 16),
+                                 static_cast<uint16_t>(x.y), static_cast<uint16_t>(x.y >> 16)};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = dead[j0 + e] ? 0.0f : load_as_float<DT>(W, o + e);
+          for (int e = 0; e < 4; ++e) w[e] = (DT == DT_BF16) ? bf16_bits_to_float(h[e]) : half_bits_to_float(h[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = ((dflags >> (8 * e)) & 0xFFu) ? 0.0f : w[e];
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -894,9 +910,16 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
   e = zero_words(rowloss, static_cast<size_t>(rows), s);
   if (e != hipSuccess) return e;
   dim3 gg(((n + 3) / 4 + 255) / 256, rows < 65535 ? rows : 65535);
-  if (wdt == DT_BF16) hipLaunchKernelGGL(gather_w_kernel<DT_BF16>, gg, dim3(256), 0, s, W, ldw, perm, dead, rows, n, Wk);
-  else if (wdt == DT_FP16) hipLaunchKernelGGL(gather_w_kernel<DT_FP16>, gg, dim3(256), 0, s, W, ldw, perm, dead, rows, n, Wk);
-  else hipLaunchKernelGGL(gather_w_kernel<DT_FP32>, gg, dim3(256), 0, s, W, ldw, perm, dead, rows, n, Wk);
+  // one vector load per four weights needs W rows, perm and dead aligned to them
+  const size_t wsz = (wdt == DT_FP32) ? 4 : 2;
+  const bool waligned = (reinterpret_cast<uintptr_t>(W) % (4 * wsz)) == 0 && (ldw % 4) == 0 &&
+                        (reinterpret_cast<uintptr_t>(perm) % 16) == 0 && (reinterpret_cast<uintptr_t>(dead) % 4) == 0;
+  if (wdt == DT_BF16)
+    hipLaunchKernelGGL(gather_w_kernel<DT_BF16>, gg, dim3(256), 0, s, W, ldw, perm, dead, rows, n, Wk, waligned);
+  else if (wdt == DT_FP16)
+    hipLaunchKernelGGL(gather_w_kernel<DT_FP16>, gg, dim3(256), 0, s, W, ldw, perm, dead, rows, n, Wk, waligned);
+  else
+    hipLaunchKernelGGL(gather_w_kernel<DT_FP32>, gg, dim3(256), 0, s, W, ldw, perm, dead, rows, n, Wk, waligned);
   GPTQ_CHECK_LAUNCH();
   hipLaunchKernelGGL(gidx_kernel, dim3((n + 255) / 256), dim3(256), 0, s, perm, n, gs > 0 ? gs : n, g_idx, invperm);
   GPTQ_CHECK_LAUNCH();
