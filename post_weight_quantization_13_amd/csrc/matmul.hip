@@ -354,6 +354,30 @@ __device__ __forceinline__ void load_chunk(const uint32_t* __restrict__ p, uint3
   }
 }
 
+// The same through a buffer resource: lane offset voff, uniform offset soff
+// (bytes).  Word 3 of a raw buffer resource: 32-bit data format.
+constexpr int kBufWord3 = 0x00020000;
+template <int BITS>
+__device__ __forceinline__ void load_chunk_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint32_t* w) {
+  if constexpr (BITS == 4) {
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+  } else if constexpr (BITS == 8) {
+    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, 0));
+    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
+    w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
+  } else if constexpr (BITS == 2) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    w[0] = v[0]; w[1] = v[1];
+  } else {
+    typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+    const u32x3 v = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0));
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
+  }
+}
+
 // Accumulator layout of the 16x16 f32 MFMA tiles: lane l, register r holds
 // row 4*(l/16) + r (token), column l%16 (output).
 __device__ __forceinline__ int acc_row(int lane, int r) { return 4 * (lane >> 4) + r; }
@@ -788,24 +812,39 @@ __global__ __launch_bounds__(256, 2) void prefill_matmul_kernel(const uint16_t* 
   const int j = lane & 15, q = lane >> 4;
   const int Tcount = (rows + 15) / 16;
   // this wave's packed output tiles (clamped past the last: loaded, dropped)
-  const uint32_t* qb[kPNT];
-  const uint32_t* szb[kPNT];
+  // Every load is a buffer load: a resource over the region the loop reads
+  // (uniform across the wave), a lane offset fixed for the whole loop and a
+  // scalar offset per chunk, so the loads need no per-chunk vector address
+  // arithmetic.  Every offset stays inside its resource's range (tokens past
+  // M are clamped to M - 1, output tiles past the last to the last).
+  __amdgpu_buffer_rsrc_t qr[kPNT], szr_rs[kPNT];   // this wave's output tiles' codes, scale/zero words
 #pragma unroll
   for (int nt = 0; nt < kPNT; ++nt) {
     const int T = min(o0 / 16 + kPNT * wn + nt, Tcount - 1);
-    qb[nt] = Q + (static_cast<int64_t>(T) * C * 64 + lane) * U::kWords;
-    szb[nt] = SZ + static_cast<int64_t>(T) * Cs * 16 * SPC + j * SPC;
+    qr[nt] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(Q + static_cast<int64_t>(T) * C * 64 * U::kWords),
+                                               0, C * 64 * U::kWords * 4, kBufWord3);
+    szr_rs[nt] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(SZ + static_cast<int64_t>(T) * Cs * 16 * SPC),
+                                                   0, Cs * 16 * SPC * 4, kBufWord3);
   }
+  const int qoff = lane * U::kWords * 4;   // bytes
+  const int szoff = j * SPC * 4;
   // activations: piece p = tid + 256 v is token p / 16, halves 8 (p % 16) ..
   // of the chunk; tokens past M read token M - 1 (their outputs are dropped)
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A + static_cast<int64_t>(m0) * lda), 0,
+      static_cast<int>((static_cast<int64_t>(min(M - m0, kPM) - 1) * lda + n) * 2), kBufWord3);
+  int aoff[8];   // bytes from the tile's first token
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int p = tid + 256 * v;
+    const int tm = min(m0 + (p >> 4), M - 1);
+    aoff[v] = ((tm - m0) * lda + 8 * (p & 15)) * 2;
+  }
   u32x4 areg[DEPTH][8];  // DEPTH register sets of activations on their way to LDS
   auto a_load = [&](int c, int set) {
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int p = tid + 256 * v;
-      const int tm = min(m0 + (p >> 4), M - 1);
-      areg[set][v] = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(tm) * lda + c * kChunk + 8 * (p & 15));
-    }
+    for (int v = 0; v < 8; ++v)
+      areg[set][v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[v], c * kChunk * 2, 0));
   };
   auto a_store = [&](int buf, int set) {
 #pragma unroll
@@ -820,9 +859,10 @@ __global__ __launch_bounds__(256, 2) void prefill_matmul_kernel(const uint16_t* 
   auto b_load = [&](int c, int d) {
 #pragma unroll
     for (int nt = 0; nt < kPNT; ++nt) {
-      load_chunk<BITS>(qb[nt] + static_cast<int64_t>(c) * 64 * U::kWords, breg[d][nt]);
+      load_chunk_buf<BITS>(qr[nt], qoff, c * 64 * U::kWords * 4, breg[d][nt]);
 #pragma unroll
-      for (int g = 0; g < SPC; ++g) szr[d][nt][g] = szb[nt][(gs > 0 ? c : 0) * 16 * SPC + g];
+      for (int g = 0; g < SPC; ++g)
+        szr[d][nt][g] = __builtin_amdgcn_raw_buffer_load_b32(szr_rs[nt], szoff + 4 * g, (gs > 0 ? c : 0) * 16 * SPC * 4, 0);
     }
   };
   f4 yacc[4][kPNT], gacc[4][kPNT];
