@@ -180,6 +180,19 @@ def _xset_on_device(wl, xset, torch):
     return X
 
 
+def _check_steps(info, loss=None):
+    """Every step's prepare found a positive definite Hessian, and every
+    step's loss (deterministic inputs, deterministic kernels) is the same
+    finite number."""
+    flags = info.cpu().tolist()
+    if any(f != 0 for f in flags):
+        raise RuntimeError(f"prepare reported a Hessian that is not positive definite: flags {flags}")
+    if loss is not None:
+        vals = loss.cpu().tolist()
+        if not all(v == vals[0] for v in vals) or not (vals[0] >= 0.0 and vals[0] < float("inf")):
+            raise RuntimeError(f"step losses differ or are not finite: {vals}")
+
+
 def block_bench(args, wl, g, torch):
     """One step = the whole block: a Hessian from scratch and a prepare per
     activation set, then a quantize per linear (the sets' factors shared)."""
@@ -209,33 +222,44 @@ def block_bench(args, wl, g, torch):
     ws_q = [g.workspace(g.gptq_quantize_workspace_bytes(lin.rows, lin.n, cfg), dev) for lin in wl.linears]
     torch.cuda.synchronize()
 
-    def step():
+    # stream-ordered prepare and quantize (no host round trip inside a step);
+    # the flags and losses are checked after the timed steps
+    nsets, nlin = len(Xs), len(wl.linears)
+    info = torch.full(((args.warmup + args.steps) * nsets,), -1, dtype=torch.int32, device=dev)
+    loss = torch.full(((args.warmup + args.steps), nlin), -1.0, dtype=torch.float64, device=dev)
+
+    def step(i):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         ev[0].record()
-        for s in range(len(Xs)):
+        for s in range(nsets):
             g.gptq_hessian_accumulate(Hs[s], 0, Xs[s], ws_h[s])
         ev[1].record()
-        for s in range(len(Xs)):
-            g.gptq_prepare_hinv(Hs[s], cfg, Us[s], perms[s], deads[s], ws_p[s])
+        for s in range(nsets):
+            g.gptq_prepare_hinv_async(Hs[s], cfg, Us[s], perms[s], deads[s], info[i * nsets + s:i * nsets + s + 1],
+                                      ws_p[s])
         ev[2].record()
         for li, lin in enumerate(wl.linears):
             s = lin.xset
             qw, sc, ze, gi = outs[li]
-            g.gptq_quantize_layer(Us[s], perms[s], deads[s], cfg, Ws[li], qw, sc, ze, gi, ws_q[li],
-                                  want_loss=False)
+            g.gptq_quantize_layer_async(Us[s], perms[s], deads[s], cfg, Ws[li], qw, sc, ze, gi,
+                                        loss[i, li:li + 1], ws_q[li])
         ev[3].record()
         return ev
 
     for i in range(args.warmup):
-        step()
+        step(i)
+        torch.cuda.synchronize()
         _log(f"warmup step {i + 1}/{args.warmup} done")
     torch.cuda.synchronize()
     events = []
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        events.append(step())
+    for i in range(args.steps):
+        events.append(step(args.warmup + i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    _check_steps(info)
+    for li in range(nlin):
+        _check_steps(info[:1], loss[:, li])
     ms_step = (t1 - t0) * 1e3 / args.steps
     st = {k: sum(e[a].elapsed_time(e[b]) for e in events) / args.steps
           for k, a, b in (("hessian", 0, 1), ("prepare", 1, 2), ("quantize", 2, 3))}
@@ -590,28 +614,36 @@ def main() -> int:
         _log("pmc probe done: 1 GiB copy + 3 Hessian launches")
         return 0
 
-    def step():
+    # The stream-ordered entry points queue every step's work without a host
+    # round trip; each step's positive-definiteness flag and loss land in
+    # device memory and are checked once the timed steps are done.
+    info = torch.full((args.warmup + args.steps,), -1, dtype=torch.int32, device=dev)
+    loss = torch.full((args.warmup + args.steps,), -1.0, dtype=torch.float64, device=dev)
+
+    def step(i):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         ev[0].record()
         g.gptq_hessian_accumulate(H, 0, X, ws_h)
         ev[1].record()
-        g.gptq_prepare_hinv(H, cfg, U, perm, dead, ws_p)
+        g.gptq_prepare_hinv_async(H, cfg, U, perm, dead, info[i:i + 1], ws_p)
         ev[2].record()
-        loss = g.gptq_quantize_layer(U, perm, dead, cfg, W, qweight, scales, zeros, g_idx, ws_q)
+        g.gptq_quantize_layer_async(U, perm, dead, cfg, W, qweight, scales, zeros, g_idx, loss[i:i + 1], ws_q)
         ev[3].record()
-        return ev, loss
+        return ev
 
     for i in range(args.warmup):
-        step()
+        step(i)
+        torch.cuda.synchronize()
         _log(f"warmup step {i + 1}/{args.warmup} done")
     torch.cuda.synchronize()
     events = []
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        events.append(step()[0])
+    for i in range(args.steps):
+        events.append(step(args.warmup + i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     _log(f"timed {args.steps} steps")
+    _check_steps(info, loss)
     ms_step = (t1 - t0) * 1e3 / args.steps
     st = {k: sum(e[a].elapsed_time(e[b]) for e in events) / args.steps
           for k, a, b in (("hessian", 0, 1), ("prepare", 1, 2), ("quantize", 2, 3))}

@@ -167,6 +167,37 @@ gptq_status gptq_quantize_layer(const float* U, const int32_t* perm, const uint8
                                 void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
+ * Stream-ordered forms of prepare and quantize ("Étape 2", "Étape 1/2/3": the
+ * same computation).  A model is quantized layer after layer; these forms let
+ * a caller queue the Hessian, prepare and quantize calls of many layers
+ * without a host round trip between them, and read every status afterwards.
+ *
+ * gptq_prepare_hinv_async: as gptq_prepare_hinv (same arguments, checks,
+ * workspace and outputs, bit-identical U, perm and dead), except that the
+ * positive-definiteness result is written in stream order to
+ *   info  device int32 [1]: 0 if the damped Hessian is positive definite,
+ *         1 if not (U then undefined),
+ * and the call does not synchronize `stream`.  A nonzero status is returned
+ * only for argument errors and failed launches.
+ *
+ * gptq_quantize_layer_async: as gptq_quantize_layer (same arguments, checks,
+ * workspace and outputs, bit-identical codes, scales, zeros, g_idx), except
+ * that the loss goes to
+ *   loss  device double [1], may be NULL: the same sum as loss_out, written
+ *         in stream order (rows == 0 writes 0),
+ * and the call never synchronizes `stream`.
+ * ------------------------------------------------------------------------- */
+gptq_status gptq_prepare_hinv_async(const double* H, int64_t n, const gptq_config* cfg,
+                                    float* U, int32_t* perm, uint8_t* dead, int32_t* info,
+                                    void* workspace, size_t ws_bytes, void* stream);
+gptq_status gptq_quantize_layer_async(const float* U, const int32_t* perm, const uint8_t* dead,
+                                      int64_t n, const gptq_config* cfg,
+                                      const void* W, gptq_dtype wdt, int64_t rows, int64_t ldw,
+                                      int32_t* qweight, uint16_t* scales, uint16_t* zeros,
+                                      int32_t* g_idx, double* loss,
+                                      void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
  * Relative layer loss ("Comment fonctionne l'algorithme GPTQ": the objective is
  * the squared output error).  Dequantizes the packed outputs and returns
  *   *rel_loss (HOST) = tr(D H D^T) / tr(W H W^T),  D = W - W_hat,

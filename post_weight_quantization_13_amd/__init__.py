@@ -43,6 +43,7 @@ EXPORTS = (
     "gptq_hessian_workspace_bytes", "gptq_hessian_chain_tokens", "gptq_hessian_accumulate",
     "gptq_prepare_workspace_bytes", "gptq_prepare_hinv",
     "gptq_quantize_workspace_bytes", "gptq_quantize_layer",
+    "gptq_prepare_hinv_async", "gptq_quantize_layer_async",
     "gptq_layer_loss_workspace_bytes", "gptq_layer_loss",
     "gptq_matmul_packed_bytes", "gptq_matmul_pack", "gptq_matmul_workspace_bytes", "gptq_matmul",
     "gptq_matmul_static_scratch_bytes", "gptq_matmul_static",
@@ -107,6 +108,11 @@ def lib() -> ctypes.CDLL:
     L.gptq_quantize_layer.argtypes = [vp, vp, vp, i64, cfgp, vp, ctypes.c_int, i64, i64, vp, vp, vp, vp,
                                       ctypes.POINTER(ctypes.c_double), vp, sz, vp]
     L.gptq_quantize_layer.restype = ctypes.c_int
+    L.gptq_prepare_hinv_async.argtypes = [vp, i64, cfgp, vp, vp, vp, vp, vp, sz, vp]
+    L.gptq_prepare_hinv_async.restype = ctypes.c_int
+    L.gptq_quantize_layer_async.argtypes = [vp, vp, vp, i64, cfgp, vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, vp,
+                                            vp, sz, vp]
+    L.gptq_quantize_layer_async.restype = ctypes.c_int
     L.gptq_layer_loss_workspace_bytes.argtypes = [i64, i64]
     L.gptq_layer_loss_workspace_bytes.restype = sz
     L.gptq_layer_loss.argtypes = [vp, i64, vp, ctypes.c_int, i64, i64, vp, vp, vp, vp, cfgp,
@@ -294,6 +300,46 @@ def gptq_quantize_layer(U, perm, dead, cfg, W, qweight, scales, zeros, g_idx, wo
                                      ctypes.byref(loss) if want_loss else None, _ptr(workspace),
                                      ws_bytes, _stream(stream, dev)))
     return loss.value if want_loss else None
+
+
+def gptq_prepare_hinv_async(H, cfg, U, perm, dead, info, workspace, stream=None) -> None:
+    """gptq_prepare_hinv without a host round trip: info (int32 [1] on H's
+    device) receives 0 (positive definite) or 1 (not) in stream order."""
+    import torch
+    n = H.shape[0] if H.dim() == 2 else -1
+    dev = H.device
+    _need(H, "H", torch.float64, (n, n), dev)
+    _need(U, "U", torch.float32, (n, n), dev)
+    _need(perm, "perm", torch.int32, (n,), dev)
+    _need(dead, "dead", torch.uint8, (n,), dev)
+    _need(info, "info", torch.int32, (1,), dev)
+    ws_bytes = _need_workspace(workspace, dev)
+    _check(lib().gptq_prepare_hinv_async(_ptr(H), n, _cfg(cfg), _ptr(U), _ptr(perm), _ptr(dead), _ptr(info),
+                                         _ptr(workspace), ws_bytes, _stream(stream, dev)))
+
+
+def gptq_quantize_layer_async(U, perm, dead, cfg, W, qweight, scales, zeros, g_idx, loss, workspace,
+                              stream=None) -> None:
+    """gptq_quantize_layer without a host round trip: the loss goes to loss
+    (float64 [1] on W's device, or None) in stream order."""
+    import torch
+    if W.dim() != 2:
+        raise ValueError("W must be a 2-D tensor")
+    rows, n = W.shape
+    c = _config(cfg)
+    dev = W.device
+    _need(U, "U", torch.float32, (n, n), dev)
+    _need(perm, "perm", torch.int32, (n,), dev)
+    _need(dead, "dead", torch.uint8, (n,), dev)
+    _need_outputs(qweight, scales, zeros, g_idx, rows, n, c, dev)
+    if loss is not None:
+        _need(loss, "loss", torch.float64, (1,), dev)
+    ldw = _row_major_2d(W, "W")
+    ws_bytes = _need_workspace(workspace, dev)
+    _check(lib().gptq_quantize_layer_async(_ptr(U), _ptr(perm), _ptr(dead), n, _cfg(c), _ptr(W), _dtype_code(W),
+                                           rows, ldw, _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(g_idx),
+                                           _ptr(loss) if loss is not None else None, _ptr(workspace), ws_bytes,
+                                           _stream(stream, dev)))
 
 
 def _need_outputs(qweight, scales, zeros, g_idx, rows, n, c: Config, dev) -> None:

@@ -17,12 +17,13 @@ size_t hessian_workspace(int64_t n, int64_t tokens, int dt);
 int64_t hessian_chain_tokens();
 size_t prepare_workspace(int64_t n);
 hipError_t launch_prepare(const double* H, int64_t n, double damp, int desc_act, float* U, int32_t* perm,
-                          uint8_t* dead, void* ws, hipStream_t s, int* info_host);
+                          uint8_t* dead, void* ws, hipStream_t s, int* info_host, int32_t* info_dev);
 size_t quantize_workspace(int64_t rows, int64_t n);
 hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* dead, int64_t n, int bits, int sym,
                            int group_size, const void* W, int wdt, int64_t rows, int64_t ldw, int32_t* qweight,
-                           uint16_t* scales, uint16_t* zeros, int32_t* g_idx, double* loss_host, void* ws,
-                           hipStream_t s);
+                           uint16_t* scales, uint16_t* zeros, int32_t* g_idx, double* loss_host,
+                           double* loss_dev, void* ws, hipStream_t s);
+hipError_t zero_loss(double* loss, hipStream_t s);
 size_t loss_workspace(int64_t rows, int64_t n);
 hipError_t launch_layer_loss(const double* H, int64_t n, const void* W, int wdt, int64_t rows, int64_t ldw,
                              const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
@@ -178,8 +179,8 @@ size_t gptq_prepare_workspace_bytes(int64_t n, const gptq_config* cfg) {
   return gptq::prepare_workspace(n);
 }
 
-gptq_status gptq_prepare_hinv(const double* H, int64_t n, const gptq_config* cfg, float* U, int32_t* perm,
-                              uint8_t* dead, void* workspace, size_t ws_bytes, void* stream) {
+static gptq_status check_prepare(const double* H, int64_t n, const gptq_config* cfg, const float* U,
+                                 const int32_t* perm, const uint8_t* dead, const void* workspace, size_t ws_bytes) {
   gptq_status st = check_config(cfg, false);
   if (st != GPTQ_OK) return st;
   if (!H || !U || !perm || !dead) return fail(GPTQ_ERR_INVALID_ARG, "NULL H, U, perm or dead");
@@ -187,11 +188,29 @@ gptq_status gptq_prepare_hinv(const double* H, int64_t n, const gptq_config* cfg
   const size_t need = gptq::prepare_workspace(n);
   if (!workspace || ws_bytes < need)
     return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace ? ws_bytes : 0, need);
+  return GPTQ_OK;
+}
+
+gptq_status gptq_prepare_hinv(const double* H, int64_t n, const gptq_config* cfg, float* U, int32_t* perm,
+                              uint8_t* dead, void* workspace, size_t ws_bytes, void* stream) {
+  gptq_status st = check_prepare(H, n, cfg, U, perm, dead, workspace, ws_bytes);
+  if (st != GPTQ_OK) return st;
   int info = 0;
   hipError_t e = gptq::launch_prepare(H, n, static_cast<double>(cfg->damp_percent), cfg->desc_act, U, perm, dead,
-                                      workspace, static_cast<hipStream_t>(stream), &info);
+                                      workspace, static_cast<hipStream_t>(stream), &info, nullptr);
   if (e != hipSuccess) return hip_fail("gptq_prepare_hinv", e);
   if (info != 0) return fail(GPTQ_ERR_NOT_PD, "damped Hessian is not positive definite");
+  return ok();
+}
+
+gptq_status gptq_prepare_hinv_async(const double* H, int64_t n, const gptq_config* cfg, float* U, int32_t* perm,
+                                    uint8_t* dead, int32_t* info, void* workspace, size_t ws_bytes, void* stream) {
+  gptq_status st = check_prepare(H, n, cfg, U, perm, dead, workspace, ws_bytes);
+  if (st != GPTQ_OK) return st;
+  if (!info) return fail(GPTQ_ERR_INVALID_ARG, "NULL info");
+  hipError_t e = gptq::launch_prepare(H, n, static_cast<double>(cfg->damp_percent), cfg->desc_act, U, perm, dead,
+                                      workspace, static_cast<hipStream_t>(stream), nullptr, info);
+  if (e != hipSuccess) return hip_fail("gptq_prepare_hinv_async", e);
   return ok();
 }
 
@@ -202,10 +221,12 @@ size_t gptq_quantize_workspace_bytes(int64_t rows, int64_t n, const gptq_config*
   return gptq::quantize_workspace(rows, n);
 }
 
-gptq_status gptq_quantize_layer(const float* U, const int32_t* perm, const uint8_t* dead, int64_t n,
-                                const gptq_config* cfg, const void* W, gptq_dtype wdt, int64_t rows, int64_t ldw,
-                                int32_t* qweight, uint16_t* scales, uint16_t* zeros, int32_t* g_idx,
-                                double* loss_out, void* workspace, size_t ws_bytes, void* stream) {
+// Shared by both forms: loss_host (sync form) or loss_dev (stream-ordered form).
+static gptq_status quantize_layer(const char* who, const float* U, const int32_t* perm, const uint8_t* dead,
+                                  int64_t n, const gptq_config* cfg, const void* W, gptq_dtype wdt, int64_t rows,
+                                  int64_t ldw, int32_t* qweight, uint16_t* scales, uint16_t* zeros, int32_t* g_idx,
+                                  double* loss_out, double* loss_dev, void* workspace, size_t ws_bytes,
+                                  void* stream) {
   gptq_status st = check_config(cfg, true);
   if (st != GPTQ_OK) return st;
   if (n < 1 || n > kMaxDim) return fail(GPTQ_ERR_INVALID_ARG, "n=%lld out of range", (long long)n);
@@ -215,6 +236,10 @@ gptq_status gptq_quantize_layer(const float* U, const int32_t* perm, const uint8
   if (!valid_dtype(wdt)) return fail(GPTQ_ERR_INVALID_ARG, "unknown dtype %d", (int)wdt);
   if (rows == 0) {
     if (loss_out) *loss_out = 0.0;
+    if (loss_dev) {
+      hipError_t e = gptq::zero_loss(loss_dev, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_fail(who, e);
+    }
     return ok();
   }
   if (!U || !perm || !dead || !W || !qweight || !scales || !zeros || !g_idx)
@@ -225,9 +250,26 @@ gptq_status gptq_quantize_layer(const float* U, const int32_t* perm, const uint8
     return fail(GPTQ_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace ? ws_bytes : 0, need);
   hipError_t e = gptq::launch_quantize(U, perm, dead, n, cfg->bits, cfg->sym, cfg->group_size, W,
                                        static_cast<int>(wdt), rows, ldw, qweight, scales, zeros, g_idx, loss_out,
-                                       workspace, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail("gptq_quantize_layer", e);
+                                       loss_dev, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(who, e);
   return ok();
+}
+
+gptq_status gptq_quantize_layer(const float* U, const int32_t* perm, const uint8_t* dead, int64_t n,
+                                const gptq_config* cfg, const void* W, gptq_dtype wdt, int64_t rows, int64_t ldw,
+                                int32_t* qweight, uint16_t* scales, uint16_t* zeros, int32_t* g_idx,
+                                double* loss_out, void* workspace, size_t ws_bytes, void* stream) {
+  return quantize_layer("gptq_quantize_layer", U, perm, dead, n, cfg, W, wdt, rows, ldw, qweight, scales, zeros,
+                        g_idx, loss_out, nullptr, workspace, ws_bytes, stream);
+}
+
+gptq_status gptq_quantize_layer_async(const float* U, const int32_t* perm, const uint8_t* dead, int64_t n,
+                                      const gptq_config* cfg, const void* W, gptq_dtype wdt, int64_t rows,
+                                      int64_t ldw, int32_t* qweight, uint16_t* scales, uint16_t* zeros,
+                                      int32_t* g_idx, double* loss, void* workspace, size_t ws_bytes,
+                                      void* stream) {
+  return quantize_layer("gptq_quantize_layer_async", U, perm, dead, n, cfg, W, wdt, rows, ldw, qweight, scales,
+                        zeros, g_idx, nullptr, loss, workspace, ws_bytes, stream);
 }
 
 // ----------------------------------------------------------------------------- loss

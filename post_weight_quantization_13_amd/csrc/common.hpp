@@ -76,6 +76,14 @@ static inline hipError_t zero_words(void* p, size_t words, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Zero one int32 (a status flag that may sit in a caller's 4-byte buffer).
+static __global__ void zero_i32_kernel(int32_t* __restrict__ p) { p[0] = 0; }
+
+static inline hipError_t zero_i32(int32_t* p, hipStream_t s) {
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, s, p);
+  return hipGetLastError();
+}
+
 // Extra streams per device (which = 0, 1) for work that overlaps the
 // caller's stream, created on first use and kept until the process ends.
 // Calls may share them; each call orders its own work with its own events.

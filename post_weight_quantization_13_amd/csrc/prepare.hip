@@ -991,8 +991,11 @@ size_t prepare_workspace(int64_t n) {
   return al(static_cast<size_t>(n) * n * 8) * 2 + al(static_cast<size_t>(n) * 8) + 256 + 256;
 }
 
+// info_dev == nullptr: the flag lives in the workspace and is read back into
+// *info_host (one synchronization); else it is written to info_dev in stream
+// order and the call does not synchronize.
 hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_act, float* U, int32_t* perm,
-                          uint8_t* dead, void* ws, hipStream_t s, int* info_host) {
+                          uint8_t* dead, void* ws, hipStream_t s, int* info_host, int32_t* info_dev) {
   const int n = static_cast<int>(n64);
   auto al = [](size_t b) { return (b + 255) & ~static_cast<size_t>(255); };
   uint8_t* p = static_cast<uint8_t*>(ws);
@@ -1004,7 +1007,7 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
   p += al(static_cast<size_t>(n) * 8);
   double* lam = reinterpret_cast<double*>(p);
   p += 256;
-  int* info = reinterpret_cast<int*>(p);
+  int* info = info_dev ? info_dev : reinterpret_cast<int*>(p);
 
   hipError_t e;
 #define GPTQ_CHECK_LAUNCH()          \
@@ -1012,7 +1015,7 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
     e = hipGetLastError();           \
     if (e != hipSuccess) return e;   \
   } while (0)
-  e = zero_words(info, 1, s);
+  e = zero_i32(info, s);
   if (e != hipSuccess) return e;
   const int nblk = (n + kB - 1) / kB;
   // Look-ahead: after a group, only the next group's block columns are
@@ -1187,6 +1190,7 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
   hipLaunchKernelGGL(write_u_kernel, dim3((n + 255) / 256, gy), dim3(256), 0, s, Linv, n, U);
   GPTQ_CHECK_LAUNCH();
 #undef GPTQ_CHECK_LAUNCH
+  if (info_dev) return hipSuccess;
   e = hipMemcpyAsync(info_host, info, sizeof(int), hipMemcpyDeviceToHost, s);
   if (e != hipSuccess) return e;
   return hipStreamSynchronize(s);

@@ -872,10 +872,12 @@ static void launch_row_params(hipStream_t s, const float* Wk, int n, int rows, f
     else GPTQ_BY_SYM(M, 8);                 \
   } while (0)
 
+hipError_t zero_loss(double* loss, hipStream_t s) { return zero_words(loss, 1, s); }
+
 hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* dead, int64_t n64, int bits,
                            int sym, int group_size, const void* W, int wdt, int64_t rows64, int64_t ldw,
                            int32_t* qweight, uint16_t* scales, uint16_t* zeros, int32_t* g_idx, double* loss_host,
-                           void* ws, hipStream_t s) {
+                           double* loss_out_dev, void* ws, hipStream_t s) {
   const int n = static_cast<int>(n64), rows = static_cast<int>(rows64);
   uint8_t* p = static_cast<uint8_t*>(ws);
   float* Wk = reinterpret_cast<float*>(p);
@@ -1031,7 +1033,10 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
   else if (bits == 4) hipLaunchKernelGGL(pack_kernel<4>, gp, dim3(256), 0, s, codes, invperm, n, rows, qweight);
   else hipLaunchKernelGGL(pack_kernel<8>, gp, dim3(256), 0, s, codes, invperm, n, rows, qweight);
   GPTQ_CHECK_LAUNCH();
-  if (loss_host) {
+  if (loss_out_dev) {  // stream order, no synchronization
+    hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, s, rowloss, rows, loss_out_dev);
+    GPTQ_CHECK_LAUNCH();
+  } else if (loss_host) {
     hipLaunchKernelGGL(loss_reduce_kernel, dim3(1), dim3(256), 0, s, rowloss, rows, loss_dev);
     GPTQ_CHECK_LAUNCH();
     e = hipMemcpyAsync(loss_host, loss_dev, sizeof(double), hipMemcpyDeviceToHost, s);

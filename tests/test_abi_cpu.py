@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(g):
     names = _declared()
-    assert len(names) == 21, names
+    assert len(names) == 23, names
     assert set(names) == set(g.EXPORTS)
     L = g.lib()
     for n in names:
@@ -100,6 +100,21 @@ def test_argument_validation(g):
     assert L.gptq_quantize_layer(FAKE, FAKE, FAKE, 256, _cfg(), FAKE, 0, 0, 256, FAKE, FAKE, FAKE, FAKE,
                                  ctypes.byref(loss), None, 0, None) == g.GPTQ_OK
     assert loss.value == 0.0
+
+    # the stream-ordered forms: the same checks, plus the device flag
+    assert L.gptq_prepare_hinv_async(None, 16, _cfg(), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == g.GPTQ_ERR_INVALID_ARG
+    assert L.gptq_prepare_hinv_async(FAKE, 16, _cfg(), FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == g.GPTQ_ERR_INVALID_ARG
+    assert b"info" in L.gptq_last_error()
+    assert L.gptq_prepare_hinv_async(FAKE, 16, _cfg(), FAKE, FAKE, FAKE, FAKE, FAKE, 10, None) == g.GPTQ_ERR_WORKSPACE
+    assert L.gptq_prepare_hinv_async(FAKE, 16, _cfg(damp_percent=-1.0), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                     None) == g.GPTQ_ERR_INVALID_ARG
+    qa = lambda n=256, rows=8, ldw=256, ws=1 << 30, cfg=None: L.gptq_quantize_layer_async(
+        FAKE, FAKE, FAKE, n, cfg or _cfg(), FAKE, 0, rows, ldw, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+    assert qa(cfg=_cfg(bits=5)) == g.GPTQ_ERR_UNSUPPORTED
+    assert qa(n=200, ldw=200) == g.GPTQ_ERR_UNSUPPORTED
+    assert qa(ldw=128) == g.GPTQ_ERR_INVALID_ARG
+    assert qa(ws=16) == g.GPTQ_ERR_WORKSPACE
+    assert b"gptq_quantize_layer_async" not in L.gptq_last_error()   # argument errors name the argument
 
     rel = ctypes.c_double(0)
     assert L.gptq_layer_loss(None, 256, FAKE, 0, 8, 256, FAKE, FAKE, FAKE, FAKE, _cfg(), ctypes.byref(rel),
