@@ -42,10 +42,14 @@ constexpr int kGroup = 4;  // panels whose trailing update is applied in one pas
 // dd[i] = H_ii, or 1 for a dead column (H_ii == 0); dead flag; a NaN/inf or
 // negative diagonal marks the matrix as not positive definite and is replaced
 // by 1 in dd so that the act-order sort stays a permutation.
+// Without act-order the sweep order is the original one: perm is written here
+// and the rank kernel is not launched.
 __global__ void prep_diag_kernel(const double* __restrict__ H, int n, double* __restrict__ dd,
-                                 uint8_t* __restrict__ dead, int* __restrict__ info) {
+                                 uint8_t* __restrict__ dead, int* __restrict__ info, int desc_act,
+                                 int32_t* __restrict__ perm) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
+  if (!desc_act) perm[i] = i;
   const double d = H[static_cast<int64_t>(i) * n + i];
   const bool isdead = (d == 0.0);
   dead[i] = isdead ? 1 : 0;
@@ -82,34 +86,53 @@ __global__ void __launch_bounds__(256) prep_rank_kernel(const double* __restrict
   if (i < n) perm[rank] = i;
 }
 
-// lambda = damp * mean(dd); one workgroup, fixed-order tree reduction in fp64.
-__global__ void __launch_bounds__(256) prep_lambda_kernel(const double* __restrict__ dd, int n,
-                                                          double damp, double* __restrict__ lam) {
-  __shared__ double red[256];
-  double s = 0.0;
-  for (int i = threadIdx.x; i < n; i += 256) s += dd[i];
-  red[threadIdx.x] = s;
+// lambda = damp * mean(dd); one workgroup of 1024, fixed-order reduction in
+// fp64: each thread sums its strided entries in four independent chains (so
+// their loads are in flight together), then a tree over the threads.
+__global__ void __launch_bounds__(1024) prep_lambda_kernel(const double* __restrict__ dd, int n,
+                                                           double damp, double* __restrict__ lam) {
+  __shared__ double red[1024];
+  const int t = threadIdx.x;
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
+  int i = t;
+  for (; i + 3 * 1024 < n; i += 4 * 1024) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] += dd[i + q * 1024];
+  }
+  for (int q = 0; i < n; i += 1024, ++q) s[q] += dd[i];
+  red[t] = (s[0] + s[1]) + (s[2] + s[3]);
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+  for (int w = 512; w > 0; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) *lam = damp * (red[0] / n);
+  if (t == 0) *lam = damp * (red[0] / n);
 }
 
 // A[a][b] (lower part, b <= a) = H_p[n-1-a][n-1-b] + lambda*delta, with
-// H_p[x][y] = H[perm[x]][perm[y]] and dead diagonals taken as 1.
-__global__ void prep_gather_kernel(const double* __restrict__ H, const int32_t* __restrict__ perm,
-                                   const double* __restrict__ dd, const double* __restrict__ lam,
-                                   int n, double* __restrict__ A) {
-  for (int a = blockIdx.y; a < n; a += gridDim.y) {
-    const int x = n - 1 - a;
-    const int px = perm[x];
-    const double* hrow = H + static_cast<int64_t>(px) * n;
-    for (int b = blockIdx.x * blockDim.x + threadIdx.x; b <= a; b += gridDim.x * blockDim.x) {
-      const int y = n - 1 - b;
-      double v = (a == b) ? dd[px] + *lam : hrow[perm[y]];
-      A[static_cast<int64_t>(a) * n + b] = v;
+// H_p[x][y] = H[perm[x]][perm[y]] and dead diagonals taken as 1.  One
+// work-group per pair of rows a and n-1-a (a + 1 and n - a entries: n + 1 in
+// all, so every work-group moves the same amount); without act-order the
+// source row is read directly (H_p = H).
+__global__ void __launch_bounds__(256) prep_gather_kernel(const double* __restrict__ H,
+                                                          const int32_t* __restrict__ perm,
+                                                          const double* __restrict__ dd,
+                                                          const double* __restrict__ lam, int n, int desc_act,
+                                                          double* __restrict__ A) {
+  const double l = *lam;
+  for (int p = blockIdx.x; 2 * p < n; p += gridDim.x) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int a = h ? n - 1 - p : p;
+      if (h && a == p) break;  // the middle row of an odd n
+      const int x = n - 1 - a;
+      const int px = desc_act ? perm[x] : x;
+      const double* hrow = H + static_cast<int64_t>(px) * n;
+      double* arow = A + static_cast<int64_t>(a) * n;
+      for (int b = threadIdx.x; b <= a; b += blockDim.x) {
+        const int y = n - 1 - b;
+        arow[b] = (a == b) ? dd[px] + l : hrow[desc_act ? perm[y] : y];
+      }
     }
   }
 }
@@ -1044,14 +1067,16 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
   }
   if (e != hipSuccess) return e;
   const int nb = (n + 255) / 256;
-  hipLaunchKernelGGL(prep_diag_kernel, dim3(nb), dim3(256), 0, s, H, n, dd, dead, info);
+  hipLaunchKernelGGL(prep_diag_kernel, dim3(nb), dim3(256), 0, s, H, n, dd, dead, info, desc_act, perm);
   GPTQ_CHECK_LAUNCH();
-  hipLaunchKernelGGL(prep_rank_kernel, dim3(nb), dim3(256), 0, s, dd, n, desc_act, perm);
-  GPTQ_CHECK_LAUNCH();
-  hipLaunchKernelGGL(prep_lambda_kernel, dim3(1), dim3(256), 0, s, dd, n, damp, lam);
+  if (desc_act) {
+    hipLaunchKernelGGL(prep_rank_kernel, dim3(nb), dim3(256), 0, s, dd, n, desc_act, perm);
+    GPTQ_CHECK_LAUNCH();
+  }
+  hipLaunchKernelGGL(prep_lambda_kernel, dim3(1), dim3(1024), 0, s, dd, n, damp, lam);
   GPTQ_CHECK_LAUNCH();
   const unsigned gy = n < 65535 ? n : 65535;
-  hipLaunchKernelGGL(prep_gather_kernel, dim3((n + 255) / 256, gy), dim3(256), 0, s, H, perm, dd, lam, n, A);
+  hipLaunchKernelGGL(prep_gather_kernel, dim3((n + 1) / 2), dim3(256), 0, s, H, perm, dd, lam, n, desc_act, A);
   GPTQ_CHECK_LAUNCH();
   if (side) {
     e = hipStreamWaitEvent(s, ev_join, 0);   // Linv cleared
