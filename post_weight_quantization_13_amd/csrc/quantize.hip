@@ -178,6 +178,9 @@ __global__ void __launch_bounds__(256) split_ut_kernel(const float* __restrict__
 // (16 lanes on two rows, all eight units of each).  Keyed on r & 7 instead,
 // rows r and r + 8 shared a slot and every read took two cycles.
 constexpr int kTK = 64;
+// 128-wide trailing tiles from this many tiles on (one per compute unit);
+// fewer tiles run 64 wide, twice as many work-groups
+constexpr int kTrailWideTiles = 256;
 __device__ __forceinline__ int tk_offset(int row, int c) {
   return row * (kTK * 2) + ((c ^ ((row >> 1) & 7)) << 4);
 }
@@ -656,9 +659,9 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
 }
 
 // ---------------------------------------------------------------- trailing update
-// Wk[r0:r0+128, c0:c0+128] -= E[r0:r0+128, 0:K] U[i1:i1+K, c0:c0+128] for
-// columns c < ce, c0 = cb + 128*blockIdx.x, r0 = 128*blockIdx.y; E given
-// split (Eh/El, row stride ldE), U as its split transpose (UTh/UTl).
+// Wk[r0:r0+128, c0:c0+TN] -= E[r0:r0+128, 0:K] U[i1:i1+K, c0:c0+TN] for
+// columns c < ce; E given split (Eh/El, row stride ldE), U as its split
+// transpose (UTh/UTl).
 // Split-bf16 product on the bf16 MFMA: each fp32 operand x = hi + lo with
 // hi = bf16(x), lo = bf16(x - hi) (round to nearest even), and
 //   E U ~ Ehi Uhi + Ehi Ulo + Elo Uhi   (fp32 accumulation),
@@ -668,28 +671,41 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
 // transposed as [col][k], so each MFMA operand fragment (8 consecutive k) is
 // one 16-byte read; the next chunk's copies are in flight during the current
 // chunk's MFMAs.
-// 256 threads; wave (wm, wn) owns a 64x64 quarter = 2x2 v_mfma_f32_32x32x16_bf16
-// tiles (accumulator q of lane l is row 8(q/4) + 4(l/32) + q%4, column l%32).
+// 256 threads; wave (wm, wn) owns a 64 x TN/2 block = 2 x TN/64
+// v_mfma_f32_32x32x16_bf16 tiles (accumulator q of lane l is row
+// 8(q/4) + 4(l/32) + q%4, column l%32).  TN = 128, or 64 for launches with
+// too few 128-wide tiles to occupy every compute unit.
+// Tiles are numbered row-major (tiles_x per 128-row band) and dealt so that
+// the work-groups of one XCD (block index mod 8) take one contiguous range of
+// that order: they share E rows and U columns in that XCD's L2.  The grid is
+// 8 * ceil(tiles / 8) work-groups; the surplus ones exit at once.
+template <int TN>
 __global__ void __launch_bounds__(256, 2) trailing_kernel(float* __restrict__ Wk, const uint16_t* __restrict__ Eh,
                                                        const uint16_t* __restrict__ El, int ldE,
                                                        const uint16_t* __restrict__ UTh,
                                                        const uint16_t* __restrict__ UTl, int n, int rows, int i1,
-                                                       int K, int cb, int ce) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4][128 * kTK * 2];  // Ehi, Elo, Uhi, Ulo: 64 KB
+                                                       int K, int cb, int ce, int tiles_x, int tiles) {
+  constexpr int NJ = TN / 64;   // MFMA tiles per wave along the columns
+  constexpr int QU = TN / 32;   // 16-byte U units per thread and chunk
+  __shared__ __attribute__((aligned(16))) uint8_t lds_e[2][128 * kTK * 2];  // Ehi, Elo
+  __shared__ __attribute__((aligned(16))) uint8_t lds_u[2][TN * kTK * 2];   // Uhi, Ulo
+  const int per = (tiles + 7) / 8;
+  const int t = static_cast<int>(blockIdx.x % 8) * per + static_cast<int>(blockIdx.x / 8);
+  if (t >= tiles) return;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  const int r0 = blockIdx.y * 128;
-  const int c0 = cb + blockIdx.x * 128;
-  f32x16 acc[2][2];
+  const int r0 = (t / tiles_x) * 128;
+  const int c0 = cb + (t % tiles_x) * TN;
+  f32x16 acc[2][NJ];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  u32x4 re[2][4], ru[2][4];  // [plane][unit]: unit u = tid + 256q -> (row or column u/8, k-octet u%8)
+  u32x4 re[2][4], ru[2][QU];  // [plane][unit]: unit u = tid + 256q -> (row or column u/8, k-octet u%8)
   auto gload = [&](int kc) {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -701,7 +717,7 @@ __global__ void __launch_bounds__(256, 2) trailing_kernel(float* __restrict__ Wk
       re[1][q] = ok ? *reinterpret_cast<const u32x4*>(El + off) : z;
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < QU; ++q) {
       const int u = tid + 256 * q, col = u >> 3, unit = u & 7;
       const bool ok = c0 + col < ce;
       const int64_t off = static_cast<int64_t>(c0 + col) * n + i1 + kc + 8 * unit;
@@ -715,62 +731,85 @@ __global__ void __launch_bounds__(256, 2) trailing_kernel(float* __restrict__ Wk
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int u = tid + 256 * q;
-      *reinterpret_cast<u32x4*>(lds[0] + tk_offset(u >> 3, u & 7)) = re[0][q];
-      *reinterpret_cast<u32x4*>(lds[1] + tk_offset(u >> 3, u & 7)) = re[1][q];
-      *reinterpret_cast<u32x4*>(lds[2] + tk_offset(u >> 3, u & 7)) = ru[0][q];
-      *reinterpret_cast<u32x4*>(lds[3] + tk_offset(u >> 3, u & 7)) = ru[1][q];
+      *reinterpret_cast<u32x4*>(lds_e[0] + tk_offset(u >> 3, u & 7)) = re[0][q];
+      *reinterpret_cast<u32x4*>(lds_e[1] + tk_offset(u >> 3, u & 7)) = re[1][q];
+    }
+#pragma unroll
+    for (int q = 0; q < QU; ++q) {
+      const int u = tid + 256 * q;
+      *reinterpret_cast<u32x4*>(lds_u[0] + tk_offset(u >> 3, u & 7)) = ru[0][q];
+      *reinterpret_cast<u32x4*>(lds_u[1] + tk_offset(u >> 3, u & 7)) = ru[1][q];
     }
     __syncthreads();
     if (kc + kTK < K) gload(kc + kTK);
 #pragma unroll
     for (int kk = 0; kk < kTK / 16; ++kk) {
       const int c = kk * 2 + (lane >> 5);
-      u32x4 ah[2], al[2], bh[2], bl[2];
+      u32x4 ah[2], al[2], bh[NJ], bl[NJ];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int m = wm * 64 + i * 32 + (lane & 31);
-        ah[i] = *reinterpret_cast<const u32x4*>(lds[0] + tk_offset(m, c));
-        al[i] = *reinterpret_cast<const u32x4*>(lds[1] + tk_offset(m, c));
+        ah[i] = *reinterpret_cast<const u32x4*>(lds_e[0] + tk_offset(m, c));
+        al[i] = *reinterpret_cast<const u32x4*>(lds_e[1] + tk_offset(m, c));
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int cc = wn * 64 + j * 32 + (lane & 31);
-        bh[j] = *reinterpret_cast<const u32x4*>(lds[2] + tk_offset(cc, c));
-        bl[j] = *reinterpret_cast<const u32x4*>(lds[3] + tk_offset(cc, c));
+      for (int j = 0; j < NJ; ++j) {
+        const int cc = wn * (TN / 2) + j * 32 + (lane & 31);
+        bh[j] = *reinterpret_cast<const u32x4*>(lds_u[0] + tk_offset(cc, c));
+        bl[j] = *reinterpret_cast<const u32x4*>(lds_u[1] + tk_offset(cc, c));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           acc[i][j] = mfma_bf16(al[i], bh[j], acc[i][j]);
           acc[i][j] = mfma_bf16(ah[i], bl[j], acc[i][j]);
           acc[i][j] = mfma_bf16(ah[i], bh[j], acc[i][j]);
         }
     }
   }
-  // Epilogue: all 64 loads of this lane's W values are issued before any store
+  // Epilogue: all loads of this lane's W values are issued before any store
   // (a load after a store to the same array would otherwise wait for it).
-  float old[2][2][16];
+  float old[2][NJ][16];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int rr = r0 + wm * 64 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-        const int cc = c0 + wn * 64 + j * 32 + (lane & 31);
+        const int cc = c0 + wn * (TN / 2) + j * 32 + (lane & 31);
         old[i][j][q] = (rr < rows && cc < ce) ? Wk[static_cast<int64_t>(rr) * n + cc] : 0.0f;
       }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int rr = r0 + wm * 64 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-        const int cc = c0 + wn * 64 + j * 32 + (lane & 31);
+        const int cc = c0 + wn * (TN / 2) + j * 32 + (lane & 31);
         if (rr < rows && cc < ce) Wk[static_cast<int64_t>(rr) * n + cc] = old[i][j][q] - acc[i][j][q];
       }
+}
+
+// Launches the trailing update of columns [cb, ce) by K rows of U from i1.
+static hipError_t launch_trailing(hipStream_t st, float* Wk, const uint16_t* Eh, const uint16_t* El, int ldE,
+                                  const uint16_t* UTh, const uint16_t* UTl, int n, int rows, int i1, int K, int cb,
+                                  int ce) {
+  const int64_t bands = (rows + 127) / 128;
+  if (bands * ((ce - cb + 63) / 64) > (int64_t{1} << 30)) return hipErrorInvalidValue;  // grid size
+  const int wide_tiles = static_cast<int>(bands * ((ce - cb + 127) / 128));
+  if (wide_tiles >= kTrailWideTiles) {
+    const int tx = (ce - cb + 127) / 128, tiles = static_cast<int>(bands) * tx;
+    hipLaunchKernelGGL(trailing_kernel<128>, dim3(8 * ((tiles + 7) / 8)), dim3(256), 0, st, Wk, Eh, El, ldE, UTh, UTl,
+                       n, rows, i1, K, cb, ce, tx, tiles);
+  } else {
+    const int tx = (ce - cb + 63) / 64, tiles = static_cast<int>(bands) * tx;
+    hipLaunchKernelGGL(trailing_kernel<64>, dim3(8 * ((tiles + 7) / 8)), dim3(256), 0, st, Wk, Eh, El, ldE, UTh, UTl,
+                       n, rows, i1, K, cb, ce, tx, tiles);
+  }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- pack
@@ -947,7 +986,6 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
   // of those columns there.
   // E holds the errors of two super-blocks (alternating), [rows, kSuper] each.
   const dim3 grid((rows + kRowsSweep - 1) / kRowsSweep);
-  const int rt = (rows + 127) / 128;
   const int nsb = (n + kSuper - 1) / kSuper;
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join[2] = {nullptr, nullptr};
@@ -999,9 +1037,8 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
         joined[(j + 1) & 1] = true;
       }
       const int ne = (s2 + kSuper < n) ? s2 + kSuper : n;
-      hipLaunchKernelGGL(trailing_kernel, dim3((ne - s2 + 127) / 128, rt), dim3(256), 0, s, Wk, Ejh, Ejl, kSuper,
-                         UTh, UTl, n, rows, s1, s2 - s1, s2, ne);
-      GPTQ_CHECK_LAUNCH();
+      e = launch_trailing(s, Wk, Ejh, Ejl, kSuper, UTh, UTl, n, rows, s1, s2 - s1, s2, ne);
+      if (e != hipSuccess) return e;
     }
     const int wide = s2 + kSuper;  // first column of super-block j+2
     if (wide < n) {
@@ -1011,9 +1048,8 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
         if (e == hipSuccess) e = hipStreamWaitEvent(side, ev_fork, 0);
         if (e != hipSuccess) return e;
       }
-      hipLaunchKernelGGL(trailing_kernel, dim3((n - wide + 127) / 128, rt), dim3(256), 0, st, Wk, Ejh, Ejl, kSuper,
-                         UTh, UTl, n, rows, s1, s2 - s1, wide, n);
-      GPTQ_CHECK_LAUNCH();
+      e = launch_trailing(st, Wk, Ejh, Ejl, kSuper, UTh, UTl, n, rows, s1, s2 - s1, wide, n);
+      if (e != hipSuccess) return e;
       if (side) {
         e = hipEventRecord(ev_join[j & 1], side);
         if (e != hipSuccess) return e;
