@@ -678,7 +678,8 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
 // Tiles are numbered row-major (tiles_x per 128-row band) and dealt so that
 // the work-groups of one XCD (block index mod 8) take one contiguous range of
 // that order: they share E rows and U columns in that XCD's L2.  The grid is
-// 8 * ceil(tiles / 8) work-groups; the surplus ones exit at once.
+// a multiple of 8; XCD k's gridDim.x / 8 work-groups walk its range with
+// that stride (one tile each when the grid is 8 * ceil(tiles / 8)).
 template <int TN>
 __global__ void __launch_bounds__(256, 2) trailing_kernel(float* __restrict__ Wk, const uint16_t* __restrict__ Eh,
                                                        const uint16_t* __restrict__ El, int ldE,
@@ -690,11 +691,13 @@ __global__ void __launch_bounds__(256, 2) trailing_kernel(float* __restrict__ Wk
   __shared__ __attribute__((aligned(16))) uint8_t lds_e[2][128 * kTK * 2];  // Ehi, Elo
   __shared__ __attribute__((aligned(16))) uint8_t lds_u[2][TN * kTK * 2];   // Uhi, Ulo
   const int per = (tiles + 7) / 8;
-  const int t = static_cast<int>(blockIdx.x % 8) * per + static_cast<int>(blockIdx.x / 8);
-  if (t >= tiles) return;
+  const int xcd = static_cast<int>(blockIdx.x % 8);
+  const int t_end = ((xcd + 1) * per < tiles) ? (xcd + 1) * per : tiles;
+  const int stride = static_cast<int>(gridDim.x / 8);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
+  for (int t = xcd * per + static_cast<int>(blockIdx.x / 8); t < t_end; t += stride) {
   const int r0 = (t / tiles_x) * 128;
   const int c0 = cb + (t % tiles_x) * TN;
   f32x16 acc[2][NJ];
@@ -791,18 +794,22 @@ __global__ void __launch_bounds__(256, 2) trailing_kernel(float* __restrict__ Wk
         const int cc = c0 + wn * (TN / 2) + j * 32 + (lane & 31);
         if (rr < rows && cc < ce) Wk[static_cast<int64_t>(rr) * n + cc] = old[i][j][q] - acc[i][j][q];
       }
+  __syncthreads();  // the next tile's first staging overwrites this tile's LDS
+  }
 }
 
-// Launches the trailing update of columns [cb, ce) by K rows of U from i1.
+// Launches the trailing update of columns [cb, ce) by K rows of U from i1, on
+// at most max_wgs work-groups (a multiple of 8).
 static hipError_t launch_trailing(hipStream_t st, float* Wk, const uint16_t* Eh, const uint16_t* El, int ldE,
                                   const uint16_t* UTh, const uint16_t* UTl, int n, int rows, int i1, int K, int cb,
-                                  int ce) {
+                                  int ce, int max_wgs) {
   const int64_t bands = (rows + 127) / 128;
   if (bands * ((ce - cb + 63) / 64) > (int64_t{1} << 30)) return hipErrorInvalidValue;  // grid size
   const int wide_tiles = static_cast<int>(bands * ((ce - cb + 127) / 128));
   if (wide_tiles >= kTrailWideTiles) {
     const int tx = (ce - cb + 127) / 128, tiles = static_cast<int>(bands) * tx;
-    hipLaunchKernelGGL(trailing_kernel<128>, dim3(8 * ((tiles + 7) / 8)), dim3(256), 0, st, Wk, Eh, El, ldE, UTh, UTl,
+    const int grid = (tiles < max_wgs) ? 8 * ((tiles + 7) / 8) : max_wgs;
+    hipLaunchKernelGGL(trailing_kernel<128>, dim3(grid), dim3(256), 0, st, Wk, Eh, El, ldE, UTh, UTl,
                        n, rows, i1, K, cb, ce, tx, tiles);
   } else {
     const int tx = (ce - cb + 63) / 64, tiles = static_cast<int>(bands) * tx;
@@ -1004,6 +1011,21 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
     if (e != hipSuccess) return e;
   }
   bool joined[2] = {true, true};  // no wide update of that parity in flight
+  // The wide update runs on 1.5 work-groups per compute unit (each looping
+  // over its XCD's tiles): with one per tile its 768 work-groups (4096 x 4096)
+  // took every slot, and the sweep block beside it waited for slots (42-58 us
+  // against 24 us).  Measured at 4096 and 11008 columns, 4096 rows: 1.07 ->
+  // 1.01 ms and 4.80 -> 4.55 ms per call; 1.25 per compute unit about the
+  // same, 1.625 per compute unit slower than one per tile.
+  int wide_wgs = 384;
+  if (side) {
+    int dev = 0, cus = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    wide_wgs = (3 * cus / 2) & ~7;
+    if (wide_wgs < 8) wide_wgs = 8;
+  }
   for (int j = 0; j < nsb; ++j) {
     const int s1 = j * kSuper;
     const int s2 = (s1 + kSuper < n) ? s1 + kSuper : n;
@@ -1037,7 +1059,7 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
         joined[(j + 1) & 1] = true;
       }
       const int ne = (s2 + kSuper < n) ? s2 + kSuper : n;
-      e = launch_trailing(s, Wk, Ejh, Ejl, kSuper, UTh, UTl, n, rows, s1, s2 - s1, s2, ne);
+      e = launch_trailing(s, Wk, Ejh, Ejl, kSuper, UTh, UTl, n, rows, s1, s2 - s1, s2, ne, 1 << 30);
       if (e != hipSuccess) return e;
     }
     const int wide = s2 + kSuper;  // first column of super-block j+2
@@ -1048,7 +1070,7 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
         if (e == hipSuccess) e = hipStreamWaitEvent(side, ev_fork, 0);
         if (e != hipSuccess) return e;
       }
-      e = launch_trailing(st, Wk, Ejh, Ejl, kSuper, UTh, UTl, n, rows, s1, s2 - s1, wide, n);
+      e = launch_trailing(st, Wk, Ejh, Ejl, kSuper, UTh, UTl, n, rows, s1, s2 - s1, wide, n, wide_wgs);
       if (e != hipSuccess) return e;
       if (side) {
         e = hipEventRecord(ev_join[j & 1], side);
