@@ -1,6 +1,7 @@
 // Shared device-side definitions for the gfx950 GPTQ kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -1121,11 +1121,15 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
   for (int k0 = 0; k0 < nblk; k0 += kGroup) {
     const int ke = (k0 + kGroup < nblk) ? k0 + kGroup : nblk;
     for (int k = k0; k < ke; ++k) {
-      hipLaunchKernelGGL(chol_step_kernel, dim3(nblk - k), dim3(256), 0, s, A, Linv, n, k, k0, ke, info);
+      // Events that other streams wait for are recorded by the launch of the
+      // kernel they follow (hipExtLaunchKernelGGL's stop event) rather than by
+      // a separate record, which costs the stream a further 1-2 us.
+      const bool top_fork = side2 && k == h / kB - 1;  // block columns < h are final
+      hipExtLaunchKernelGGL(chol_step_kernel, dim3(nblk - k), dim3(256), 0, s, nullptr, top_fork ? ev2.fork : nullptr,
+                            0, A, Linv, n, k, k0, ke, info);
       GPTQ_CHECK_LAUNCH();
-      if (side2 && k == h / kB - 1) {  // block columns < h are final
-        e = hipEventRecord(ev2.fork, s);
-        if (e == hipSuccess) e = hipStreamWaitEvent(side2, ev2.fork, 0);
+      if (top_fork) {
+        e = hipStreamWaitEvent(side2, ev2.fork, 0);
         for (int sz = kB; e == hipSuccess && sz < h; sz *= 2) {
           e = level(sz, 0, 0, h / (2 * sz), side2);
           if (e == hipSuccess) e = level(sz, 1, 0, h / (2 * sz), side2);
@@ -1144,11 +1148,11 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
         } else if (e == hipSuccess) {
           const int tiles = (h / kB) * (h / kB);
           const int wgs = (top_wgs < tiles) ? top_wgs : tiles;
-          hipLaunchKernelGGL(trtri_level_kernel, dim3(1, wgs), dim3(256), kTopLds - sizeof(TileSmem), side2, A, Linv, n,
-                             h, 0, 0);
+          hipExtLaunchKernelGGL(trtri_level_kernel, dim3(1, wgs), dim3(256), kTopLds - sizeof(TileSmem), side2, nullptr,
+                                ev2.join, 0, A, Linv, n, h, 0, 0);
           e = hipGetLastError();
         }
-        if (e == hipSuccess) e = hipEventRecord(ev2.join, side2);
+        if (e == hipSuccess && h > kTopSplitMax) e = hipEventRecord(ev2.join, side2);
         if (e != hipSuccess) return e;
       }
     }
@@ -1162,7 +1166,9 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
     }
     int strip = 0;
     for (int j = ke; j < ne; ++j) strip += nblk - j;
-    hipLaunchKernelGGL(chol_update_kernel, dim3(strip), dim3(256), 0, s, A, n, k0, ke, ke, 2, nblk, ne - ke);
+    const bool fork = side && ne < nblk;  // a side pass follows: its fork is recorded by the strip's launch
+    hipExtLaunchKernelGGL(chol_update_kernel, dim3(strip), dim3(256), 0, s, nullptr, fork ? ev_fork : nullptr, 0, A, n,
+                          k0, ke, ke, 2, nblk, ne - ke);
     GPTQ_CHECK_LAUNCH();
     // the rest (block columns >= ne), K = 64 * group width; forked after the
     // strip so that the strip, which the next panel step waits for, is not
@@ -1170,24 +1176,21 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
     if (ne < nblk) {
       hipStream_t st = side ? side : s;
       if (side) {
-        e = hipEventRecord(ev_fork, s);
-        if (e == hipSuccess) e = hipStreamWaitEvent(side, ev_fork, 0);
+        e = hipStreamWaitEvent(side, ev_fork, 0);
         if (e != hipSuccess) return e;
       }
+      hipEvent_t done = side ? ev_join : nullptr;
       const int nt = (n - ne * kB + kT2 - 1) / kT2;
       if (nt * (nt + 1) / 2 >= kBigTiles) {
-        hipLaunchKernelGGL(chol_trail_kernel, dim3(nt * (nt + 1) / 2), dim3(256), 0, st, A, n, k0, ke, ne * kB);
+        hipExtLaunchKernelGGL(chol_trail_kernel, dim3(nt * (nt + 1) / 2), dim3(256), 0, st, nullptr, done, 0, A, n, k0,
+                              ke, ne * kB);
       } else {
         const int rest = nblk - ne;
-        hipLaunchKernelGGL(chol_update_kernel, dim3(rest * (rest + 1) / 2), dim3(256), 0, st, A, n, k0, ke, ne, 0,
-                           nblk, 1);
+        hipExtLaunchKernelGGL(chol_update_kernel, dim3(rest * (rest + 1) / 2), dim3(256), 0, st, nullptr, done, 0, A, n,
+                              k0, ke, ne, 0, nblk, 1);
       }
       GPTQ_CHECK_LAUNCH();
-      if (side) {
-        e = hipEventRecord(ev_join, side);
-        if (e != hipSuccess) return e;
-        pending = true;
-      }
+      if (side) pending = true;
     }
   }
   if (pending) {

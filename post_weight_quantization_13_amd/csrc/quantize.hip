@@ -799,22 +799,25 @@ __global__ void __launch_bounds__(256, 2) trailing_kernel(float* __restrict__ Wk
 }
 
 // Launches the trailing update of columns [cb, ce) by K rows of U from i1, on
-// at most max_wgs work-groups (a multiple of 8).
+// at most max_wgs work-groups (a multiple of 8).  A non-null `done` is
+// recorded by the launch itself when the kernel completes (no separate marker
+// on the stream: a marker between two kernels of a stream delays the second
+// by about 7 us).
 static hipError_t launch_trailing(hipStream_t st, float* Wk, const uint16_t* Eh, const uint16_t* El, int ldE,
                                   const uint16_t* UTh, const uint16_t* UTl, int n, int rows, int i1, int K, int cb,
-                                  int ce, int max_wgs) {
+                                  int ce, int max_wgs, hipEvent_t done = nullptr) {
   const int64_t bands = (rows + 127) / 128;
   if (bands * ((ce - cb + 63) / 64) > (int64_t{1} << 30)) return hipErrorInvalidValue;  // grid size
   const int wide_tiles = static_cast<int>(bands * ((ce - cb + 127) / 128));
   if (wide_tiles >= kTrailWideTiles) {
     const int tx = (ce - cb + 127) / 128, tiles = static_cast<int>(bands) * tx;
     const int grid = (tiles < max_wgs) ? 8 * ((tiles + 7) / 8) : max_wgs;
-    hipLaunchKernelGGL(trailing_kernel<128>, dim3(grid), dim3(256), 0, st, Wk, Eh, El, ldE, UTh, UTl,
-                       n, rows, i1, K, cb, ce, tx, tiles);
+    hipExtLaunchKernelGGL(trailing_kernel<128>, dim3(grid), dim3(256), 0, st, nullptr, done, 0, Wk, Eh, El, ldE, UTh,
+                          UTl, n, rows, i1, K, cb, ce, tx, tiles);
   } else {
     const int tx = (ce - cb + 63) / 64, tiles = static_cast<int>(bands) * tx;
-    hipLaunchKernelGGL(trailing_kernel<64>, dim3(8 * ((tiles + 7) / 8)), dim3(256), 0, st, Wk, Eh, El, ldE, UTh, UTl,
-                       n, rows, i1, K, cb, ce, tx, tiles);
+    hipExtLaunchKernelGGL(trailing_kernel<64>, dim3(8 * ((tiles + 7) / 8)), dim3(256), 0, st, nullptr, done, 0, Wk, Eh,
+                          El, ldE, UTh, UTl, n, rows, i1, K, cb, ce, tx, tiles);
   }
   return hipGetLastError();
 }
@@ -1059,24 +1062,24 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
         joined[(j + 1) & 1] = true;
       }
       const int ne = (s2 + kSuper < n) ? s2 + kSuper : n;
-      e = launch_trailing(s, Wk, Ejh, Ejl, kSuper, UTh, UTl, n, rows, s1, s2 - s1, s2, ne, 1 << 30);
+      // when a wide update follows (it waits for this kernel), the fork event
+      // is recorded by this launch
+      const bool fork = side && s2 + kSuper < n;
+      e = launch_trailing(s, Wk, Ejh, Ejl, kSuper, UTh, UTl, n, rows, s1, s2 - s1, s2, ne, 1 << 30,
+                          fork ? ev_fork : nullptr);
       if (e != hipSuccess) return e;
     }
     const int wide = s2 + kSuper;  // first column of super-block j+2
     if (wide < n) {
       hipStream_t st = side ? side : s;
-      if (side) {
-        e = hipEventRecord(ev_fork, s);
-        if (e == hipSuccess) e = hipStreamWaitEvent(side, ev_fork, 0);
+      if (side) {  // ev_fork was recorded by the next super-block's update above
+        e = hipStreamWaitEvent(side, ev_fork, 0);
         if (e != hipSuccess) return e;
       }
-      e = launch_trailing(st, Wk, Ejh, Ejl, kSuper, UTh, UTl, n, rows, s1, s2 - s1, wide, n, wide_wgs);
+      e = launch_trailing(st, Wk, Ejh, Ejl, kSuper, UTh, UTl, n, rows, s1, s2 - s1, wide, n, wide_wgs,
+                          side ? ev_join[j & 1] : nullptr);
       if (e != hipSuccess) return e;
-      if (side) {
-        e = hipEventRecord(ev_join[j & 1], side);
-        if (e != hipSuccess) return e;
-        joined[j & 1] = false;
-      }
+      if (side) joined[j & 1] = false;
     }
   }
   for (int par = 0; par < 2; ++par) {
