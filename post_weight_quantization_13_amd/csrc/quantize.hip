@@ -383,11 +383,15 @@ constexpr float near_midpoint() {
   return (BITS <= 4) ? 3.814697265625e-06f : 3.814697265625e-06f * static_cast<float>(1 << (BITS - 4));
 }
 
+// One launch sweeps the nb blocks of a super-block from column s1: a
+// work-group's pending updates need only its own rows' errors of the earlier
+// blocks (written to Ejh/Ejl, read back after a work-group barrier), so the
+// blocks follow one another inside the work-group without a launch between.
 template <int BITS, int SYM>
 __global__ void __launch_bounds__(256) sweep_block_kernel(
     const float* __restrict__ Wk, const float* __restrict__ U, const uint16_t* __restrict__ UTh,
-    const uint16_t* __restrict__ UTl, int n, int rows, int i1, uint8_t* __restrict__ codes,
-    uint16_t* __restrict__ Eh, uint16_t* __restrict__ El, int ldE, PendSeg sa, PendSeg sb,
+    const uint16_t* __restrict__ UTl, int n, int rows, int s1, int nb, uint8_t* __restrict__ codes,
+    uint16_t* __restrict__ Ejh, uint16_t* __restrict__ Ejl, int ldE, PendSeg sa,
     uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, double* __restrict__ rowloss, int gs,
     const float* __restrict__ rowsz) {
   __shared__ __attribute__((aligned(16))) float UT[kBlk][kBlk + 4];
@@ -399,6 +403,18 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
   const int wave = tid >> 6, lane = tid & 63;
   const int r = blockIdx.x * kRowsSweep + lane;
   const bool valid = r < rows;
+  double loss = 0.0;
+  for (int blk = 0; blk < nb; ++blk) {
+  const int i1 = s1 + blk * kBlk;
+  uint16_t* const Eh = Ejh + blk * kBlk;  // this block's columns of the split errors
+  uint16_t* const El = Ejl + blk * kBlk;
+  const PendSeg sb{Ejh, Ejl, blk * kBlk, s1};  // the earlier blocks of the super-block
+  if (blk > 0) {
+    // the previous block's split errors (global) are visible to every wave,
+    // and its LDS contents are no longer read
+    __threadfence_block();
+    __syncthreads();
+  }
 
   // Staging: every global load of the block is issued before the LDS stores.
   // LDS banks on this chip: 4-byte stores see word % 32 per half-wave, 16-byte
@@ -446,7 +462,6 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
   constexpr float maxq = static_cast<float>((1 << BITS) - 1);
   const float lo = (SYM == 1) ? 1.0f : 0.0f;
   float sv = 1.0f, zv = 0.0f, rs = 1.0f;
-  double loss = 0.0;
   // Wave 0: scale and zero point of the group of columns c0 .. c0 + cnt - 1
   // of the block, from their current (compensated) values, written out as
   // group (i1 + c0) / gs.  The range includes 0; a group whose range is {0}
@@ -655,6 +670,7 @@ __global__ void __launch_bounds__(256) sweep_block_kernel(
     }
   }
   if (wave > 0) store_split(kSubs - 1);   // Es of the last sub-block is final after the last barrier
+  }
   if (wave == 0 && valid) rowloss[r] += 0.5 * loss;
 }
 
@@ -893,11 +909,11 @@ size_t quantize_workspace(int64_t rows, int64_t n) {
 
 template <int BITS, int SYM>
 static void launch_sweep(dim3 g, hipStream_t s, const float* Wk, const float* U, const uint16_t* UTh,
-                         const uint16_t* UTl, int n, int rows, int i1, uint8_t* codes, uint16_t* Eh, uint16_t* El,
-                         const PendSeg& sa, const PendSeg& sb, uint16_t* scales, uint16_t* zeros, double* rowloss,
+                         const uint16_t* UTl, int n, int rows, int s1, int nb, uint8_t* codes, uint16_t* Ejh,
+                         uint16_t* Ejl, const PendSeg& sa, uint16_t* scales, uint16_t* zeros, double* rowloss,
                          int gs, const float* rowsz) {
-  hipLaunchKernelGGL((sweep_block_kernel<BITS, SYM>), g, dim3(256), 0, s, Wk, U, UTh, UTl, n, rows, i1, codes, Eh, El,
-                     kSuper, sa, sb, scales, zeros, rowloss, gs, rowsz);
+  hipLaunchKernelGGL((sweep_block_kernel<BITS, SYM>), g, dim3(256), 0, s, Wk, U, UTh, UTl, n, rows, s1, nb, codes, Ejh,
+                     Ejl, kSuper, sa, scales, zeros, rowloss, gs, rowsz);
 }
 
 template <int BITS, int SYM>
@@ -1042,12 +1058,10 @@ hipError_t launch_quantize(const float* U, const int32_t* perm, const uint8_t* d
       joined[j & 1] = true;
     }
     const PendSeg sa{Eph, Epl, 0, s1 - kSuper};  // the previous super-block: already applied
-    for (int i1 = s1; i1 < s2; i1 += kBlk) {
-      const PendSeg sb{Ejh, Ejl, i1 - s1, s1};
-      uint16_t* Ebh = Ejh + (i1 - s1);
-      uint16_t* Ebl = Ejl + (i1 - s1);
+    {
+      const int nbk = (s2 - s1) / kBlk;  // blocks of this super-block, one launch
 #define GPTQ_SWEEP(B, S) \
-  launch_sweep<B, S>(grid, s, Wk, U, UTh, UTl, n, rows, i1, codes, Ebh, Ebl, sa, sb, scales, zeros, rowloss, gs, rowsz)
+  launch_sweep<B, S>(grid, s, Wk, U, UTh, UTl, n, rows, s1, nbk, codes, Ejh, Ejl, sa, scales, zeros, rowloss, gs, rowsz)
       GPTQ_BY_BITS_SYM(GPTQ_SWEEP);
 #undef GPTQ_SWEEP
       GPTQ_CHECK_LAUNCH();
