@@ -112,6 +112,13 @@ int main() {
   EXPECT(gptq_prepare_hinv(H, BIG, &cfg, U, perm, dead, p, 1 << 20, nullptr), GPTQ_ERR_INVALID_ARG);
   EXPECT(gptq_prepare_hinv(H, 64, &cfg, U, perm, dead, nullptr, 0, nullptr), GPTQ_ERR_WORKSPACE);
   EXPECT(gptq_prepare_hinv(H, 64, &cfg, U, perm, dead, p, 8, nullptr), GPTQ_ERR_WORKSPACE);
+  // the stream-ordered form: the same checks, and its device flag
+  int32_t* info = static_cast<int32_t*>(p);
+  EXPECT(gptq_prepare_hinv_async(H, 64, nullptr, U, perm, dead, info, p, 1 << 20, nullptr), GPTQ_ERR_INVALID_ARG);
+  EXPECT(gptq_prepare_hinv_async(nullptr, 64, &cfg, U, perm, dead, info, p, 1 << 20, nullptr), GPTQ_ERR_INVALID_ARG);
+  EXPECT(gptq_prepare_hinv_async(H, 64, &cfg, U, perm, dead, nullptr, p, 1 << 20, nullptr), GPTQ_ERR_INVALID_ARG);
+  EXPECT(gptq_prepare_hinv_async(H, BIG, &cfg, U, perm, dead, info, p, 1 << 20, nullptr), GPTQ_ERR_INVALID_ARG);
+  EXPECT(gptq_prepare_hinv_async(H, 64, &cfg, U, perm, dead, info, p, 8, nullptr), GPTQ_ERR_WORKSPACE);
 
   // ---------------------------------------------------------------- quantize
   int32_t* qw = static_cast<int32_t*>(p);
@@ -163,6 +170,22 @@ int main() {
   EXPECT(gptq_quantize_layer(U, perm, dead, 256, &cfg, p, GPTQ_FP32, 8, 256, qw, sc, sc, gi, &d0, nullptr, 0, nullptr),
          GPTQ_ERR_WORKSPACE);
   EXPECT(gptq_quantize_layer(U, perm, dead, 256, &cfg, p, GPTQ_FP32, 8, 256, qw, sc, sc, gi, &d0, p, 64, nullptr),
+         GPTQ_ERR_WORKSPACE);
+  // the stream-ordered form (its loss pointer is device memory: never touched on these paths)
+  double* dloss = static_cast<double*>(p);
+  c = cfg;
+  c.bits = 5;
+  EXPECT(gptq_quantize_layer_async(U, perm, dead, 256, &c, p, GPTQ_FP32, 8, 256, qw, sc, sc, gi, dloss, p, 1 << 20,
+                                   nullptr),
+         GPTQ_ERR_UNSUPPORTED);
+  EXPECT(gptq_quantize_layer_async(nullptr, perm, dead, 256, &cfg, p, GPTQ_FP32, 8, 256, qw, sc, sc, gi, dloss, p,
+                                   1 << 20, nullptr),
+         GPTQ_ERR_INVALID_ARG);
+  EXPECT(gptq_quantize_layer_async(U, perm, dead, 256, &cfg, p, GPTQ_FP32, 8, 255, qw, sc, sc, gi, dloss, p, 1 << 20,
+                                   nullptr),
+         GPTQ_ERR_INVALID_ARG);
+  EXPECT(gptq_quantize_layer_async(U, perm, dead, 256, &cfg, p, GPTQ_FP32, 8, 256, qw, sc, sc, gi, dloss, p, 64,
+                                   nullptr),
          GPTQ_ERR_WORKSPACE);
 
   // ---------------------------------------------------------------- layer loss
