@@ -753,6 +753,12 @@ constexpr int kT2 = 128;
 // 128x128 tiles pay off only with enough of them to keep every compute unit
 // busy with two; below that the 64x64 kernels run more tiles in parallel.
 constexpr int kBigTiles = 512;
+// The factorization's trailing passes switch to 128x128 tiles from this many
+// when n <= kSmallN (measured, prepare alone at n = 4096: 2.716-2.719 against
+// 2.753-2.755 ms with kBigTiles; at n = 11008 the smaller threshold was 0.3 %
+// slower, so larger n keep kBigTiles).
+constexpr int kTrailBigTilesSmallN = 128;
+constexpr int kSmallN = 4096;
 // LDS requested per work-group of the overlapped top level of the inverse
 constexpr int kTopLds = 96 * 1024;
 // largest top-level split h whose first product runs on part of the chip
@@ -1181,7 +1187,7 @@ hipError_t launch_prepare(const double* H, int64_t n64, double damp, int desc_ac
       }
       hipEvent_t done = side ? ev_join : nullptr;
       const int nt = (n - ne * kB + kT2 - 1) / kT2;
-      if (nt * (nt + 1) / 2 >= kBigTiles) {
+      if (nt * (nt + 1) / 2 >= (n <= kSmallN ? kTrailBigTilesSmallN : kBigTiles)) {
         hipExtLaunchKernelGGL(chol_trail_kernel, dim3(nt * (nt + 1) / 2), dim3(256), 0, st, nullptr, done, 0, A, n, k0,
                               ke, ne * kB);
       } else {

@@ -156,9 +156,10 @@ def _spd_with_dead(n, seed, dead=()):
 
 
 # n = 4608 is the smallest size here whose trailing passes and last inverse
-# level have enough 128x128 tiles to run on the 128-tile fp64 kernels.
+# level have enough 128x128 tiles to run on the 128-tile fp64 kernels; at
+# n = 4096 the factorization's trailing passes switch to them from 128 tiles.
 @pytest.mark.parametrize("n,desc_act,dead", [(64, False, ()), (300, True, (7, 299)), (640, False, ()),
-                                             (1000, True, (0,)), (4608, True, (3, 4000))])
+                                             (1000, True, (0,)), (4096, False, (5,)), (4608, True, (3, 4000))])
 def test_prepare_matches_oracle(g, n, desc_act, dead):
     import torch
     H = _spd_with_dead(n, n, dead)
